@@ -1,0 +1,330 @@
+"""Pins of the CPU oracle against what the source page and the mathematics fix.
+
+The method ("MiniMax goes sparse: decoding M3's attention from a single diagram", §1 Step 1
+and Step 2) has no printed worked example, so the oracle is pinned by:
+  * a hand-derived example in the diagram's shape (tests/golden/diagram_shape_example.json);
+  * the dense special case: keeping every block must reproduce dense GQA attention
+    (torch SDPA, float64), since attention runs on the real K/V;
+  * brute-force enumeration of every k-subset on tiny inputs, and numpy's stable argsort;
+  * the linearity identity: <mean query, mean key> = mean of the token-level scores;
+  * a masked dense softmax as a second route to sparse attention over the selected blocks;
+  * closed forms: one visible token, q = 0, constant V, weights summing to 1;
+  * invariances: page permutation, power-of-two query scaling;
+  * prefill: k >= candidates gives dense causal attention; k = 0 gives the diagonal block
+    alone (local causal attention).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_decode_case, make_prefill_case, storage, round_to_bf16
+from helpers import as_f64, dense_gqa, decode_inputs, logical_kv, prefill_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "diagram_shape_example.json")
+
+
+# ----------------------------------------------------------------------------- golden example
+def _golden_inputs(dtype):
+    g = json.load(open(GOLDEN))
+    Hq, Hkv, D, P, N = g["Hq"], g["Hkv"], g["D"], g["P"], g["N"]
+    nb = N // P
+    k = np.zeros((nb, Hkv, P, D), np.float32)
+    v = np.zeros((nb, Hkv, P, D), np.float32)
+    for grp in range(Hkv):
+        for t in range(N):
+            k[t // P, grp, t % P] = g["k"][str(grp)][t]
+            v[t // P, grp, t % P] = g["v"][str(grp)][t]
+    q = np.array(g["q"], np.float32)[None]
+    table = np.arange(nb, dtype=np.int32)[None]
+    return g, dict(q=storage(q, dtype), k_pool=storage(k, dtype), v_pool=storage(v, dtype),
+                   block_table=table, seq_lens=np.array([N], np.int32), Hq=Hq, Hkv=Hkv,
+                   scale=g["scale"], P=P)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_golden_diagram_example(dtype):
+    g, kw = _golden_inputs(dtype)
+    ex = g["expected"]
+    r1 = oracle.decode(top_k=1, want_weights=True, **kw)
+    np.testing.assert_array_equal(r1["scores"][0], np.array(ex["scores"], np.float64))
+    np.testing.assert_array_equal(r1["idx"][0], np.array(ex["k1"]["idx"]))
+    np.testing.assert_allclose(r1["o"][0], np.array(ex["k1"]["o"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r1["lse"][0], np.array(ex["k1"]["lse"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r1["w"][0].sum(axis=1), 1.0, atol=1e-15)
+    r2 = oracle.decode(top_k=2, **kw)
+    np.testing.assert_array_equal(r2["idx"][0], np.array(ex["k2"]["idx"]))
+    np.testing.assert_allclose(r2["o"][0, 0], ex["k2"]["o_head0"], atol=1e-14)
+    np.testing.assert_allclose(r2["lse"][0, 0], ex["k2"]["lse_head0"], atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- top-k
+def _brute_force_topk(s, k):
+    """The unique k-subset S with: for i in S, j not in S, s_i > s_j or (s_i == s_j and i < j)."""
+    n = len(s)
+    keff = min(k, n)
+    winners = []
+    for S in itertools.combinations(range(n), keff):
+        inside = set(S)
+        if all((s[i] > s[j]) or (s[i] == s[j] and i < j)
+               for i in inside for j in range(n) if j not in inside):
+            winners.append(list(S))
+    assert len(winners) == 1
+    return winners[0] + [-1] * (k - keff)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_brute_force(seed):
+    r = np.random.default_rng(seed)
+    n = int(r.integers(1, 13))
+    k = int(r.integers(1, 6))
+    # integer-valued scores make ties frequent; half the cases also include -0.0 and +0.0
+    s = r.integers(-3, 4, size=n).astype(np.float64)
+    if seed % 2:
+        s[s == 0] = -0.0
+        s[::3] = np.where(s[::3] == 0, 0.0, s[::3])
+    got = oracle.topk(s, k)
+    assert list(got) == _brute_force_topk(list(s), k)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_topk_matches_stable_argsort(seed):
+    r = np.random.default_rng(100 + seed)
+    n = int(r.integers(50, 5000))
+    k = int(r.integers(1, 200))
+    s = np.round(r.standard_normal(n), 2)  # rounded: many ties
+    want = np.sort(np.argsort(-s, kind="stable")[:min(k, n)])
+    got = oracle.topk(s, k)
+    np.testing.assert_array_equal(got[:len(want)], want)
+    assert np.all(got[len(want):] == -1)
+
+
+def test_topk_special_cases():
+    np.testing.assert_array_equal(oracle.topk(np.full(10, 3.5), 4), [0, 1, 2, 3])
+    s = np.array([0.1, 0.9, -2.0, 0.9, 0.5])
+    np.testing.assert_array_equal(oracle.topk(s, 1), [1])          # first argmax
+    np.testing.assert_array_equal(oracle.topk(s, 8), [0, 1, 2, 3, 4, -1, -1, -1])  # k >= nb
+    np.testing.assert_array_equal(oracle.topk(np.array([-0.0, 0.0]), 1), [0])  # -0 == +0
+
+
+# ----------------------------------------------------------------------------- stage 1
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scores_equal_mean_token_scores(dtype):
+    """<mean of the group's queries, mean of the block's keys> = mean over (head, token) of
+    <q_h, k_t>: token-level scores, pooled, computed with numpy matmul."""
+    c = make_decode_case(B=2, Hq=6, Hkv=2, lens=[1000, 130], top_k=4, dtype=dtype, seed=3)
+    r = oracle.decode(**decode_inputs(c))
+    G = c.Hq // c.Hkv
+    for b in range(c.B):
+        N = int(c.seq_lens[b])
+        K = as_f64(storage(logical_kv(c.k_pool, c.block_table, b, N), dtype))
+        qb = as_f64(storage(c.q[b], dtype))
+        for g in range(c.Hkv):
+            tok = qb[g * G:(g + 1) * G] @ K[:, g, :].T   # [G][N]
+            nb = (N + c.P - 1) // c.P
+            want = [tok[:, j * c.P:min(N, (j + 1) * c.P)].mean() for j in range(nb)]
+            np.testing.assert_allclose(r["scores"][b, g, :nb], want, rtol=1e-12, atol=1e-12)
+            assert np.all(np.isneginf(r["scores"][b, g, nb:]))
+
+
+def test_scores_scale_exactly_with_power_of_two_query():
+    c = make_decode_case(B=1, Hq=8, Hkv=2, lens=[777], top_k=5, dtype="f32", seed=4)
+    kw = decode_inputs(c)
+    r = oracle.decode(**kw)
+    kw2 = dict(kw, q=(kw["q"] * np.float32(8.0)).astype(np.float32))
+    r2 = oracle.decode(**kw2)
+    np.testing.assert_array_equal(r2["scores"], r["scores"] * 8.0)
+    np.testing.assert_array_equal(r2["idx"], r["idx"])
+
+
+# ----------------------------------------------------------------------------- stage 2
+@pytest.mark.parametrize("dtype,lens,Hq,Hkv", [("f32", [640], 6, 2), ("bf16", [1000, 64, 1], 8, 2),
+                                               ("f32", [4096], 8, 1), ("bf16", [333], 32, 8)])
+def test_all_blocks_equals_dense_gqa(dtype, lens, Hq, Hkv):
+    """k >= nb: the sparse path must be dense GQA attention over the real K/V."""
+    nbmax = max((n + 63) // 64 for n in lens)
+    c = make_decode_case(B=len(lens), Hq=Hq, Hkv=Hkv, lens=lens, top_k=nbmax + 3, dtype=dtype, seed=5)
+    r = oracle.decode(**decode_inputs(c))
+    for b, N in enumerate(lens):
+        K = as_f64(storage(logical_kv(c.k_pool, c.block_table, b, N), dtype))
+        V = as_f64(storage(logical_kv(c.v_pool, c.block_table, b, N), dtype))
+        o, lse = dense_gqa(as_f64(storage(c.q[b], dtype)), K, V, c.scale)
+        np.testing.assert_allclose(r["o"][b], o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][b], lse, rtol=1e-12, atol=1e-12)
+        nb = (N + 63) // 64
+        assert list(r["idx"][b, 0, :nb]) == list(range(nb))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sparse_equals_masked_dense(seed):
+    """Attention over the gathered blocks == dense softmax with every unselected token masked."""
+    c = make_decode_case(B=2, Hq=6, Hkv=2, lens=[1500, 700], top_k=5, dtype="bf16", seed=seed,
+                         plant=("count", 2), permute=True)
+    r = oracle.decode(want_weights=True, **decode_inputs(c))
+    G = c.Hq // c.Hkv
+    for b in range(c.B):
+        N = int(c.seq_lens[b])
+        K = as_f64(storage(logical_kv(c.k_pool, c.block_table, b, N), "bf16"))
+        V = as_f64(storage(logical_kv(c.v_pool, c.block_table, b, N), "bf16"))
+        qb = as_f64(storage(c.q[b], "bf16"))
+        for g in range(c.Hkv):
+            sel = r["idx"][b, g]
+            assert len(set(sel[sel >= 0])) == (sel >= 0).sum() and np.all(np.diff(sel[sel >= 0]) > 0)
+            mask = np.isin(np.arange(N) // c.P, sel[sel >= 0])
+            o, lse = dense_gqa(qb[g * G:(g + 1) * G], K[:, g:g + 1], V[:, g:g + 1], c.scale, mask=mask)
+            np.testing.assert_allclose(r["o"][b, g * G:(g + 1) * G], o, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(r["lse"][b, g * G:(g + 1) * G], lse, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(r["w"][b, g * G:(g + 1) * G].sum(axis=1), 1.0, atol=1e-13)
+
+
+def test_closed_forms():
+    # one visible token: o is that value row, lse the single logit
+    c = make_decode_case(B=1, Hq=4, Hkv=1, lens=[1], top_k=1, dtype="f32", seed=6)
+    r = oracle.decode(**decode_inputs(c))
+    v0 = c.v_pool[c.block_table[0, 0], 0, 0].astype(np.float64)
+    k0 = c.k_pool[c.block_table[0, 0], 0, 0].astype(np.float64)
+    for h in range(4):
+        np.testing.assert_array_equal(r["o"][0, h], v0)
+        np.testing.assert_allclose(r["lse"][0, h], c.scale * float(c.q[0, h].astype(np.float64) @ k0), atol=1e-14)
+    # q = 0: uniform weights over the selected tokens -> o = their mean, lse = ln(count)
+    c = make_decode_case(B=1, Hq=4, Hkv=2, lens=[900], top_k=3, dtype="f32", seed=7)
+    kw = decode_inputs(c)
+    kw["q"] = np.zeros_like(kw["q"])
+    r = oracle.decode(**kw)
+    V = logical_kv(c.v_pool, c.block_table, 0, 900).astype(np.float64)
+    for g in range(2):
+        sel = r["idx"][0, g]
+        assert list(sel) == [0, 1, 2]  # all scores are 0: ties break to the lowest indices
+        toks = np.concatenate([np.arange(j * 64, min(900, j * 64 + 64)) for j in sel])
+        np.testing.assert_allclose(r["o"][0, 2 * g], V[toks, g].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(r["lse"][0, 2 * g], math.log(len(toks)), atol=1e-13)
+    # constant V: o = that constant whatever the weights
+    c = make_decode_case(B=1, Hq=8, Hkv=2, lens=[2000], top_k=4, dtype="bf16", seed=8)
+    kw = decode_inputs(c)
+    kw["v_pool"] = storage(np.full(c.v_pool.shape, 1.75, np.float32), "bf16")
+    r = oracle.decode(**kw)
+    np.testing.assert_allclose(r["o"], 1.75, rtol=1e-14)
+
+
+def test_empty_sequence():
+    c = make_decode_case(B=2, Hq=4, Hkv=2, lens=[0, 100], top_k=2, dtype="f32", seed=9)
+    r = oracle.decode(**decode_inputs(c))
+    assert np.all(r["idx"][0] == -1)
+    assert np.all(r["o"][0] == 0) and np.all(np.isneginf(r["lse"][0]))
+    assert np.all(np.isfinite(r["o"][1]))
+
+
+def test_page_permutation_invariance():
+    a = make_decode_case(B=2, Hq=8, Hkv=2, lens=[3000, 1234], top_k=6, dtype="bf16", seed=10)
+    kw = decode_inputs(a)
+    r1 = oracle.decode(**kw)
+    perm = np.random.default_rng(0).permutation(a.num_pages)   # new page id of old page p = perm[p]
+    k2 = np.empty_like(kw["k_pool"]); k2[perm] = kw["k_pool"]
+    v2 = np.empty_like(kw["v_pool"]); v2[perm] = kw["v_pool"]
+    t2 = np.where(a.block_table >= 0, perm[np.maximum(a.block_table, 0)], -1).astype(np.int32)
+    r2 = oracle.decode(**dict(kw, k_pool=k2, v_pool=v2, block_table=t2))
+    for key in ("scores", "idx", "o", "lse"):
+        np.testing.assert_array_equal(r1[key], r2[key])
+
+
+def test_idx_override_and_padding():
+    c = make_decode_case(B=1, Hq=4, Hkv=1, lens=[500], top_k=4, dtype="f32", seed=11)
+    kw = decode_inputs(c)
+    forced = np.array([[[7, 2, -1, 99]]], np.int32)     # unsorted, padded, out-of-range entry
+    r = oracle.decode(idx_in=forced, **kw)
+    mask = np.isin(np.arange(500) // 64, [2, 7])
+    K = logical_kv(c.k_pool, c.block_table, 0, 500).astype(np.float64)
+    V = logical_kv(c.v_pool, c.block_table, 0, 500).astype(np.float64)
+    o, lse = dense_gqa(c.q[0].astype(np.float64), K, V, c.scale, mask=mask)
+    np.testing.assert_allclose(r["o"][0], o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["lse"][0], lse, rtol=1e-12)
+
+
+def test_precomputed_summaries_agree():
+    c = make_decode_case(B=3, Hq=8, Hkv=2, lens=[1000, 64, 65], top_k=3, dtype="bf16", seed=12, permute=True)
+    kw = decode_inputs(c)
+    S = oracle.summaries(k_pool=kw["k_pool"], block_table=c.block_table, seq_lens=c.seq_lens,
+                         Hkv=c.Hkv, D=c.D, P=c.P)
+    r1 = oracle.decode(**kw)
+    r2 = oracle.decode(summaries_in=S, **kw)
+    for key in ("scores", "idx", "o", "lse"):
+        np.testing.assert_array_equal(r1[key], r2[key])
+    # partial block: mean over the valid tokens only (the padded slots hold a large constant)
+    last = as_f64(kw["k_pool"][c.block_table[2, 1], :, :1, :]).mean(axis=1)
+    np.testing.assert_allclose(S[2, 1], last, rtol=1e-15)
+
+
+@pytest.mark.parametrize("name,shape", [("small_fp32", dict(B=1, Hq=8, Hkv=1, lens=[4096], top_k=16, dtype="f32", plant=("count", 3))),
+                                        ("small_bf16", dict(B=2, Hq=32, Hkv=8, lens=[8192, 8192], top_k=32, dtype="bf16", plant=("frac", 0.01)))])
+def test_planted_blocks_are_found(name, shape):
+    """Sanity of the input recipe: blocks lifted along the group's query direction rank high."""
+    c = make_decode_case(seed=13, **shape)
+    r = oracle.decode(**decode_inputs(c))
+    hit = tot = 0
+    for (b, g), blocks in c.planted.items():
+        hit += len(set(blocks) & set(r["idx"][b, g]))
+        tot += len(blocks)
+    assert hit / tot >= 0.9
+
+
+# ----------------------------------------------------------------------------- prefill
+@pytest.mark.parametrize("past_len,T,dtype", [(256, 128, "f32"), (128, 100, "bf16"), (0, 130, "f32")])
+def test_prefill_all_blocks_equals_dense_causal(past_len, T, dtype):
+    c = make_prefill_case(Hq=8, Hkv=2, past_len=past_len, T=T, top_k=64, dtype=dtype, seed=14)
+    kw = prefill_inputs(c)
+    r = oracle.prefill(**kw)
+    N = past_len + T
+    Kc = logical_kv(c.k_pool, c.block_table, 0, past_len) if past_len else np.zeros((0, 2, 128), np.float32)
+    Vc = logical_kv(c.v_pool, c.block_table, 0, past_len) if past_len else np.zeros((0, 2, 128), np.float32)
+    K = as_f64(storage(np.concatenate([Kc, c.k_new]), dtype))
+    V = as_f64(storage(np.concatenate([Vc, c.v_new]), dtype))
+    mask = np.arange(N)[None, :] <= (past_len + np.arange(T))[:, None]
+    o, lse = dense_gqa(as_f64(kw["q"]), K, V, c.scale, mask=mask)
+    np.testing.assert_allclose(r["o"], o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-12, atol=1e-12)
+    ntiles = (T + 63) // 64
+    for tau in range(ntiles):
+        d = past_len // 64 + tau
+        assert list(r["idx"][tau, 0, :d + 1]) == list(range(d + 1))
+
+
+def test_prefill_k0_is_local_causal():
+    c = make_prefill_case(Hq=4, Hkv=1, past_len=192, T=150, top_k=0, dtype="f32", seed=15)
+    r = oracle.prefill(**prefill_inputs(c))
+    for tau in range(3):
+        rows = slice(tau * 64, min(150, tau * 64 + 64))
+        n = rows.stop - rows.start
+        K = c.k_new[rows].astype(np.float64)
+        V = c.v_new[rows].astype(np.float64)
+        mask = np.tril(np.ones((n, n), bool))
+        o, lse = dense_gqa(c.q[rows].astype(np.float64), K, V, c.scale, mask=mask)
+        np.testing.assert_allclose(r["o"][rows], o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][rows], lse, rtol=1e-12, atol=1e-12)
+        assert r["idx"][tau, 0, 0] == 3 + tau
+
+
+def test_prefill_selection_and_tile_scores():
+    """Tile scores = mean over the tile's (row, head, token) scores; selection = oracle top-k over
+    the blocks before the diagonal, then the diagonal appended; sampled tiles agree with a full run."""
+    c = make_prefill_case(Hq=8, Hkv=2, past_len=640, T=200, top_k=3, dtype="bf16", seed=16)
+    kw = prefill_inputs(c)
+    r = oracle.prefill(**kw)
+    part = oracle.prefill(tiles=(1, 3), **kw)
+    np.testing.assert_array_equal(part["o"][64:192], r["o"][64:192])
+    np.testing.assert_array_equal(part["idx"][1:3], r["idx"][1:3])
+    G = 4
+    K = as_f64(storage(np.concatenate([logical_kv(c.k_pool, c.block_table, 0, 640), c.k_new]), "bf16"))
+    q = as_f64(kw["q"])
+    for tau in range(4):
+        rows = slice(tau * 64, min(200, tau * 64 + 64))
+        d = 10 + tau
+        for g in range(2):
+            tok = q[rows, g * G:(g + 1) * G].reshape(-1, 128) @ K[:, g].T
+            want = np.array([tok[:, j * 64:(j + 1) * 64].mean() for j in range(d)])
+            np.testing.assert_allclose(r["scores"][tau, g, :d], want, rtol=1e-12, atol=1e-12)
+            sel = oracle.topk(want, 3)
+            assert list(r["idx"][tau, g]) == list(sel) + [d]
