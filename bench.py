@@ -1,0 +1,287 @@
+#!/usr/bin/env python
+"""Benchmark of two-stage GQA block-sparse attention on one MI355X.
+
+Headline: sparse decode at 1M-token context (batch 1, 32 query / 8 KV heads, head_dim 128,
+64-token blocks, top-64 blocks, bf16 paged KV cache with permuted pages). One step = one full
+decode step: append the new token and refresh its block summary, score every block, top-k,
+gather-attend over the selected blocks, merge. Also reported: selected-KV bandwidth of the
+attend stage against HBM peak, the stage-1 scan bandwidth, sparse prefill TFLOP/s (4096 new
+tokens on a 262,144-token cache, top-32 + diagonal per 64-query tile), and the CPU oracle's
+rate on a bounded sample of the same decode workload.
+
+Timing: inputs are resident in HBM before the timed region; steps rotate over --layers
+independent caches (4 x 4 GiB by default, far beyond the 256 MB infinity cache) and over fresh
+queries; the steps are captured once in a HIP graph and replayed; HIP events on the launch
+stream bracket exactly --steps steps, with a device synchronisation on both sides.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode tokens/s + KV GB/s (% HBM peak) at 1M ctx; prefill TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def selected_kv_bytes(idx, lens, P=64, D=128, elem=2):
+    """K+V bytes the attend stage must read: valid tokens of every selected block."""
+    import numpy as np
+    idx = idx.cpu().numpy()
+    total = 0
+    for b in range(idx.shape[0]):
+        n = int(lens[b])
+        nb = (n + P - 1) // P
+        for g in range(idx.shape[1]):
+            for j in idx[b, g]:
+                if 0 <= j < nb:
+                    total += min(P, n - j * P) * D * elem * 2
+    return total
+
+
+def timed_graph(fn_steps, nsteps_graph, torch):
+    """Capture nsteps_graph calls of fn_steps(i) (after one eager pass) in a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(nsteps_graph):   # eager warm pass on the capture stream
+            fn_steps(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nsteps_graph):
+            fn_steps(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def run_graph(g, replays, torch):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
+    ap.add_argument("--workload", default="decode_bf16_1m_paged")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import long_context_sparse_select_amd as msa
+    from synth import make_decode_case_torch, make_prefill_case_torch, workload
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    kw = workload(args.workload, seed=args.seed)
+    L = max(1, args.layers)
+    log("generating %d caches of %s" % (L, args.workload))
+    caches, cases = [], []
+    for layer in range(L):
+        kwl = dict(kw, seed=args.seed + 1000 * layer)
+        c = make_decode_case_torch(device=dev, **kwl)
+        table = torch.from_numpy(c.block_table).to(dev)
+        lens = torch.from_numpy(c.seq_lens).to(dev)
+        S = torch.empty((c.num_pages, c.Hkv, c.D), dtype=torch.float32, device=dev)
+        cache = msa.KVCache(c.k_pool, c.v_pool, S, table, lens)
+        cfg = msa.make_config(c.Hq, c.Hkv, c.top_k, dtype=c.dtype, softmax_scale=c.scale)
+        msa.msa_build_summaries(cfg, cache, c.B, c.max_seq_len)
+        caches.append(cache)
+        cases.append(c)
+    c0 = cases[0]
+    B, Hq, Hkv, D, k = c0.B, c0.Hq, c0.Hkv, c0.D, c0.top_k
+    max_len = c0.max_seq_len
+    tdt = torch.bfloat16 if c0.dtype == "bf16" else torch.float32
+    R = 8
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 77)
+    q_ring = [torch.randn((B, Hq, D), generator=gen, device=dev).to(tdt) for _ in range(R)]
+    kn_ring = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(tdt) for _ in range(R)]
+    vn_ring = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(tdt) for _ in range(R)]
+    out = torch.empty((B, Hq, D), dtype=tdt, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    idx_bufs = [torch.empty((B, Hkv, k), dtype=torch.int32, device=dev) for _ in range(L)]
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def decode(i):
+        layer = i % L
+        msa.msa_decode_step(cfg, q_ring[i % R], caches[layer], B, max_len, out, k_new=kn_ring[i % R],
+                            v_new=vn_ring[i % R], idx_out=idx_bufs[layer], lse_out=lse, workspace=ws)
+
+    def select(i):
+        layer = i % L
+        msa.msa_select(cfg, q_ring[i % R], caches[layer], B, max_len, idx_bufs[layer], workspace=ws)
+
+    def attend(i):
+        layer = i % L
+        msa.msa_attend(cfg, q_ring[i % R], caches[layer], B, max_len, idx_bufs[layer], out, lse_out=lse,
+                       workspace=ws)
+
+    per_graph = L * R // math.gcd(L, R) if L * R <= 64 else L
+    replays = max(1, args.steps // per_graph)
+    steps = replays * per_graph
+    wreplays = max(1, args.warmup // per_graph)
+
+    g_dec = timed_graph(decode, per_graph, torch)
+    run_graph(g_dec, wreplays, torch)
+    t_step = run_graph(g_dec, replays, torch) / steps
+    log("decode step: %.2f us" % (t_step * 1e6))
+
+    # stage timings (same rotation): Step 1 (score + top-k) and Step 2 (attend + merge)
+    g_sel = timed_graph(select, per_graph, torch)
+    run_graph(g_sel, wreplays, torch)
+    t_sel = run_graph(g_sel, replays, torch) / steps
+    g_att = timed_graph(attend, per_graph, torch)
+    run_graph(g_att, wreplays, torch)
+    t_att = run_graph(g_att, replays, torch) / steps
+    torch.cuda.synchronize()
+    kv_bytes = np.mean([selected_kv_bytes(idx_bufs[l], cases[l].seq_lens, elem=2 if c0.dtype == "bf16" else 4)
+                        for l in range(L)])
+    nb_tot = sum((int(n) + 63) // 64 for n in c0.seq_lens)
+    s1_bytes = nb_tot * Hkv * D * 4
+    kv_gbps = kv_bytes / t_att / 1e9
+    s1_gbps = s1_bytes / t_sel / 1e9
+    log("select %.2f us (%.0f GB/s of summaries); attend %.2f us (%.0f GB/s of selected KV)"
+        % (t_sel * 1e6, s1_gbps, t_att * 1e6, kv_gbps))
+
+    rec = {
+        "metric": METRIC,
+        "value": B / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wreplays * per_graph,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c0.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, planted blocks, permuted 64-token pages)",
+        "config": {"workload": args.workload, "batch": B, "context": int(max_len), "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block": 64, "top_k": k,
+                   "caches_rotated": L, "graph_steps": per_graph},
+        "kv_GBps": kv_gbps,
+        "kv_hbm_frac": kv_gbps / HBM_PEAK_GBPS,
+        "stage1_GBps": s1_gbps,
+        "stage1_us": t_sel * 1e6,
+        "attend_us": t_att * 1e6,
+        "roofline": {"bound": "hbm", "kernel": "msa_attend (gather-attend + merge)",
+                     "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": kv_bytes},
+    }
+
+    # ---- prefill
+    if not args.no_prefill:
+        try:
+            rec["prefill"] = bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev)
+        except msa.MsaError as e:
+            log("prefill skipped: %s" % e)
+            rec["prefill"] = None
+    # ---- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args, cases[0], caches[0], torch, np)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
+    kw = workload("prefill_bf16_4k_on_256k", seed=args.seed)
+    p = make_prefill_case_torch(device=dev, **kw)
+    table = torch.from_numpy(p.block_table).to(dev)
+    S = torch.empty((p.num_pages, p.Hkv, p.D), dtype=torch.float32, device=dev)
+    cache = msa.KVCache(p.k_pool, p.v_pool, S, table, torch.tensor([p.past_len], dtype=torch.int32, device=dev))
+    cfg = msa.make_config(p.Hq, p.Hkv, p.top_k, dtype="bf16", softmax_scale=p.scale)
+    msa.msa_build_summaries(cfg, cache, 1, p.past_len)
+    out = torch.empty_like(p.q)
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_PREFILL, 1, p.past_len + p.T, p.T),
+                     dtype=torch.uint8, device=dev)
+
+    def chunk(i):
+        msa.msa_prefill_chunk(cfg, p.q, p.k_new, p.v_new, cache, p.past_len, p.T, out, workspace=ws)
+
+    chunk(0)
+    torch.cuda.synchronize()
+    g = timed_graph(chunk, 1, torch)
+    run_graph(g, 3, torch)
+    n = 20
+    t = run_graph(g, n, torch) / n
+    ntiles = (p.T + 63) // 64
+    pairs = 0
+    for tau in range(ntiles):
+        rows = min(64, p.T - tau * 64)
+        keff = min(p.top_k, p.past_len // 64 + tau)
+        pairs += rows * 64 * keff + rows * (rows + 1) // 2
+    flops = 4.0 * p.D * p.Hq * pairs
+    tf = flops / t / 1e12
+    log("prefill chunk: %.1f us, %.1f TFLOP/s (causal-visible, whole chunk)" % (t * 1e6, tf))
+    return {"workload": "prefill_bf16_4k_on_256k", "chunk_us": t * 1e6, "TFLOPs": tf,
+            "bf16_mfma_frac": tf / BF16_PEAK_TFLOPS, "flops": flops,
+            "note": "whole chunk: append + summaries + tile query + score + top-k + MFMA attend"}
+
+
+def cpu_baseline(args, case, cache, torch, np):
+    """The fp64 oracle (untuned) on a bounded sample of the same decode workload: select from
+    cached block summaries + attend, for as many steps as fit in about --cpu-seconds."""
+    import oracle
+
+    def host_storage(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+    q = host_storage(case.q)
+    k = host_storage(case.k_pool)
+    v = host_storage(case.v_pool)
+    S = oracle.summaries(k_pool=k, block_table=case.block_table, seq_lens=case.seq_lens, Hkv=case.Hkv,
+                         D=case.D, P=case.P)
+    units = case.B * case.Hkv
+    threads = min(oracle.default_threads(), units)
+    kw = dict(q=q, k_pool=k, v_pool=v, block_table=case.block_table, seq_lens=case.seq_lens, Hq=case.Hq,
+              Hkv=case.Hkv, top_k=case.top_k, scale=case.scale, P=case.P, summaries_in=S, nthreads=threads)
+    t0 = time.perf_counter()
+    oracle.decode(**kw)
+    one = time.perf_counter() - t0
+    n = int(max(2, min(200, args.cpu_seconds / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        oracle.decode(**kw)
+    dt = time.perf_counter() - t0
+    log("cpu oracle: %d steps in %.1f s on %d threads" % (n, dt, threads))
+    return {"value": n * case.B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cores": os.cpu_count(),
+            "sample": "%d decode steps (select from cached fp64 summaries + attend) of the same 1M-token "
+                      "workload, fp64 C oracle, threads over (sequence, KV group) units" % n}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,321 @@
+// libmsa C ABI: argument validation, workspace layout and the launch sequence of each entry
+// point. The contract of every function is stated in include/msa.h.
+//
+// Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
+// §1 Steps 1-2; §3 decode / prefill):
+//   msa_decode_step   [append + block summary] -> score (+histogram) -> top-k -> attend -> merge
+//   msa_prefill_chunk append + summaries -> tile query -> score -> top-k (+diagonal) -> attend
+// Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
+// HIP call, so an invalid call enqueues nothing.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "msa.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace msa;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t scores = 0, hist = 0, idx = 0, qtile = 0, part_o = 0, part_ml = 0, total = 0;
+  int row_stride = 0;   // scores per row
+  int bps = 1, nsplit = 0;
+};
+
+msa_status check_config(const msa_config* c) {
+  if (c == nullptr) return MSA_ERR_INVALID_ARG;
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->num_q_heads % c->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (c->top_k < 1) return MSA_ERR_INVALID_ARG;
+  if (c->q_dtype != MSA_F32 && c->q_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
+  if (c->kv_dtype != MSA_F32 && c->kv_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
+  if (c->out_dtype != MSA_F32 && c->out_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
+  if (c->score_mode != MSA_SCORE_MEAN_KEY && c->score_mode != MSA_SCORE_MAX_TOKEN) return MSA_ERR_INVALID_ARG;
+  if (!std::isfinite(c->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (c->head_dim != MSA_HEAD_DIM || c->block_size != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
+  if (c->top_k > MSA_MAX_TOP_K) return MSA_ERR_UNSUPPORTED;
+  if (c->num_q_heads / c->num_kv_heads > MSA_MAX_GROUP) return MSA_ERR_UNSUPPORTED;
+  if (c->num_kv_heads > MSA_MAX_KV_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (c->kv_dtype != c->q_dtype || c->out_dtype != c->q_dtype) return MSA_ERR_UNSUPPORTED;
+  if (c->score_mode != MSA_SCORE_MEAN_KEY) return MSA_ERR_UNSUPPORTED;
+  if (c->keep_local != 0) return MSA_ERR_UNSUPPORTED;
+  if (c->q_tile != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+// decode-side layouts (op = SELECT, ATTEND or DECODE)
+Layout decode_layout(const msa_config* c, int op, int B, int max_len) {
+  Layout L;
+  const int Hkv = c->num_kv_heads, Hq = c->num_q_heads, k = c->top_k;
+  const size_t rows = (size_t)B * Hkv;
+  L.row_stride = (max_len + MSA_BLOCK - 1) / MSA_BLOCK;
+  L.bps = decode_blocks_per_split(B, Hkv, k);
+  L.nsplit = (k + L.bps - 1) / L.bps;
+  const bool sel = op == MSA_OP_SELECT || op == MSA_OP_DECODE;
+  const bool att = op == MSA_OP_ATTEND || op == MSA_OP_DECODE;
+  size_t off = 0;
+  if (sel) {
+    L.scores = off; off += align256(rows * (size_t)(L.row_stride > 0 ? L.row_stride : 1) * sizeof(float));
+    L.hist = off;   off += align256(rows * (size_t)kHistBins * sizeof(uint32_t));
+  }
+  if (op == MSA_OP_DECODE) { L.idx = off; off += align256(rows * (size_t)k * sizeof(int32_t)); }
+  if (att) {
+    L.part_o = off;  off += align256((size_t)B * Hq * L.nsplit * kD * sizeof(float));
+    L.part_ml = off; off += align256((size_t)B * Hq * L.nsplit * 2 * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+Layout prefill_layout(const msa_config* c, int max_len, int T) {
+  Layout L;
+  const int Hkv = c->num_kv_heads, k = c->top_k;
+  const int ntiles = (T + kP - 1) / kP;
+  const size_t rows = (size_t)ntiles * Hkv;
+  L.row_stride = (max_len + kP - 1) / kP;
+  size_t off = 0;
+  L.scores = off; off += align256(rows * (size_t)(L.row_stride > 0 ? L.row_stride : 1) * sizeof(float));
+  L.hist = off;   off += align256(rows * (size_t)kHistBins * sizeof(uint32_t));
+  L.qtile = off;  off += align256(rows * (size_t)kD * sizeof(float));
+  L.idx = off;    off += align256(rows * (size_t)(k + 1) * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
+
+msa_status check_cache(const msa_kv_cache* cache, bool need_kv, bool need_lens) {
+  if (cache == nullptr || cache->summaries == nullptr || cache->block_table == nullptr) return MSA_ERR_INVALID_ARG;
+  if (need_kv && (cache->k_pages == nullptr || cache->v_pages == nullptr)) return MSA_ERR_INVALID_ARG;
+  if (need_lens && cache->seq_lens == nullptr) return MSA_ERR_INVALID_ARG;
+  if (cache->num_pages < 0 || cache->max_blocks < 1) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+msa_status check_batch(const msa_kv_cache* cache, int B, int max_len) {
+  if (B < 0 || max_len < 0) return MSA_ERR_INVALID_ARG;
+  if ((long long)max_len > (long long)cache->max_blocks * MSA_BLOCK) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+CacheArgs cache_args(const msa_kv_cache* c) {
+  return CacheArgs{c->k_pages, c->v_pages, c->summaries, c->block_table, c->seq_lens, c->num_pages, c->max_blocks};
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+#define MSA_TRY(expr)                        \
+  do {                                       \
+    const msa_status s_ = (expr);            \
+    if (s_ != MSA_OK) return s_;             \
+  } while (0)
+
+// Step 1 on validated arguments
+msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                      float* scores, uint32_t* hist, int row_stride, int32_t* idx, hipStream_t st) {
+  const bool bf16 = cfg->q_dtype == MSA_BF16;
+  const CacheArgs ca = cache_args(cache);
+  MSA_TRY(hip_status(launch_score_decode(bf16, q, ca, B, cfg->num_q_heads, cfg->num_kv_heads, max_len, scores,
+                                         row_stride, hist, st)));
+  TopkArgs t{};
+  t.scores = scores;
+  t.row_stride = row_stride;
+  t.hist = hist;
+  t.idx = idx;
+  t.idx_stride = cfg->top_k;
+  t.rows = B * cfg->num_kv_heads;
+  t.k = cfg->top_k;
+  t.Hkv = cfg->num_kv_heads;
+  t.lens = cache->seq_lens;
+  t.max_len = max_len;
+  t.base_blocks = 0;
+  return hip_status(launch_topk(t, st));
+}
+
+// Step 2 on validated arguments
+msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                      const int32_t* idx, void* out, float* lse, const Layout& L, void* ws, hipStream_t st) {
+  AttendArgs a{};
+  a.q = q;
+  a.kpool = cache->k_pages;
+  a.vpool = cache->v_pages;
+  a.table = cache->block_table;
+  a.lens = cache->seq_lens;
+  a.idx = idx;
+  a.num_pages = cache->num_pages;
+  a.max_blocks = cache->max_blocks;
+  a.max_len = max_len;
+  a.B = B;
+  a.Hq = cfg->num_q_heads;
+  a.Hkv = cfg->num_kv_heads;
+  a.k = cfg->top_k;
+  a.scale_log2 = cfg->softmax_scale * kLog2e;
+  a.blocks_per_split = L.bps;
+  a.nsplit = L.nsplit;
+  a.part_o = at<float>(ws, L.part_o);
+  a.part_ml = at<float>(ws, L.part_ml);
+  a.out = out;
+  a.lse = lse;
+  return hip_status(launch_attend_decode(cfg->q_dtype == MSA_BF16, a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_workspace_size(const msa_config* cfg, int32_t op, int32_t batch, int32_t max_seq_len,
+                              int32_t chunk_len, size_t* bytes) {
+  MSA_TRY(check_config(cfg));
+  if (bytes == nullptr || batch < 0 || max_seq_len < 0) return MSA_ERR_INVALID_ARG;
+  switch (op) {
+    case MSA_OP_SELECT:
+    case MSA_OP_ATTEND:
+    case MSA_OP_DECODE:
+      *bytes = decode_layout(cfg, op, batch, max_seq_len).total;
+      return MSA_OK;
+    case MSA_OP_PREFILL:
+      if (chunk_len < 1 || batch != 1 || max_seq_len < chunk_len) return MSA_ERR_INVALID_ARG;
+      *bytes = prefill_layout(cfg, max_seq_len, chunk_len).total;
+      return MSA_OK;
+    default:
+      return MSA_ERR_INVALID_ARG;
+  }
+}
+
+msa_status msa_build_summaries(const msa_config* cfg, const msa_kv_cache* cache, int32_t batch,
+                               int32_t max_seq_len, void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, false, true));
+  if (cache->k_pages == nullptr) return MSA_ERR_INVALID_ARG;
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (batch == 0) return MSA_OK;
+  return hip_status(launch_build_summaries(cfg->kv_dtype == MSA_BF16, cache_args(cache), batch, cfg->num_kv_heads,
+                                           max_seq_len, (hipStream_t)stream));
+}
+
+msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
+                      int32_t max_seq_len, float* scores_out, int32_t* idx_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, false, true));
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (q == nullptr || idx_out == nullptr) return MSA_ERR_INVALID_ARG;
+  const Layout L = decode_layout(cfg, MSA_OP_SELECT, batch, max_seq_len);
+  if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
+  if (batch == 0) return MSA_OK;
+  float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
+  return run_select(cfg, q, cache, batch, max_seq_len, scores, at<uint32_t>(workspace, L.hist), L.row_stride,
+                    idx_out, (hipStream_t)stream);
+}
+
+msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
+                      int32_t max_seq_len, const int32_t* idx, void* out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, true, true));
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (q == nullptr || idx == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  const Layout L = decode_layout(cfg, MSA_OP_ATTEND, batch, max_seq_len);
+  if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
+  if (batch == 0) return MSA_OK;
+  return run_attend(cfg, q, cache, batch, max_seq_len, idx, out, lse_out, L, workspace, (hipStream_t)stream);
+}
+
+msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
+                           int32_t max_seq_len, const void* k_new, const void* v_new, int32_t* idx_out,
+                           float* scores_out, void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, true, true));
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (q == nullptr || out == nullptr || ((k_new == nullptr) != (v_new == nullptr))) return MSA_ERR_INVALID_ARG;
+  const Layout L = decode_layout(cfg, MSA_OP_DECODE, batch, max_seq_len);
+  if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
+  if (batch == 0) return MSA_OK;
+  const hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = cfg->q_dtype == MSA_BF16;
+  if (k_new != nullptr)
+    MSA_TRY(hip_status(launch_append_decode(bf16, cache_args(cache), k_new, v_new, batch, cfg->num_kv_heads,
+                                            max_seq_len, st)));
+  float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
+  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, at<uint32_t>(workspace, L.hist), L.row_stride, idx,
+                     st));
+  return run_attend(cfg, q, cache, batch, max_seq_len, idx, out, lse_out, L, workspace, st);
+}
+
+msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k_new, const void* v_new,
+                             const msa_kv_cache* cache, int32_t past_len, int32_t T, int32_t* idx_out,
+                             float* scores_out, void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, true, false));
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (T < 1 || past_len < 0) return MSA_ERR_INVALID_ARG;
+  if ((long long)past_len + T > (long long)cache->max_blocks * MSA_BLOCK) return MSA_ERR_INVALID_ARG;
+  if (past_len % MSA_BLOCK != 0) return MSA_ERR_UNSUPPORTED;
+  if (cfg->q_dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  const int max_len = past_len + T;
+  const Layout L = prefill_layout(cfg, max_len, T);
+  if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
+  const hipStream_t st = (hipStream_t)stream;
+  const int Hkv = cfg->num_kv_heads, Hq = cfg->num_q_heads;
+  const int past_blocks = past_len / kP, ntiles = (T + kP - 1) / kP;
+  const CacheArgs ca = cache_args(cache);
+  float* qtile = at<float>(workspace, L.qtile);
+  float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
+  uint32_t* hist = at<uint32_t>(workspace, L.hist);
+
+  MSA_TRY(hip_status(launch_append_prefill(true, ca, k_new, v_new, past_blocks, T, Hkv, st)));
+  MSA_TRY(hip_status(launch_tile_query(true, q, T, Hq, Hkv, qtile, st)));
+  MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, hist, st)));
+  TopkArgs t{};
+  t.scores = scores;
+  t.row_stride = L.row_stride;
+  t.hist = hist;
+  t.idx = idx;
+  t.idx_stride = cfg->top_k + 1;
+  t.rows = ntiles * Hkv;
+  t.k = cfg->top_k;
+  t.Hkv = Hkv;
+  t.lens = nullptr;
+  t.max_len = max_len;
+  t.base_blocks = past_blocks;
+  MSA_TRY(hip_status(launch_topk(t, st)));
+  PrefillArgs p{};
+  p.q = q;
+  p.kpool = cache->k_pages;
+  p.vpool = cache->v_pages;
+  p.table = cache->block_table;
+  p.idx = idx;
+  p.num_pages = cache->num_pages;
+  p.past_len = past_len;
+  p.T = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.k = cfg->top_k;
+  p.scale_log2 = cfg->softmax_scale * kLog2e;
+  p.out = out;
+  p.lse = lse_out;
+  return hip_status(launch_attend_prefill(p, st));
+}
+
+const char* msa_status_string(msa_status status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: a required pointer is null or a count/size is invalid";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: valid configuration that this library does not implement";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace is null or smaller than msa_workspace_size()";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown msa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal launchers of libmsa (host side). Every launcher enqueues on `st` and returns the
+// launch status; all argument validation happens before, in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct CacheArgs {
+  void* k;               // [num_pages][Hkv][64][128]
+  void* v;
+  float* S;              // [num_pages][Hkv][128]
+  const int32_t* table;  // [B][max_blocks]
+  const int32_t* lens;   // [B] (decode paths)
+  int num_pages;
+  int max_blocks;
+};
+
+// ---- block summaries / append
+hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv, int max_len, hipStream_t st);
+hipError_t launch_append_decode(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new, int B,
+                                int Hkv, int max_len, hipStream_t st);
+hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
+                                 int past_blocks, int T, int Hkv, hipStream_t st);
+
+// ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats
+// each; hist rows hold kHistBins counters per row (added to, then cleared by the top-k kernel).
+hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
+                               int max_len, float* scores, int row_stride, uint32_t* hist, hipStream_t st);
+hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st);
+hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
+                                float* scores, int row_stride, uint32_t* hist, hipStream_t st);
+
+// ---- Step 1 top-k
+struct TopkArgs {
+  const float* scores;
+  int row_stride;
+  uint32_t* hist;
+  int32_t* idx;
+  int idx_stride;      // top_k (decode) or top_k + 1 (prefill)
+  int rows;
+  int k;
+  int Hkv;
+  const int32_t* lens; // decode: n = ceil(clamp(lens[row / Hkv]) / 64); null -> prefill mode
+  int max_len;
+  int base_blocks;     // prefill: n = base_blocks + row / Hkv, and block n is appended
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+// ---- Step 2, decode
+struct AttendArgs {
+  const void* q;        // [B][Hq][128]
+  const void* kpool;    // pools
+  const void* vpool;
+  const int32_t* table;
+  const int32_t* lens;
+  const int32_t* idx;   // [B][Hkv][k]
+  int num_pages, max_blocks, max_len;
+  int B, Hq, Hkv, k;
+  float scale_log2;     // softmax_scale * log2(e)
+  int blocks_per_split, nsplit;
+  float* part_o;        // [B][Hq][nsplit][128]
+  float* part_ml;       // [B][Hq][nsplit][2]
+  void* out;            // [B][Hq][128]
+  float* lse;           // nullable [B][Hq]
+};
+int decode_blocks_per_split(int B, int Hkv, int k);
+hipError_t launch_attend_decode(bool bf16, const AttendArgs& a, hipStream_t st);
+
+// ---- Step 2, prefill (bf16, MFMA)
+struct PrefillArgs {
+  const void* q;        // [T][Hq][128] bf16
+  const void* kpool;    // pools (bf16)
+  const void* vpool;
+  const int32_t* table; // [max_blocks] of the one sequence
+  const int32_t* idx;   // [ntiles][Hkv][k+1]
+  int num_pages, past_len, T, Hq, Hkv, k;
+  float scale_log2;
+  void* out;            // [T][Hq][128] bf16
+  float* lse;           // nullable [T][Hq]
+};
+hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace msa

@@ -1,0 +1,144 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every function that
+include/msa.h declares, sizes workspaces, and rejects invalid calls on the host before any
+HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+lib_mod = pytest.importorskip("long_context_sparse_select_amd._lib")
+L = lib_mod
+if not os.path.exists(L.library_path()):
+    pytest.skip("libmsa.so is not built", allow_module_level=True)
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:msa_status|const char\*)\s+(msa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.load_library()
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert L.msa_status_string(s).startswith("MSA_")
+    assert "unknown" in L.msa_status_string(99)
+
+
+def cfg(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, top_k=64, dtype="bf16")
+    base.update(kw)
+    return L.make_config(**base)
+
+
+def ws_size(c, op, B=1, max_len=1 << 20, T=0):
+    n = ctypes.c_size_t(0)
+    st = L.load_library().msa_workspace_size(ctypes.byref(c), op, B, max_len, T, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    c = cfg()
+    st, sel = ws_size(c, L.MSA_OP_SELECT)
+    assert st == 0
+    # scores 8 x 16384 fp32 + 8 histogram rows of 4096 counters
+    assert sel == 8 * 16384 * 4 + 8 * 4096 * 4
+    st, att = ws_size(c, L.MSA_OP_ATTEND)
+    assert st == 0 and att > 0
+    st, dec = ws_size(c, L.MSA_OP_DECODE)
+    assert st == 0 and dec >= sel + att
+    st, pre = ws_size(c, L.MSA_OP_PREFILL, 1, 262144 + 4096, 4096)
+    assert st == 0 and pre > 0
+    assert ws_size(c, L.MSA_OP_PREFILL, 2, 4096, 64)[0] == L.MSA_ERR_INVALID_ARG
+    assert ws_size(c, 17)[0] == L.MSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 0, L.MSA_ERR_INVALID_ARG),
+    ("num_q_heads", 30, L.MSA_ERR_INVALID_ARG),        # Hq % Hkv != 0
+    ("num_kv_heads", 2, L.MSA_ERR_UNSUPPORTED),       # group of 16 > 8
+    ("top_k", 0, L.MSA_ERR_INVALID_ARG),
+    ("top_k", 5000, L.MSA_ERR_UNSUPPORTED),
+    ("head_dim", 64, L.MSA_ERR_UNSUPPORTED),
+    ("block_size", 128, L.MSA_ERR_UNSUPPORTED),
+    ("q_dtype", 7, L.MSA_ERR_INVALID_ARG),
+    ("kv_dtype", 0, L.MSA_ERR_UNSUPPORTED),            # mixed q / kv types
+    ("score_mode", 1, L.MSA_ERR_UNSUPPORTED),          # block max pool: not implemented
+    ("score_mode", 5, L.MSA_ERR_INVALID_ARG),
+    ("keep_local", 1, L.MSA_ERR_UNSUPPORTED),
+    ("q_tile", 32, L.MSA_ERR_UNSUPPORTED),
+    ("softmax_scale", float("nan"), L.MSA_ERR_INVALID_ARG),
+])
+def test_config_validation(field, value, status):
+    c = cfg()
+    setattr(c, field, value)
+    assert ws_size(c, L.MSA_OP_DECODE)[0] == status
+
+
+def fake_cache(max_blocks=16, num_pages=16, **kw):
+    c = L.MsaKvCache(FAKE, FAKE, FAKE, FAKE, FAKE, num_pages, max_blocks)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def call_decode(c, cache, B=1, max_len=1024, q=FAKE, out=FAKE, k_new=None, v_new=None, ws=FAKE, nbytes=1 << 30):
+    return L.load_library().msa_decode_step(ctypes.byref(c), q, ctypes.byref(cache), B, max_len, k_new, v_new,
+                                            None, None, out, None, ws, nbytes, None)
+
+
+def test_decode_argument_errors():
+    c = cfg()
+    ok_cache = fake_cache()
+    assert call_decode(c, ok_cache, q=None) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, ok_cache, out=None) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, ok_cache, k_new=FAKE) == L.MSA_ERR_INVALID_ARG          # v_new missing
+    assert call_decode(c, ok_cache, B=-1) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, ok_cache, max_len=16 * 64 + 1) == L.MSA_ERR_INVALID_ARG  # beyond the table
+    assert call_decode(c, fake_cache(k_pages=None)) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, fake_cache(seq_lens=None)) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, fake_cache(max_blocks=0)) == L.MSA_ERR_INVALID_ARG
+    assert call_decode(c, ok_cache, ws=None) == L.MSA_ERR_WORKSPACE
+    assert call_decode(c, ok_cache, nbytes=16) == L.MSA_ERR_WORKSPACE
+    bad = cfg(top_k=0)
+    assert call_decode(bad, ok_cache) == L.MSA_ERR_INVALID_ARG
+
+
+def test_select_attend_build_errors():
+    lib = L.load_library()
+    c = cfg()
+    cache = fake_cache()
+    assert lib.msa_select(ctypes.byref(c), FAKE, ctypes.byref(cache), 1, 1024, None, None, FAKE, 1 << 30, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_select(ctypes.byref(c), FAKE, ctypes.byref(cache), 1, 1024, None, FAKE, FAKE, 8, None) == L.MSA_ERR_WORKSPACE
+    assert lib.msa_attend(ctypes.byref(c), FAKE, ctypes.byref(cache), 1, 1024, None, FAKE, None, FAKE, 1 << 30, None) == L.MSA_ERR_INVALID_ARG
+    nokv = fake_cache(v_pages=None)
+    assert lib.msa_attend(ctypes.byref(c), FAKE, ctypes.byref(nokv), 1, 1024, FAKE, FAKE, None, FAKE, 1 << 30, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_build_summaries(ctypes.byref(c), ctypes.byref(fake_cache(summaries=None)), 1, 1024, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_build_summaries(ctypes.byref(c), ctypes.byref(cache), 1, 5000, None) == L.MSA_ERR_INVALID_ARG
+
+
+def test_prefill_errors():
+    lib = L.load_library()
+    cache = fake_cache(max_blocks=80, num_pages=80)
+
+    def call(c, past=1024, T=256, q=FAKE, nbytes=1 << 30):
+        return lib.msa_prefill_chunk(ctypes.byref(c), q, FAKE, FAKE, ctypes.byref(cache), past, T, None, None,
+                                     FAKE, None, FAKE, nbytes, None)
+    assert call(cfg(), past=1000) == L.MSA_ERR_UNSUPPORTED       # past_len % 64 != 0
+    assert call(cfg(), T=0) == L.MSA_ERR_INVALID_ARG
+    assert call(cfg(), past=80 * 64, T=1) == L.MSA_ERR_INVALID_ARG  # beyond the table
+    assert call(cfg(), q=None) == L.MSA_ERR_INVALID_ARG
+    assert call(cfg(dtype="f32")) == L.MSA_ERR_UNSUPPORTED       # prefill is bf16 only
+    assert call(cfg(), nbytes=100) == L.MSA_ERR_WORKSPACE
