@@ -3,7 +3,7 @@
 //
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
-//   msa_decode_step   [append + block summary] -> score (+histogram) -> top-k -> attend -> merge
+//   msa_decode_step   [append + block summary] -> score -> top-k -> attend (+ split-K merge)
 //   msa_prefill_chunk append + summaries -> tile query -> score -> top-k (+diagonal) -> attend
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
 // HIP call, so an invalid call enqueues nothing.
@@ -24,7 +24,7 @@ using namespace msa;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t scores = 0, hist = 0, idx = 0, qtile = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t scores = 0, idx = 0, pages = 0, qtile = 0, part_o = 0, part_ml = 0, total = 0;
   int row_stride = 0;   // scores per row
   int bps = 1, nsplit = 0;
 };
@@ -62,12 +62,14 @@ Layout decode_layout(const msa_config* c, int op, int B, int max_len) {
   size_t off = 0;
   if (sel) {
     L.scores = off; off += align256(rows * (size_t)(L.row_stride > 0 ? L.row_stride : 1) * sizeof(float));
-    L.hist = off;   off += align256(rows * (size_t)kHistBins * sizeof(uint32_t));
   }
-  if (op == MSA_OP_DECODE) { L.idx = off; off += align256(rows * (size_t)k * sizeof(int32_t)); }
+  if (op == MSA_OP_DECODE) {
+    L.idx = off;   off += align256(rows * (size_t)k * sizeof(int32_t));
+    L.pages = off; off += align256(rows * (size_t)k * sizeof(int32_t));
+  }
   if (att) {
-    L.part_o = off;  off += align256((size_t)B * Hq * L.nsplit * kD * sizeof(float));
-    L.part_ml = off; off += align256((size_t)B * Hq * L.nsplit * 2 * sizeof(float));
+    L.part_o = off;   off += align256((size_t)B * Hq * L.nsplit * kD * sizeof(float));
+    L.part_ml = off;  off += align256((size_t)B * Hq * L.nsplit * 2 * sizeof(float));
   }
   L.total = off;
   return L;
@@ -81,7 +83,6 @@ Layout prefill_layout(const msa_config* c, int max_len, int T) {
   L.row_stride = (max_len + kP - 1) / kP;
   size_t off = 0;
   L.scores = off; off += align256(rows * (size_t)(L.row_stride > 0 ? L.row_stride : 1) * sizeof(float));
-  L.hist = off;   off += align256(rows * (size_t)kHistBins * sizeof(uint32_t));
   L.qtile = off;  off += align256(rows * (size_t)kD * sizeof(float));
   L.idx = off;    off += align256(rows * (size_t)(k + 1) * sizeof(int32_t));
   L.total = off;
@@ -116,17 +117,16 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
     if (s_ != MSA_OK) return s_;             \
   } while (0)
 
-// Step 1 on validated arguments
+// Step 1 on validated arguments; pages (page ids of the kept blocks) is the decode step's extra
 msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
-                      float* scores, uint32_t* hist, int row_stride, int32_t* idx, hipStream_t st) {
+                      float* scores, int row_stride, int32_t* idx, int32_t* pages, hipStream_t st) {
   const bool bf16 = cfg->q_dtype == MSA_BF16;
   const CacheArgs ca = cache_args(cache);
   MSA_TRY(hip_status(launch_score_decode(bf16, q, ca, B, cfg->num_q_heads, cfg->num_kv_heads, max_len, scores,
-                                         row_stride, hist, st)));
+                                         row_stride, st)));
   TopkArgs t{};
   t.scores = scores;
   t.row_stride = row_stride;
-  t.hist = hist;
   t.idx = idx;
   t.idx_stride = cfg->top_k;
   t.rows = B * cfg->num_kv_heads;
@@ -135,12 +135,17 @@ msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   t.lens = cache->seq_lens;
   t.max_len = max_len;
   t.base_blocks = 0;
+  t.pages = pages;
+  t.table = cache->block_table;
+  t.max_blocks = cache->max_blocks;
+  t.num_pages = cache->num_pages;
   return hip_status(launch_topk(t, st));
 }
 
 // Step 2 on validated arguments
 msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
-                      const int32_t* idx, void* out, float* lse, const Layout& L, void* ws, hipStream_t st) {
+                      const int32_t* idx, const int32_t* pages, void* out, float* lse, const Layout& L, void* ws,
+                      hipStream_t st) {
   AttendArgs a{};
   a.q = q;
   a.kpool = cache->k_pages;
@@ -148,6 +153,7 @@ msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   a.table = cache->block_table;
   a.lens = cache->seq_lens;
   a.idx = idx;
+  a.pages = pages;
   a.num_pages = cache->num_pages;
   a.max_blocks = cache->max_blocks;
   a.max_len = max_len;
@@ -210,8 +216,8 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
-  return run_select(cfg, q, cache, batch, max_seq_len, scores, at<uint32_t>(workspace, L.hist), L.row_stride,
-                    idx_out, (hipStream_t)stream);
+  return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr,
+                    (hipStream_t)stream);
 }
 
 msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
@@ -224,7 +230,8 @@ msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   const Layout L = decode_layout(cfg, MSA_OP_ATTEND, batch, max_seq_len);
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
-  return run_attend(cfg, q, cache, batch, max_seq_len, idx, out, lse_out, L, workspace, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  return run_attend(cfg, q, cache, batch, max_seq_len, idx, nullptr, out, lse_out, L, workspace, st);
 }
 
 msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
@@ -245,9 +252,9 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
                                             max_seq_len, st)));
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
-  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, at<uint32_t>(workspace, L.hist), L.row_stride, idx,
-                     st));
-  return run_attend(cfg, q, cache, batch, max_seq_len, idx, out, lse_out, L, workspace, st);
+  int32_t* pages = at<int32_t>(workspace, L.pages);
+  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx, pages, st));
+  return run_attend(cfg, q, cache, batch, max_seq_len, idx, pages, out, lse_out, L, workspace, st);
 }
 
 msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k_new, const void* v_new,
@@ -271,17 +278,16 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   float* qtile = at<float>(workspace, L.qtile);
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
-  uint32_t* hist = at<uint32_t>(workspace, L.hist);
 
   MSA_TRY(hip_status(launch_append_prefill(true, ca, k_new, v_new, past_blocks, T, Hkv, st)));
   MSA_TRY(hip_status(launch_tile_query(true, q, T, Hq, Hkv, qtile, st)));
-  MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, hist, st)));
+  MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, st)));
   TopkArgs t{};
   t.scores = scores;
   t.row_stride = L.row_stride;
-  t.hist = hist;
   t.idx = idx;
   t.idx_stride = cfg->top_k + 1;
+  t.pages = nullptr;
   t.rows = ntiles * Hkv;
   t.k = cfg->top_k;
   t.Hkv = Hkv;

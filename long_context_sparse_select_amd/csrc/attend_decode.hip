@@ -15,8 +15,10 @@
 //   * q.k uses packed bf16 dot2 (v_dot2c_f32_bf16) and a 16-lane DPP row sum; the softmax is
 //     online and wave-local (running max in the log2 domain, exp2), so no barrier is needed
 //     inside the block loop; the 4 waves merge through LDS at the end;
-//   * each workgroup writes an unnormalised partial (O, m, l) per head; k_merge combines the
-//     splits with a log-sum-exp merge and writes o (bf16 / fp32) and lse (natural log).
+//   * each workgroup writes an unnormalised partial (O, m, l) per head; k_merge (one workgroup
+//     per (sequence, group), every partial load in flight at once) combines the splits with a
+//     log-sum-exp merge and writes o (bf16 / fp32) and lse (natural log). With one split the
+//     workgroup's partial is final and is written directly.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,6 +78,16 @@ template <> struct Q8<float> {
   }
 };
 
+constexpr int kMaxSplit = 256;
+
+template <typename T> __device__ __forceinline__ void store_out2(T* out, long long i, float a, float b);
+template <> __device__ __forceinline__ void store_out2<uint16_t>(uint16_t* out, long long i, float a, float b) {
+  reinterpret_cast<uint32_t*>(out)[i / 2] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+template <> __device__ __forceinline__ void store_out2<float>(float* out, long long i, float a, float b) {
+  reinterpret_cast<float2*>(out)[i / 2] = make_float2(a, b);
+}
+
 template <typename T, int G>
 __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
   __shared__ float s_m[4][G], s_l[4][G];
@@ -87,6 +99,7 @@ __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
   const int nb = (N + kP - 1) / kP;
   const int e0 = split * a.blocks_per_split;
   const int e1 = min(a.k, e0 + a.blocks_per_split);
+  const long long rowbg = (long long)b * a.Hkv + g;
 
   Q8<T> q[G];
 #pragma unroll
@@ -101,11 +114,11 @@ __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
-  const int32_t* ids = a.idx + ((long long)b * a.Hkv + g) * a.k;
+  const int32_t* ids = a.idx + rowbg * a.k;
   for (int e = e0; e < e1; ++e) {
     const int j = ids[e];
     if (j < 0 || j >= nb) continue;
-    const int page = a.table[(long long)b * a.max_blocks + j];
+    const int page = a.pages != nullptr ? a.pages[rowbg * a.k + e] : a.table[(long long)b * a.max_blocks + j];
     if (!page_ok(page, a.num_pages)) continue;
     const int ntok = min(kP, N - j * kP);
     const long long head = ((long long)page * a.Hkv + g) * kP * kD;
@@ -167,6 +180,27 @@ __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
     }
   }
   __syncthreads();
+  T* out = reinterpret_cast<T*>(a.out);
+  if (a.nsplit == 1) {  // the workgroup holds the whole row: normalise and write
+    for (int x = 2 * tid; x < G * kD; x += 512) {
+      const int h = x / kD, d = x % kD;
+      const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+      float O0 = 0.f, O1 = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = rescale(s_m[w][h], M);
+        O0 = fmaf(s_o[w][h][d], sc, O0);
+        O1 = fmaf(s_o[w][h][d + 1], sc, O1);
+        L = fmaf(s_l[w][h], sc, L);
+      }
+      const long long oi = ((long long)b * a.Hq + g * G + h) * kD + d;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      store_out2<T>(out, oi, O0 * inv, O1 * inv);
+      if (a.lse != nullptr && d == 0)
+        a.lse[(long long)b * a.Hq + g * G + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   for (int x = tid; x < G * kD; x += 256) {
     const int h = x / kD, d = x % kD;
     const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
@@ -185,61 +219,109 @@ __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
   }
 }
 
-// log-sum-exp merge of the splits: one wave per (sequence, head), 2 dims per lane
-template <typename TO>
-__global__ void __launch_bounds__(256) k_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                               int nsplit, int units, TO* __restrict__ out, float* __restrict__ lse) {
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (unit >= units) return;
-  const float* ml = part_ml + (long long)unit * nsplit * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  const float* po = part_o + (long long)unit * nsplit * kD + 2 * lane;
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = rescale(ml[2 * s], M);
-    L = fmaf(ml[2 * s + 1], w, L);
-    const float2 v = *reinterpret_cast<const float2*>(po + (long long)s * kD);
-    o0 = fmaf(v.x, w, o0);
-    o1 = fmaf(v.y, w, o1);
+// log-sum-exp merge of the splits of one (sequence, group): G heads x 128 dims
+template <typename T, int G>
+__global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
+  __shared__ float s_w[kMaxSplit * G];
+  __shared__ float s_M[G], s_L[G];
+  __shared__ float4 s_red[256];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ns = a.nsplit;
+  const long long unit0 = ((long long)b * a.Hq + g * G) * ns;   // head h, split s -> unit0 + h*ns + s
+  // per-head max and weights: wave w handles heads w, w+4, ...
+  for (int h = wave; h < G; h += 4) {
+    const float* ml = a.part_ml + (unit0 + h * ns) * 2;
+    float mv[kMaxSplit / 64], lv[kMaxSplit / 64];
+#pragma unroll
+    for (int i = 0; i < kMaxSplit / 64; ++i) {   // all loads first, from clamped addresses
+      const int s2 = min(lane + 64 * i, ns - 1);
+      mv[i] = ml[2 * s2];
+      lv[i] = ml[2 * s2 + 1];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit / 64; ++i)
+      if (lane + 64 * i < ns) mx = fmaxf(mx, mv[i]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit / 64; ++i) {
+      const int s2 = lane + 64 * i;
+      if (s2 < ns) {
+        const float w = rescale(mv[i], mx);
+        s_w[s2 * G + h] = w;
+        L = fmaf(lv[i], w, L);
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (lane == 0) { s_M[h] = mx; s_L[h] = L; }
   }
-  float lv = -INFINITY;
-  if (L > 0.f) {
-    o0 /= L;
-    o1 /= L;
-    lv = (M + log2f(L)) * kLn2;
-  } else {
-    o0 = o1 = 0.f;
+  __syncthreads();
+  // weighted sum of the partial outputs: thread -> float4 column c of G*128/4, split group sg
+  constexpr int kCols = G * (kD / 4);
+  constexpr int kGroups = 256 / kCols > 0 ? 256 / kCols : 1;
+  constexpr int kBatch = 16;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int c = tid % kCols, sg = tid / kCols;
+  const int h = c / (kD / 4), c4 = c % (kD / 4);
+  if (sg < kGroups) {
+    const float* po = a.part_o + (unit0 + h * ns) * kD + c4 * 4;
+    for (int s0 = sg; s0 < ns; s0 += kGroups * kBatch) {
+      float4 v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = *reinterpret_cast<const float4*>(po + (long long)min(s0 + kGroups * i, ns - 1) * kD);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int s2 = s0 + kGroups * i;
+        const float w = s2 < ns ? s_w[s2 * G + h] : 0.f;
+        sum.x = fmaf(v[i].x, w, sum.x); sum.y = fmaf(v[i].y, w, sum.y);
+        sum.z = fmaf(v[i].z, w, sum.z); sum.w = fmaf(v[i].w, w, sum.w);
+      }
+    }
+    s_red[sg * kCols + c] = sum;   // kGroups * kCols <= 256
   }
-  if constexpr (sizeof(TO) == 2) {
-    reinterpret_cast<uint32_t*>(out)[(long long)unit * (kD / 2) + lane] = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
-  } else {
-    reinterpret_cast<float2*>(out)[(long long)unit * (kD / 2) + lane] = make_float2(o0, o1);
+  __syncthreads();
+  if (sg == 0) {
+    float4 t = s_red[c];
+    for (int k2 = 1; k2 < kGroups; ++k2) {
+      const float4 u = s_red[k2 * kCols + c];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    const float L = s_L[h];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T* out = reinterpret_cast<T*>(a.out);
+    const long long oi = ((long long)b * a.Hq + g * G + h) * kD + c4 * 4;
+    store_out2<T>(out, oi, t.x * inv, t.y * inv);
+    store_out2<T>(out, oi + 2, t.z * inv, t.w * inv);
+    if (a.lse != nullptr && c4 == 0)
+      a.lse[(long long)b * a.Hq + g * G + h] = L > 0.f ? (s_M[h] + log2f(L)) * kLn2 : -INFINITY;
   }
-  if (lse != nullptr && lane == 0) lse[unit] = lv;
+}
+
+template <typename T, int G>
+hipError_t launch_attend_g(const AttendArgs& a, hipStream_t st) {
+  k_attend_decode<T, G><<<dim3(a.nsplit, a.Hkv, a.B), 256, 0, st>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.nsplit == 1) return err;
+  k_merge<T, G><<<dim3(a.Hkv, a.B), 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_attend_typed(const AttendArgs& a, int G, hipStream_t st) {
-  const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (G) {
-    case 1: k_attend_decode<T, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: k_attend_decode<T, 2><<<grid, 256, 0, st>>>(a); break;
-    case 3: k_attend_decode<T, 3><<<grid, 256, 0, st>>>(a); break;
-    case 4: k_attend_decode<T, 4><<<grid, 256, 0, st>>>(a); break;
-    case 5: k_attend_decode<T, 5><<<grid, 256, 0, st>>>(a); break;
-    case 6: k_attend_decode<T, 6><<<grid, 256, 0, st>>>(a); break;
-    case 7: k_attend_decode<T, 7><<<grid, 256, 0, st>>>(a); break;
-    case 8: k_attend_decode<T, 8><<<grid, 256, 0, st>>>(a); break;
+    case 1: return launch_attend_g<T, 1>(a, st);
+    case 2: return launch_attend_g<T, 2>(a, st);
+    case 3: return launch_attend_g<T, 3>(a, st);
+    case 4: return launch_attend_g<T, 4>(a, st);
+    case 5: return launch_attend_g<T, 5>(a, st);
+    case 6: return launch_attend_g<T, 6>(a, st);
+    case 7: return launch_attend_g<T, 7>(a, st);
+    case 8: return launch_attend_g<T, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int units = a.B * a.Hq;
-  const dim3 mgrid((units + 3) / 4);
-  k_merge<T><<<mgrid, 256, 0, st>>>(a.part_o, a.part_ml, a.nsplit, units, reinterpret_cast<T*>(a.out), a.lse);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -247,9 +329,10 @@ hipError_t launch_attend_typed(const AttendArgs& a, int G, hipStream_t st) {
 int decode_blocks_per_split(int B, int Hkv, int k) {
   const long long rows = (long long)B * Hkv;
   int bps = 1;
-  while (bps < k && rows * ((k + bps - 1) / bps) > 2048) bps *= 2;
+  while (bps < k && (rows * ((k + bps - 1) / bps) > 2048 || (k + bps - 1) / bps > kMaxSplit)) bps *= 2;
   return bps;
 }
+
 
 hipError_t launch_attend_decode(bool bf16, const AttendArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;

@@ -241,10 +241,9 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const float* v = &o[dt][4 * i4];
       uint2 pk;
-      pk.x = pack_bf16(v[0] * inv, v[1] * inv);
-      pk.y = pack_bf16(v[2] * inv, v[3] * inv);
+      pk.x = pack_bf16(o[dt][4 * i4 + 0] * inv, o[dt][4 * i4 + 1] * inv);
+      pk.y = pack_bf16(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * c) = pk;
     }
   if (a.lse != nullptr && c == 0)

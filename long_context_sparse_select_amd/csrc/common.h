@@ -8,6 +8,7 @@ namespace msa {
 
 constexpr int kD = 128;        // head_dim
 constexpr int kP = 64;         // tokens per block (== page)
+constexpr int kMaxGroup = 8;   // query heads per KV head
 constexpr int kHistBits = 12;  // coarse score histogram: top 12 bits of the order key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr float kLog2e = 1.4426950408889634f;

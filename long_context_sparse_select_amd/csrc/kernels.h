@@ -24,19 +24,17 @@ hipError_t launch_append_decode(bool bf16, const CacheArgs& c, const void* k_new
 hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
                                  int past_blocks, int T, int Hkv, hipStream_t st);
 
-// ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats
-// each; hist rows hold kHistBins counters per row (added to, then cleared by the top-k kernel).
+// ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats each.
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
-                               int max_len, float* scores, int row_stride, uint32_t* hist, hipStream_t st);
+                               int max_len, float* scores, int row_stride, hipStream_t st);
 hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st);
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
-                                float* scores, int row_stride, uint32_t* hist, hipStream_t st);
+                                float* scores, int row_stride, hipStream_t st);
 
 // ---- Step 1 top-k
 struct TopkArgs {
   const float* scores;
   int row_stride;
-  uint32_t* hist;
   int32_t* idx;
   int idx_stride;      // top_k (decode) or top_k + 1 (prefill)
   int rows;
@@ -45,6 +43,12 @@ struct TopkArgs {
   const int32_t* lens; // decode: n = ceil(clamp(lens[row / Hkv]) / 64); null -> prefill mode
   int max_len;
   int base_blocks;     // prefill: n = base_blocks + row / Hkv, and block n is appended
+  // decode only (nullable): page ids of the kept blocks [rows][k] (-1 for padding or a bad page
+  // id), translated through table [B][max_blocks]
+  int32_t* pages;
+  const int32_t* table;
+  int max_blocks;
+  int num_pages;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
@@ -56,6 +60,7 @@ struct AttendArgs {
   const int32_t* table;
   const int32_t* lens;
   const int32_t* idx;   // [B][Hkv][k]
+  const int32_t* pages; // nullable [B][Hkv][k]: page ids of idx (else translated through table)
   int num_pages, max_blocks, max_len;
   int B, Hq, Hkv, k;
   float scale_log2;     // softmax_scale * log2(e)

@@ -7,13 +7,11 @@
 // (prefill); a block's score is <index query, block summary>, unscaled, in fp32.
 //
 // Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 per sequence), so the
-// kernel is shaped for HBM: a workgroup owns a chunk of 32 logical blocks of one sequence,
+// kernel is shaped for HBM: a workgroup owns a chunk of 16 logical blocks of one sequence,
 // stages the chunk's page ids and the Hkv index queries in LDS, and then walks (block, group)
-// pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 one pass of a wave reads two
-// whole 4 KiB pages' worth of contiguous summaries, whatever the page permutation. Eight
-// independent 16 B loads per lane are issued before any arithmetic. Each score also bumps a
-// coarse per-row histogram of its order key, which lets the top-k kernel find the k-th score's
-// neighbourhood in one pass.
+// pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 the workgroup reads the
+// chunk's 16 pages as 16 contiguous 4 KiB runs, whatever the page permutation, and each lane
+// has all 16 of its loads in flight before any arithmetic.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,8 +19,8 @@ namespace msa {
 
 namespace {
 
-constexpr int kChunk = 32;    // logical blocks per workgroup (decode)
-constexpr int kUnroll = 8;    // pairs in flight per 32-lane slot
+constexpr int kChunk = 16;    // logical blocks per workgroup (decode)
+constexpr int kUnroll = 16;   // pairs in flight per 32-lane slot
 
 template <typename T> __device__ __forceinline__ float ld(const T* p, long long i);
 template <> __device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
@@ -35,8 +33,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
                                                       const int32_t* __restrict__ table,
                                                       const int32_t* __restrict__ lens, int num_pages,
                                                       int max_blocks, int Hq, int Hkv, int max_len,
-                                                      float* __restrict__ scores, int row_stride,
-                                                      uint32_t* __restrict__ hist) {
+                                                      float* __restrict__ scores, int row_stride) {
   extern __shared__ float s_qidx[];             // [Hkv][128] index queries
   __shared__ int s_page[kChunk];
   const int b = blockIdx.y;
@@ -46,39 +43,49 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   const int nb = (N + kP - 1) / kP;
   const int jend = min(j0 + kChunk, row_stride);
 
-  if (tid < kChunk) {
-    const int j = j0 + tid;
-    int page = -1;
-    if (j < nb) {
-      page = table[(long long)b * max_blocks + j];
-      if (!page_ok(page, num_pages)) page = -1;
-    }
-    s_page[tid] = page;
-  }
-  if (j0 < nb) {  // [MGS §1 Step 1] one index query per group: mean of the group's heads
+  // the page ids, the sequence length and the queries are loaded in one round trip: the table
+  // read does not wait for the length (j < row_stride <= max_blocks keeps it in bounds)
+  const int my_page = table[(long long)b * max_blocks + min(j0 + (tid & (kChunk - 1)), row_stride - 1)];
+  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads
     const int G = Hq / Hkv;
     const TQ* qb = q + (long long)b * Hq * kD;
-    for (int e = tid; e < Hkv * kD; e += 256) {
-      const int g = e / kD, d = e % kD;
-      float acc = 0.f;
-      for (int h = 0; h < G; ++h) acc += ld(qb, (long long)(g * G + h) * kD + d);
-      s_qidx[e] = acc / (float)G;
+    const int ne = Hkv * kD;
+    for (int e0 = 0; e0 < ne; e0 += 1024) {
+      float v[4][kMaxGroup];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {     // all loads first (clamped in-bounds indices)
+        const int e = min(e0 + tid + 256 * i, ne - 1);
+        const int g = e / kD, d = e % kD;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) v[i][h] = ld(qb, (long long)(g * G + min(h, G - 1)) * kD + d);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + tid + 256 * i;
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h)
+          if (h < G) acc += v[i][h];
+        if (e < ne) s_qidx[e] = acc / (float)G;
+      }
     }
   }
+  if (tid < kChunk) s_page[tid] = (j0 + tid < nb && page_ok(my_page, num_pages)) ? my_page : -1;
   __syncthreads();
 
   const int slot = tid >> 5;    // 8 pair slots per pass
   const int l32 = tid & 31;     // 4 dims per lane
   const int npairs = (jend - j0) * Hkv;
+  const bool any_page = num_pages > 0;
   for (int p0 = 0; p0 < npairs; p0 += 8 * kUnroll) {
     float4 sv[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {   // every load issued before any is used
       const int p = p0 + u * 8 + slot;
-      const int jl = p / Hkv, g = p % Hkv;
-      const int page = (p < npairs) ? s_page[jl] : -1;
+      const int pg = s_page[min(p / Hkv, kChunk - 1)];
+      const int page = (p < npairs && pg >= 0) ? pg : 0;   // page 0: a valid address, result unused
       sv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (page >= 0) sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD + l32 * 4);
+      if (any_page) sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + p % Hkv) * kD + l32 * 4);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -95,29 +102,43 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       part += __shfl_xor(part, 16);
       if (l32 == 0) {
         const long long row = (long long)b * Hkv + g;
-        float s = -INFINITY;
-        if (j < nb) {
-          if (s_page[jl] >= 0) s = part;
-          atomicAdd(&hist[row * kHistBins + (order_key(s) >> (32 - kHistBits))], 1u);
-        }
-        scores[row * row_stride + j] = s;
+        scores[row * row_stride + j] = (j < nb && s_page[jl] >= 0) ? part : -INFINITY;
       }
     }
   }
 }
 
-// tile index query: qtile[tau][g][d] = mean over the tile's rows and the group's heads
+// tile index query: qtile[tau][g][d] = mean over the tile's rows and the group's heads.
+// 512 threads: thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (all 2G loads
+// in flight at once); the 64 rows are then summed per dim through LDS, in row order.
 template <typename TQ>
-__global__ void __launch_bounds__(128) k_tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv,
+__global__ void __launch_bounds__(512) k_tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv,
                                                     float* __restrict__ qtile) {
-  const int tau = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
+  __shared__ float s_rows[kP][kD + 1];
+  const int tau = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int G = Hq / Hkv;
-  const int i0 = tau * kP, i1 = min(T, i0 + kP);
-  float acc = 0.f;
-  for (int i = i0; i < i1; ++i)
-#pragma unroll 4
-    for (int h = 0; h < G; ++h) acc += ld(q, ((long long)i * Hq + g * G + h) * kD + d);
-  qtile[((long long)tau * Hkv + g) * kD + d] = acc / (float)((i1 - i0) * G);
+  const int i0 = tau * kP, n = min(T, i0 + kP) - i0;
+  const int i = tid >> 3, d0 = (tid & 7) * 16;
+  const int row = i0 + min(i, n - 1);
+  float v[kMaxGroup][16];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[h][e] = ld(q, ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0 + e);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) acc += v[h][e];
+    s_rows[i][d0 + e] = i < n ? acc : 0.f;
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float acc = 0.f;
+    for (int r = 0; r < n; ++r) acc += s_rows[r][tid];
+    qtile[((long long)tau * Hkv + g) * kD + tid] = acc / (float)(n * G);
+  }
 }
 
 // prefill scores: a 64-tile x 64-block fp32 product per workgroup, from LDS; tile tau scores
@@ -130,28 +151,40 @@ constexpr int kPB = 64;   // blocks per workgroup
 __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__ qtile, const float* __restrict__ S,
                                                        const int32_t* __restrict__ table, int num_pages,
                                                        int past_blocks, int ntiles, int Hkv,
-                                                       float* __restrict__ scores, int row_stride,
-                                                       uint32_t* __restrict__ hist) {
+                                                       float* __restrict__ scores, int row_stride) {
   __shared__ float s_q[kD][kPT];
   __shared__ float s_s[kD][kPB];
   const int j0 = blockIdx.x * kPB, g = blockIdx.y, t0 = blockIdx.z * kPT;
   const int tid = threadIdx.x;
   const int ncand_max = past_blocks + ntiles - 1;   // candidates of the last tile
-  for (int e = tid; e < kPT * (kD / 4); e += 256) {
-    const int t = e % kPT, c = e / kPT;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t0 + t < ntiles) v = *reinterpret_cast<const float4*>(qtile + ((long long)(t0 + t) * Hkv + g) * kD + c * 4);
-    s_q[c * 4 + 0][t] = v.x; s_q[c * 4 + 1][t] = v.y; s_q[c * 4 + 2][t] = v.z; s_q[c * 4 + 3][t] = v.w;
-  }
-  for (int e = tid; e < kPB * (kD / 4); e += 256) {
-    const int jl = e % kPB, c = e / kPB;
-    const int j = j0 + jl;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j < ncand_max) {
-      const int page = table[j];
-      if (page_ok(page, num_pages)) v = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD + c * 4);
+  {
+    // staging: all 16 float4 loads of a thread in flight at once, from clamped addresses
+    constexpr int kIt = kPT * (kD / 4) / 256;   // 8 (same for the block operand)
+    float4 qv[kIt], sv[kIt];
+    int pg[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = tid + 256 * it;
+      const int t = e % kPT, jl = e % kPB;
+      const int j = min(j0 + jl, max(ncand_max - 1, 0));
+      pg[it] = table[j];
+      qv[it] = *reinterpret_cast<const float4*>(qtile + ((long long)min(t0 + t, ntiles - 1) * Hkv + g) * kD + (e / kPT) * 4);
     }
-    s_s[c * 4 + 0][jl] = v.x; s_s[c * 4 + 1][jl] = v.y; s_s[c * 4 + 2][jl] = v.z; s_s[c * 4 + 3][jl] = v.w;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int page = page_ok(pg[it], num_pages) ? pg[it] : -1;
+      sv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (page >= 0) sv[it] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD + ((tid + 256 * it) / kPB) * 4);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = tid + 256 * it;
+      const int t = e % kPT, c = e / kPT, jl = e % kPB;
+      const float4 a = t0 + t < ntiles ? qv[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = j0 + jl < ncand_max ? sv[it] : make_float4(0.f, 0.f, 0.f, 0.f);
+      s_q[c * 4 + 0][t] = a.x; s_q[c * 4 + 1][t] = a.y; s_q[c * 4 + 2][t] = a.z; s_q[c * 4 + 3][t] = a.w;
+      s_s[c * 4 + 0][jl] = b.x; s_s[c * 4 + 1][jl] = b.y; s_s[c * 4 + 2][jl] = b.z; s_s[c * 4 + 3][jl] = b.w;
+    }
   }
   __syncthreads();
   // thread owns tiles ty*4 .. +3 and blocks tx + 16*c, c = 0..3
@@ -188,12 +221,7 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
     for (int c = 0; c < 4; ++c) {
       const int j = j0 + tx + 16 * c;
       if (j >= row_stride) continue;
-      float s = -INFINITY;
-      if (j < ncand) {
-        if (ok[c]) s = acc[a][c];
-        atomicAdd(&hist[row * kHistBins + (order_key(s) >> (32 - kHistBits))], 1u);
-      }
-      scores[row * row_stride + j] = s;
+      scores[row * row_stride + j] = (j < ncand && ok[c]) ? acc[a][c] : -INFINITY;
     }
   }
 }
@@ -201,33 +229,33 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
 }  // namespace
 
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
-                               float* scores, int row_stride, uint32_t* hist, hipStream_t st) {
+                               float* scores, int row_stride, hipStream_t st) {
   if (B == 0 || row_stride == 0) return hipSuccess;
   const dim3 grid((row_stride + kChunk - 1) / kChunk, B);
   const size_t lds = (size_t)Hkv * kD * sizeof(float);
   if (bf16)
     k_score_decode<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)q, c.S, c.table, c.lens, c.num_pages,
-                                                     c.max_blocks, Hq, Hkv, max_len, scores, row_stride, hist);
+                                                     c.max_blocks, Hq, Hkv, max_len, scores, row_stride);
   else
     k_score_decode<float><<<grid, 256, lds, st>>>((const float*)q, c.S, c.table, c.lens, c.num_pages,
-                                                  c.max_blocks, Hq, Hkv, max_len, scores, row_stride, hist);
+                                                  c.max_blocks, Hq, Hkv, max_len, scores, row_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st) {
   const dim3 grid((T + kP - 1) / kP, Hkv);
   if (bf16)
-    k_tile_query<uint16_t><<<grid, 128, 0, st>>>((const uint16_t*)q, T, Hq, Hkv, qtile);
+    k_tile_query<uint16_t><<<grid, 512, 0, st>>>((const uint16_t*)q, T, Hq, Hkv, qtile);
   else
-    k_tile_query<float><<<grid, 128, 0, st>>>((const float*)q, T, Hq, Hkv, qtile);
+    k_tile_query<float><<<grid, 512, 0, st>>>((const float*)q, T, Hq, Hkv, qtile);
   return hipGetLastError();
 }
 
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
-                                float* scores, int row_stride, uint32_t* hist, hipStream_t st) {
+                                float* scores, int row_stride, hipStream_t st) {
   const dim3 grid((row_stride + kPB - 1) / kPB, Hkv, (ntiles + kPT - 1) / kPT);
   k_score_prefill<<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
-                                        row_stride, hist);
+                                        row_stride);
   return hipGetLastError();
 }
 

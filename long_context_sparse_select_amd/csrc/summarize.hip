@@ -50,9 +50,9 @@ __device__ __forceinline__ void write_mean(float* acc, int n, float* dst, int la
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = across_rows_sum(acc[e]);
   if (lane < 16) {
-    const float inv_n = (float)n;
-    float4 lo = make_float4(acc[0] / inv_n, acc[1] / inv_n, acc[2] / inv_n, acc[3] / inv_n);
-    float4 hi = make_float4(acc[4] / inv_n, acc[5] / inv_n, acc[6] / inv_n, acc[7] / inv_n);
+    const float fn = (float)n;
+    float4 lo = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+    float4 hi = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
     reinterpret_cast<float4*>(dst + lane * 8)[0] = lo;
     reinterpret_cast<float4*>(dst + lane * 8)[1] = hi;
   }
@@ -77,12 +77,13 @@ __global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ k
   if (!page_ok(page, num_pages)) return;
   const T* base = kpool + ((long long)page * Hkv + g) * kP * kD + (lane & 15) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int r = lane >> 4; r < n; r += 4) {
-    Vec8<T> v;
-    v.load(base + (long long)r * kD);
-    v.add_to(acc);
-  }
+  Vec8<T> v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)  // all 16 row loads in flight before the sum (clamped rows)
+    v[i].load(base + (long long)min((lane >> 4) + 4 * i, n - 1) * kD);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((lane >> 4) + 4 * i < n) v[i].add_to(acc);
   write_mean(acc, n, S + ((long long)page * Hkv + g) * kD, lane);
 }
 
@@ -113,11 +114,13 @@ __global__ void __launch_bounds__(256) k_append_decode(T* __restrict__ kpool, T*
     vn.store(vpool + head + (long long)slot * kD + d0);
     kn.add_to(acc);  // the new key enters the mean from registers, not from the pool
   }
-  for (int r = lane >> 4; r < slot; r += 4) {
-    Vec8<T> v;
-    v.load(kpool + head + (long long)r * kD + d0);
-    v.add_to(acc);
-  }
+  Vec8<T> v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)  // the block's older rows, all loads in flight (clamped rows)
+    v[i].load(kpool + head + (long long)min((lane >> 4) + 4 * i, max(slot - 1, 0)) * kD + d0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((lane >> 4) + 4 * i < slot) v[i].add_to(acc);
   write_mean(acc, slot + 1, S + ((long long)page * Hkv + g) * kD, lane);
 }
 

@@ -6,18 +6,20 @@
 // min(k, n); the list is written in ascending block order and padded with -1; in prefill the
 // tile's diagonal block is appended after the k_eff entries.
 //
-// One 1024-thread workgroup per row. Scores are compared as order-preserving 32-bit keys.
-//  1. The scoring kernel has already counted the row's keys in a 4096-bin histogram of their
-//     top 12 bits. A suffix scan over it finds bin b1 holding the k_eff-th largest key
-//     (the histogram row is cleared here for the next call).
-//  2. One pass over the row collects A = keys in bins above b1 and B = keys in bin b1 into LDS,
-//     counting both exactly. If |A| < k_eff <= |A| + |B| and B fits in LDS, the answer is A plus
-//     the k_eff - |A| best of B (ranked in LDS by the full order) -- correct whatever the
-//     histogram said, because the counts are exact. Otherwise (a stale histogram, or very many
-//     ties) an exact fallback finds the k_eff-th key by a bitwise search over the key space and
-//     emits the selection with an ordered compaction.
-//  3. The k_eff kept indices are sorted ascending by counting in LDS.
-// The output is deterministic: it depends only on the scores.
+// One 1024-thread workgroup per row; scores are compared as order-preserving 32-bit keys.
+// Rows of up to 16384 candidates are held in registers (16 per thread, j = tid + 1024 i):
+//  1. each thread's maximum is a group maximum; the k_eff-th largest group maximum is a lower
+//     bound T0 of the k_eff-th largest key (the k_eff groups with the largest maxima each hold
+//     a key >= T0). A 256-bin histogram of the group maxima, normalised to their range, finds
+//     a bin whose lower edge still leaves >= k_eff maxima above it; T0 = the smallest group
+//     maximum in or above that bin, so >= k_eff keys are >= T0 -- whatever the data;
+//  2. the survivors (keys >= T0; typically a little over k) are gathered in LDS and ranked
+//     exactly by (key desc, index asc); ranks < k_eff are kept;
+//  3. the kept indices are sorted ascending by counting.
+// Longer rows, or rows where too many keys tie at T0, take an exact fallback: a bitwise search
+// for the k_eff-th key over the row in memory, then an ordered compaction.
+// Decode rows also get each kept block's page id (for the attend kernel). The output depends
+// only on the scores.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,8 +29,35 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCapB = 2048;
+constexpr int kPer = 16;
+constexpr int kMaxFast = kThreads * kPer;
+constexpr int kCap = 2048;
+constexpr int kBins = 256;
 constexpr int kMaxK = 4096;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+// wave-uniform max / min: DPP within each 16-lane row, then the four rows through readlane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));
+  v = min(v, dpp_u32<0x4E>(v));
+  v = min(v, dpp_u32<0x141>(v));
+  v = min(v, dpp_u32<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
 
 // block-wide integer sum (all threads get it); s_tmp holds kWaves ints
 __device__ int block_sum(int v, int* s_tmp) {
@@ -62,16 +91,67 @@ __device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
   return before + in_wave;
 }
 
-__global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int32_t s_sel[kMaxK];
-  __shared__ uint32_t s_bkey[kCapB];
-  __shared__ int32_t s_bidx[kCapB];
-  __shared__ int s_tmp[kWaves];
-  __shared__ int s_b1, s_above, s_cntA, s_cntB;
+struct TopkShared {
+  unsigned long long comp[kCap + 2];   // survivors: (key << 32) | ~index, larger = better
+  int32_t sel[kMaxK + 4];
+  int32_t selpg[kMaxK];
+  uint32_t hist[kBins];
+  uint32_t red[2 * kWaves];
+  int tmp[kWaves];
+  int cnt;
+  int bstar;
+};
 
-  const int row = blockIdx.x;
+__device__ __forceinline__ int page_of(const TopkArgs& a, int row, int j) {
+  const int p = a.table[(long long)(row / a.Hkv) * a.max_blocks + j];
+  return page_ok(p, a.num_pages) ? p : -1;
+}
+
+__device__ __forceinline__ void emit(const TopkArgs& a, int row, int pos, int j) {
+  a.idx[(long long)row * a.idx_stride + pos] = j;
+  if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = page_of(a, row, j);
+}
+
+__device__ __forceinline__ void pad(const TopkArgs& a, int row, int keff, int n, bool prefill) {
+  for (int i = keff + threadIdx.x; i < a.idx_stride; i += kThreads) {
+    a.idx[(long long)row * a.idx_stride + i] = (prefill && i == keff) ? n : -1;
+    if (a.pages != nullptr && i < a.k) a.pages[(long long)row * a.k + i] = -1;
+  }
+}
+
+// exact selection straight from memory: T = k_eff-th largest key, then ordered compaction
+__device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, TopkShared& sh) {
   const int tid = threadIdx.x;
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+    for (int j = tid; j < n; j += kThreads) c += order_key(srow[j]) >= cand;
+    if (block_sum(c, sh.tmp) >= keff) T = cand;
+  }
+  int gt = 0;
+  for (int j = tid; j < n; j += kThreads) gt += order_key(srow[j]) > T;
+  const int need_eq = keff - block_sum(gt, sh.tmp);
+  int run_eq = 0, run_sel = 0;
+  for (int base = 0; base < n; base += kThreads) {
+    const int j = base + tid;
+    const uint32_t key = j < n ? order_key(srow[j]) : 0u;
+    const bool is_gt = j < n && key > T;
+    const bool is_eq = j < n && key == T;
+    int tot_eq, tot_sel;
+    const int eq_rank = run_eq + block_excl_count(is_eq, sh.tmp, &tot_eq);
+    const bool sel = is_gt || (is_eq && eq_rank < need_eq);
+    const int pos = run_sel + block_excl_count(sel, sh.tmp, &tot_sel);
+    if (sel) emit(a, row, pos, j);
+    run_eq += tot_eq;
+    run_sel += tot_sel;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool prefill = a.lens == nullptr;
   int n;
   if (!prefill) {
@@ -82,110 +162,123 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   }
   const int keff = min(a.k, n);
   const float* srow = a.scores + (long long)row * a.row_stride;
-  int32_t* out = a.idx + (long long)row * a.idx_stride;
-  uint32_t* grow = a.hist + (long long)row * kHistBins;
-
-  for (int i = tid; i < kHistBins; i += kThreads) {
-    s_hist[i] = grow[i];
-    grow[i] = 0u;
-  }
-  if (tid == 0) { s_b1 = -1; s_above = 0; s_cntA = 0; s_cntB = 0; }
-  __syncthreads();
 
   if (keff == n) {  // every candidate is kept
-    for (int i = tid; i < a.idx_stride; i += kThreads) out[i] = i < n ? i : ((prefill && i == n) ? n : -1);
+    for (int i = tid; i < n; i += kThreads) emit(a, row, i, i);
+    pad(a, row, keff, n, prefill);
     return;
   }
 
-  // ---- 1. bin of the k_eff-th largest key: thread t owns bins 4t .. 4t+3
-  {
-    const uint32_t c0 = s_hist[4 * tid], c1 = s_hist[4 * tid + 1], c2 = s_hist[4 * tid + 2], c3 = s_hist[4 * tid + 3];
-    const uint32_t local = c0 + c1 + c2 + c3;
-    const int lane = tid & 63, wave = tid >> 6;
-    uint32_t incl = local;  // inclusive suffix sum within the wave
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_down(incl, off);
-      if (lane + off < 64) incl += y;
+  bool done = false;
+  if (n <= kMaxFast) {
+    // every load is issued before any is used: clamped in-bounds addresses, masked afterwards
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + kThreads * i, n - 1)];
+    uint32_t key[kPer];
+    uint32_t cm = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      key[i] = tid + kThreads * i < n ? order_key(v[i]) : 0u;
+      cm = max(cm, key[i]);
     }
-    if (lane == 0) s_tmp[wave] = (int)incl;
-    __syncthreads();
-    uint32_t above = incl - local;
-    for (int w = wave + 1; w < kWaves; ++w) above += (uint32_t)s_tmp[w];
-    const uint32_t c[4] = {c0, c1, c2, c3};
-    uint32_t run = above;
-    for (int i = 3; i >= 0; --i) {
-      if (run < (uint32_t)keff && run + c[i] >= (uint32_t)keff) { s_b1 = 4 * tid + i; s_above = (int)run; }
-      run += c[i];
+    const int ngroups = min(n, kThreads);     // threads holding at least one candidate
+    const bool has = tid < ngroups;
+    uint32_t T0 = 0u;
+    if (tid == 0) sh.cnt = 0;
+    if (keff <= ngroups) {
+      // ---- 1. range of the group maxima
+      const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
+      if (lane == 0) { sh.red[wave] = wmx; sh.red[kWaves + wave] = wmn; }
+      if (tid < kBins) sh.hist[tid] = 0u;
+      if (tid == 0) sh.bstar = 0;   // bin 0 keeps every group maximum: always a valid bound
+      __syncthreads();
+      uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kWaves + w]); }
+      const unsigned long long span = (unsigned long long)(mx - mn) + 1ull;
+      uint32_t bin = 0u;
+      if (has) {
+        bin = (uint32_t)(((unsigned long long)(cm - mn) * kBins) / span);
+        atomicAdd(&sh.hist[bin], 1u);
+      }
+      __syncthreads();
+      // ---- bin holding the k_eff-th largest group maximum (wave 0: lane owns bins 4l..4l+3)
+      if (wave == 0) {
+        const uint4 c4 = reinterpret_cast<const uint4*>(sh.hist)[lane];
+        const uint32_t local = c4.x + c4.y + c4.z + c4.w;
+        uint32_t incl = local;  // suffix sum over lanes >= lane
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
+          if (lane + off < 64) incl += y;
+        }
+        uint32_t run = incl - local;
+        const uint32_t cc[4] = {c4.x, c4.y, c4.z, c4.w};
+        for (int i = 3; i >= 0; --i) {
+          if (run < (uint32_t)keff && run + cc[i] >= (uint32_t)keff) sh.bstar = 4 * lane + i;
+          run += cc[i];
+        }
+      }
+      __syncthreads();
+      // ---- T0 = smallest group maximum in bins >= bstar
+      const uint32_t t0 = wave_min_u32((has && bin >= (uint32_t)sh.bstar) ? cm : 0xffffffffu);
+      if (lane == 0) sh.red[wave] = t0;
+      __syncthreads();
+      T0 = 0xffffffffu;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) T0 = min(T0, sh.red[w]);
+    } else {
+      __syncthreads();
     }
-  }
-  __syncthreads();
-
-  // ---- 2. one pass over the row
-  const int b1 = s_b1;
-  if (b1 >= 0) {
-    for (int j = tid; j < n; j += kThreads) {
-      const uint32_t key = order_key(srow[j]);
-      const int bin = (int)(key >> (32 - kHistBits));
-      if (bin > b1) {
-        const int p = atomicAdd(&s_cntA, 1);
-        if (p < keff) s_sel[p] = j;
-      } else if (bin == b1) {
-        const int p = atomicAdd(&s_cntB, 1);
-        if (p < kCapB) { s_bkey[p] = key; s_bidx[p] = j; }
+    // ---- 2. survivors, as (key, ~index) composites
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tid + kThreads * i;
+      if (j < n && key[i] >= T0) {
+        const int p = atomicAdd(&sh.cnt, 1);
+        if (p < kCap) sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
       }
     }
-  }
-  __syncthreads();
-  const int cntA = s_cntA, cntB = s_cntB;
-  const bool fast = b1 >= 0 && cntA < keff && cntA + cntB >= keff && cntB <= kCapB;
-
-  if (fast) {
-    const int need = keff - cntA;
-    for (int e = tid; e < cntB; e += kThreads) {
-      const uint32_t ke = s_bkey[e];
-      const int je = s_bidx[e];
-      int rank = 0;
-      for (int f = 0; f < cntB; ++f) {
-        const uint32_t kf = s_bkey[f];
-        rank += (kf > ke) || (kf == ke && s_bidx[f] < je);
-      }
-      if (rank < need) s_sel[cntA + rank] = je;
-    }
     __syncthreads();
-    for (int e = tid; e < keff; e += kThreads) {
-      const int v = s_sel[e];
-      int pos = 0;
-      for (int f = 0; f < keff; ++f) pos += s_sel[f] < v;
-      out[pos] = v;
-    }
-  } else {
-    // ---- exact fallback: T = largest key with count(key >= T) >= k_eff
-    uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
-      for (int j = tid; j < n; j += kThreads) c += order_key(srow[j]) >= cand;
-      if (block_sum(c, s_tmp) >= keff) T = cand;
-    }
-    int gt = 0;
-    for (int j = tid; j < n; j += kThreads) gt += order_key(srow[j]) > T;
-    const int need_eq = keff - block_sum(gt, s_tmp);
-    int run_eq = 0, run_sel = 0;
-    for (int base = 0; base < n; base += kThreads) {
-      const int j = base + tid;
-      const uint32_t key = j < n ? order_key(srow[j]) : 0u;
-      const bool is_gt = j < n && key > T;
-      const bool is_eq = j < n && key == T;
-      int tot_eq, tot_sel;
-      const int eq_rank = run_eq + block_excl_count(is_eq, s_tmp, &tot_eq);
-      const bool sel = is_gt || (is_eq && eq_rank < need_eq);
-      const int pos = run_sel + block_excl_count(sel, s_tmp, &tot_sel);
-      if (sel) out[pos] = j;
-      run_eq += tot_eq;
-      run_sel += tot_sel;
+    const int m = sh.cnt;
+    if (m >= keff && m <= kCap) {   // uniform; m >= k_eff holds by construction of T0
+      if (tid < 2) sh.comp[m + tid] = 0ull;   // pad: never counts as better
+      __syncthreads();
+      const int npair = (m + 1) >> 1;
+      const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
+      for (int e = tid; e < m; e += kThreads) {
+        const unsigned long long ce = sh.comp[e];
+        const int je = (int)~(uint32_t)ce;
+        const int pg = a.pages != nullptr ? page_of(a, row, je) : -1;   // latency hidden by the ranking
+        int rank = 0;
+#pragma unroll 4
+        for (int f = 0; f < npair; ++f) {
+          const ulonglong2 c2 = cp[f];
+          rank += (c2.x > ce) + (c2.y > ce);
+        }
+        if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pg; }
+      }
+      if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
+      __syncthreads();
+      // ---- 3. ascending block order
+      const int nq = (keff + 3) >> 2;
+      const int4* sp = reinterpret_cast<const int4*>(sh.sel);
+      for (int e = tid; e < keff; e += kThreads) {
+        const int vj = sh.sel[e];
+        int pos = 0;
+#pragma unroll 4
+        for (int f = 0; f < nq; ++f) {
+          const int4 q4 = sp[f];
+          pos += (q4.x < vj) + (q4.y < vj) + (q4.z < vj) + (q4.w < vj);
+        }
+        a.idx[(long long)row * a.idx_stride + pos] = vj;
+        if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = sh.selpg[e];
+      }
+      done = true;
     }
   }
-  for (int i = keff + tid; i < a.idx_stride; i += kThreads) out[i] = (prefill && i == keff) ? n : -1;
+  if (!done) select_fallback(a, srow, row, n, keff, sh);
+  pad(a, row, keff, n, prefill);
 }
 
 }  // namespace

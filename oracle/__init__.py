@@ -55,7 +55,7 @@ def _load():
         lib.orc_decode.restype = I
         lib.orc_summaries.argtypes = [I, I, I, I, I, P, I, P, I, P, P]
         lib.orc_summaries.restype = I
-        lib.orc_prefill.argtypes = [I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, I]
+        lib.orc_prefill.argtypes = [I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
         lib.orc_prefill.restype = I
         _lib = lib
     return _lib
@@ -139,10 +139,10 @@ def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k
 
 def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: int, Hkv: int,
             top_k: int, scale: float, P: int = 64, tiles: Optional[tuple] = None,
-            nthreads: Optional[int] = None) -> dict:
+            idx_in: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> dict:
     """Prefill chunk of T tokens on one sequence. Returns scores [ntiles][Hkv][max_blocks],
     idx [ntiles][Hkv][top_k+1], o [T][Hq][D], lse [T][Hq]; only tiles [lo, hi) are computed
-    (rows of other tiles are NaN)."""
+    (rows of other tiles are NaN). idx_in ([ntiles][Hkv][top_k+1]) replaces the selection."""
     q, k_new, v_new, k_pool, v_pool = map(_c, (q, k_new, v_new, k_pool, v_pool))
     dt = _dtype_code(q)
     table = _c(block_table, np.int32).reshape(-1)
@@ -157,6 +157,7 @@ def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: 
     rc = _load().orc_prefill(Hq, Hkv, D, P, top_k, float(scale), dt, _ptr(q), _ptr(k_new),
                              _ptr(v_new), _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
                              _ptr(table), mb, int(past_len), int(T), int(lo), int(hi),
+                             _ptr(None if idx_in is None else _c(idx_in, np.int32)),
                              _ptr(scores), _ptr(idx), _ptr(o), _ptr(lse),
                              int(nthreads or default_threads()))
     if rc != 0:

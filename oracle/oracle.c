@@ -299,6 +299,7 @@ typedef struct {
     double scale;
     const void *q, *k_new, *v_new, *k_pool, *v_pool;
     const int32_t* table;        /* one sequence: [max_blocks] */
+    const int32_t* idx_in;       /* nullable [ntiles][Hkv][top_k+1] lists to attend over */
     const double* S;             /* [nblocks][Hkv][D] summaries of the appended sequence */
     double *scores_out, *o_out, *lse_out;
     int32_t* idx_out;
@@ -353,6 +354,11 @@ static int prefill_unit(const prefill_args* a, int tau, int g) {
     sel[keff] = diag;                                  /* the diagonal block is always kept */
     for (int e = keff + 1; e <= K; ++e) sel[e] = -1;
     if (a->idx_out) memcpy(a->idx_out + ((size_t)tau * a->Hkv + g) * (K + 1), sel, sizeof(int32_t) * (size_t)(K + 1));
+    if (a->idx_in) {       /* attend over a caller's lists instead (entries < 0 or > diag skipped) */
+        memcpy(sel, a->idx_in + ((size_t)tau * a->Hkv + g) * (K + 1), sizeof(int32_t) * (size_t)(K + 1));
+        keff = K;
+        for (int e = 0; e <= K; ++e) if (sel[e] < 0 || sel[e] > diag) sel[e] = -1;
+    }
 
     for (int i = i0; i < i1; ++i) {
         const int pos = a->past_len + i;
@@ -360,7 +366,7 @@ static int prefill_unit(const prefill_args* a, int tau, int g) {
             size_t n = 0;
             double m = -INFINITY, v;
             for (int e = 0; e <= keff; ++e)
-                for (int t = sel[e] * P; t < (sel[e] + 1) * P && t <= pos; ++t) {
+                for (int t = sel[e] * P; sel[e] >= 0 && t < (sel[e] + 1) * P && t <= pos; ++t) {
                     double acc = 0.0;
                     for (int d = 0; d < D; ++d) {
                         if (full_elem(a, 0, t, g, d, &v)) { rc = -4; goto done; }
@@ -376,7 +382,7 @@ static int prefill_unit(const prefill_args* a, int tau, int g) {
             for (int d = 0; d < D; ++d) o[d] = 0.0;
             size_t r = 0;
             for (int e = 0; e <= keff; ++e)
-                for (int t = sel[e] * P; t < (sel[e] + 1) * P && t <= pos; ++t, ++r) {
+                for (int t = sel[e] * P; sel[e] >= 0 && t < (sel[e] + 1) * P && t <= pos; ++t, ++r) {
                     double wt = exp(z[r] - m) / den;
                     for (int d = 0; d < D; ++d) {
                         if (full_elem(a, 1, t, g, d, &v)) { rc = -4; goto done; }
@@ -426,13 +432,14 @@ static void* prefill_worker(void* p) {
 
 /* Prefill chunk: T new tokens (q, k_new, v_new [T][..][D]) after past_len cached tokens of one
  * sequence (pool + table). Computes tiles [tile_lo, tile_hi) only.
+ * idx_in (nullable) [ntiles][Hkv][top_k+1]: lists to attend over instead of the selection.
  * scores_out (nullable) [ntiles][Hkv][max_blocks]; idx_out (nullable) [ntiles][Hkv][top_k+1];
  * o_out [T][Hq][D] and lse_out [T][Hq] (rows of the computed tiles are written). */
 int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtype,
                 const void* q, const void* k_new, const void* v_new, const void* k_pool,
                 const void* v_pool, int num_pages, const int32_t* table, int max_blocks,
-                int past_len, int T, int tile_lo, int tile_hi, double* scores_out,
-                int32_t* idx_out, double* o_out, double* lse_out, int nthreads) {
+                int past_len, int T, int tile_lo, int tile_hi, const int32_t* idx_in,
+                double* scores_out, int32_t* idx_out, double* o_out, double* lse_out, int nthreads) {
     int ntiles = (T + P - 1) / P;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P < 1 || top_k < 0 || T < 1 || past_len < 0 ||
         past_len % P || !q || !k_new || !v_new || !k_pool || !v_pool || !table || !o_out ||
@@ -443,8 +450,8 @@ int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtyp
     double* S = (double*)malloc(sizeof(double) * (size_t)nblocks * Hkv * D);
     if (!S) return -3;
     prefill_args a = {Hq, Hkv, D, P, top_k, dtype, num_pages, max_blocks, past_len, T, tile_lo,
-                      tile_hi, scale, q, k_new, v_new, k_pool, v_pool, table, S, scores_out,
-                      o_out, lse_out, idx_out, 0};
+                      tile_hi, scale, q, k_new, v_new, k_pool, v_pool, table, idx_in, S,
+                      scores_out, o_out, lse_out, idx_out, 0};
     if (nthreads < 1) nthreads = 1;
     prefill_job* jobs = (prefill_job*)malloc(sizeof(prefill_job) * (size_t)nthreads);
     if (!jobs) { free(S); return -3; }

@@ -53,8 +53,8 @@ def test_workspace_sizes():
     c = cfg()
     st, sel = ws_size(c, L.MSA_OP_SELECT)
     assert st == 0
-    # scores 8 x 16384 fp32 + 8 histogram rows of 4096 counters
-    assert sel == 8 * 16384 * 4 + 8 * 4096 * 4
+    # scores: 8 rows x 16384 blocks, fp32
+    assert sel == 8 * 16384 * 4
     st, att = ws_size(c, L.MSA_OP_ATTEND)
     assert st == 0 and att > 0
     st, dec = ws_size(c, L.MSA_OP_DECODE)
