@@ -89,6 +89,7 @@ def main():
     ap.add_argument("--workload", default="decode_bf16_1m_paged")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
@@ -153,27 +154,30 @@ def main():
     steps = replays * per_graph
     wreplays = max(1, args.warmup // per_graph)
 
-    g_dec = timed_graph(decode, per_graph, torch)
-    run_graph(g_dec, wreplays, torch)
-    t_step = run_graph(g_dec, replays, torch) / steps
-    log("decode step: %.2f us" % (t_step * 1e6))
+    def timed(fn):
+        """seconds per call of fn(i), graph-replayed over the same rotation as the step"""
+        g = timed_graph(fn, per_graph, torch)
+        run_graph(g, wreplays, torch)
+        return run_graph(g, replays, torch) / steps
 
-    # stage timings (same rotation): Step 1 (score + top-k) and Step 2 (attend + merge)
-    g_sel = timed_graph(select, per_graph, torch)
-    run_graph(g_sel, wreplays, torch)
-    t_sel = run_graph(g_sel, replays, torch) / steps
-    g_att = timed_graph(attend, per_graph, torch)
-    run_graph(g_att, wreplays, torch)
-    t_att = run_graph(g_att, replays, torch) / steps
+    t_step = timed(decode)
+    log("decode step: %.2f us" % (t_step * 1e6))
+    # stage timings: Step 1 scoring alone (one kernel), Step 1 (score + top-k), Step 2 (attend + merge)
+    mb = (max_len + 63) // 64
+    sc_buf = torch.empty((B, Hkv, mb), dtype=torch.float32, device=dev)
+    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf))
+    t_sel = timed(select)
+    t_att = timed(attend)
     torch.cuda.synchronize()
-    kv_bytes = np.mean([selected_kv_bytes(idx_bufs[l], cases[l].seq_lens, elem=2 if c0.dtype == "bf16" else 4)
-                        for l in range(L)])
+    elem = 2 if c0.dtype == "bf16" else 4
+    kv_bytes = float(np.mean([selected_kv_bytes(idx_bufs[l], cases[l].seq_lens, elem=elem) for l in range(L)]))
     nb_tot = sum((int(n) + 63) // 64 for n in c0.seq_lens)
-    s1_bytes = nb_tot * Hkv * D * 4
+    # algorithmic bytes of one scoring launch: summaries + block-table entries read, scores written
+    score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
     kv_gbps = kv_bytes / t_att / 1e9
-    s1_gbps = s1_bytes / t_sel / 1e9
-    log("select %.2f us (%.0f GB/s of summaries); attend %.2f us (%.0f GB/s of selected KV)"
-        % (t_sel * 1e6, s1_gbps, t_att * 1e6, kv_gbps))
+    score_gbps = score_bytes / t_score / 1e9
+    log("score %.2f us (%.0f GB/s); select %.2f us; attend %.2f us (%.0f GB/s of selected KV)"
+        % (t_score * 1e6, score_gbps, t_sel * 1e6, t_att * 1e6, kv_gbps))
 
     rec = {
         "metric": METRIC,
@@ -193,14 +197,20 @@ def main():
                    "caches_rotated": L, "graph_steps": per_graph},
         "kv_GBps": kv_gbps,
         "kv_hbm_frac": kv_gbps / HBM_PEAK_GBPS,
-        "stage1_GBps": s1_gbps,
-        "stage1_us": t_sel * 1e6,
-        "attend_us": t_att * 1e6,
-        "roofline": {"bound": "hbm", "kernel": "msa_attend (gather-attend + merge)",
-                     "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": kv_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": kv_bytes},
+        "roofline": {"bound": "hbm", "kernel": "k_score_decode (msa_score): Step 1 block scoring",
+                     "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": score_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": score_bytes, "us_per_launch": t_score * 1e6},
+        "stages_us": {"score": t_score * 1e6, "select": t_sel * 1e6, "attend_merge": t_att * 1e6,
+                      "step": t_step * 1e6},
+        "attend_roofline": {"bound": "hbm", "kernel": "k_attend_decode + k_merge (msa_attend)",
+                            "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": kv_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kv_bytes},
     }
+    del caches, cases, q_ring, kn_ring, vn_ring, idx_bufs, ws
+    torch.cuda.empty_cache()
+    if not args.no_batched:
+        rec["batched_attend"] = bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev)
 
     # ---- prefill
     if not args.no_prefill:
@@ -209,9 +219,11 @@ def main():
         except msa.MsaError as e:
             log("prefill skipped: %s" % e)
             rec["prefill"] = None
-    # ---- CPU oracle baseline
+    # ---- CPU oracle baseline (regenerates the first cache of the workload: same seed, same data)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(args, cases[0], caches[0], torch, np)
+        c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed))
+        rec["cpu_baseline"] = cpu_baseline(args, c, torch, np)
+        del c
     print(json.dumps(rec), flush=True)
 
 
@@ -250,7 +262,40 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
             "note": "whole chunk: append + summaries + tile query + score + top-k + MFMA attend"}
 
 
-def cpu_baseline(args, case, cache, torch, np):
+def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev):
+    """Gather-attend bandwidth on the batch-8, 131072-token workload (64 MiB of selected K/V per
+    launch, so the stage is less latency-bound than at batch 1). Two caches rotated."""
+    kw = workload("decode_bf16_b8_128k", seed=args.seed)
+    L = 2
+    items = []
+    for layer in range(L):
+        c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed + 1000 * layer))
+        table = torch.from_numpy(c.block_table).to(dev)
+        lens = torch.from_numpy(c.seq_lens).to(dev)
+        S = torch.empty((c.num_pages, c.Hkv, c.D), dtype=torch.float32, device=dev)
+        cache = msa.KVCache(c.k_pool, c.v_pool, S, table, lens)
+        cfg = msa.make_config(c.Hq, c.Hkv, c.top_k, dtype="bf16", softmax_scale=c.scale)
+        msa.msa_build_summaries(cfg, cache, c.B, c.max_seq_len)
+        idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device=dev)
+        msa.msa_select(cfg, c.q, cache, c.B, c.max_seq_len, idx)
+        items.append((c, cache, idx))
+    c0 = items[0][0]
+    out = torch.empty_like(c0.q)
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, c0.B, c0.max_seq_len), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    g = timed_graph(lambda i: msa.msa_attend(cfg, items[i % L][0].q, items[i % L][1], c0.B, c0.max_seq_len,
+                                             items[i % L][2], out, workspace=ws), 8, torch)
+    run_graph(g, 3, torch)
+    n = 25
+    t = run_graph(g, n, torch) / (8 * n)
+    kv = float(np.mean([selected_kv_bytes(it[2], it[0].seq_lens) for it in items]))
+    log("batch-8 attend: %.2f us, %.0f GB/s of selected KV" % (t * 1e6, kv / t / 1e9))
+    return {"workload": "decode_bf16_b8_128k", "attend_us": t * 1e6, "kv_GBps": kv / t / 1e9,
+            "kv_hbm_frac": kv / t / 1e9 / HBM_PEAK_GBPS, "bytes_per_launch": kv}
+
+
+def cpu_baseline(args, case, torch, np):
     """The fp64 oracle (untuned) on a bounded sample of the same decode workload: select from
     cached block summaries + attend, for as many steps as fit in about --cpu-seconds."""
     import oracle
@@ -271,7 +316,7 @@ def cpu_baseline(args, case, cache, torch, np):
     t0 = time.perf_counter()
     oracle.decode(**kw)
     one = time.perf_counter() - t0
-    n = int(max(2, min(200, args.cpu_seconds / max(one, 1e-3))))
+    n = int(max(2, min(5000, args.cpu_seconds / max(one, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(n):
         oracle.decode(**kw)

@@ -85,7 +85,7 @@ typedef struct msa_config {
     int32_t head_dim;         /* must be 128 */
     int32_t block_size;       /* must be 64 (== page size) */
     int32_t top_k;            /* 1 .. MSA_MAX_TOP_K blocks kept per group (per tile in prefill) */
-    float softmax_scale;      /* logit scale, 1/sqrt(head_dim) in the usual setting */
+    float softmax_scale;      /* logit scale > 0, 1/sqrt(head_dim) in the usual setting */
     int32_t q_dtype;          /* msa_dtype of q and k_new/v_new */
     int32_t kv_dtype;         /* msa_dtype of the K/V pools; must equal q_dtype */
     int32_t out_dtype;        /* msa_dtype of out; must equal q_dtype */
@@ -114,6 +114,15 @@ msa_status msa_workspace_size(const msa_config* cfg, int32_t op, int32_t batch,
  * every block of every sequence, for b < batch. */
 msa_status msa_build_summaries(const msa_config* cfg, const msa_kv_cache* cache, int32_t batch,
                                int32_t max_seq_len, void* stream);
+
+/* Step 1 scoring alone ([MGS §1 Step 1] index branch, before TopK): scores_out[b][g][j] =
+ * <mean of the group's query heads, summaries[block_table[b][j]][g]> for j < nb_b, -inf for
+ * j in [nb_b, ceil(max_seq_len/64)) and for blocks whose page id is out of range.
+ *   q           [batch][Hq][128] q_dtype
+ *   scores_out  [batch][Hkv][ceil(max_seq_len/64)] float32 (required)
+ * One kernel launch; no workspace. */
+msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* cache,
+                     int32_t batch, int32_t max_seq_len, float* scores_out, void* stream);
 
 /* Step 1 ([MGS §1 Step 1]): per (sequence b, KV group g) score every block j < nb_b with
  * <mean of the group's query heads, summary> and keep the top-k.

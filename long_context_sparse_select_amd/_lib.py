@@ -15,7 +15,7 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_SCORE_MEAN_KEY, MSA_SCORE_MAX_TOKEN = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL = range(4)
 
-EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_select", "msa_attend",
+EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_score", "msa_select", "msa_attend",
             "msa_decode_step", "msa_prefill_chunk", "msa_status_string")
 
 
@@ -60,6 +60,7 @@ def load_library():
         C, K = ctypes.POINTER(MsaConfig), ctypes.POINTER(MsaKvCache)
         lib.msa_workspace_size.argtypes = [C, I, I, I, I, ctypes.POINTER(Z)]
         lib.msa_build_summaries.argtypes = [C, K, I, I, V]
+        lib.msa_score.argtypes = [C, V, K, I, I, V, V]
         lib.msa_select.argtypes = [C, V, K, I, I, V, V, V, Z, V]
         lib.msa_attend.argtypes = [C, V, K, I, I, V, V, V, V, Z, V]
         lib.msa_decode_step.argtypes = [C, V, K, I, I, V, V, V, V, V, V, V, Z, V]
@@ -136,6 +137,13 @@ def msa_build_summaries(cfg: MsaConfig, cache: KVCache, batch: int, max_seq_len:
     c = cache.struct()
     _check(load_library().msa_build_summaries(ctypes.byref(cfg), ctypes.byref(c), batch, max_seq_len,
                                               _stream(stream, cache.k_pages)), "msa_build_summaries")
+
+
+def msa_score(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: int, scores_out,
+              stream=None) -> None:
+    c = cache.struct()
+    _check(load_library().msa_score(ctypes.byref(cfg), _p(q), ctypes.byref(c), batch, max_seq_len,
+                                    _p(scores_out), _stream(stream, q)), "msa_score")
 
 
 def msa_select(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: int, idx_out,

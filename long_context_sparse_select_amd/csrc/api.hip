@@ -3,7 +3,8 @@
 //
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
-//   msa_decode_step   [append + block summary] -> score -> top-k -> attend (+ split-K merge)
+//   msa_decode_step   score -> top-k (+ append: new K/V row, that block's summary and score)
+//                     -> attend -> split-K merge
 //   msa_prefill_chunk append + summaries -> tile query -> score -> top-k (+diagonal) -> attend
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
 // HIP call, so an invalid call enqueues nothing.
@@ -37,7 +38,7 @@ msa_status check_config(const msa_config* c) {
   if (c->kv_dtype != MSA_F32 && c->kv_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->out_dtype != MSA_F32 && c->out_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->score_mode != MSA_SCORE_MEAN_KEY && c->score_mode != MSA_SCORE_MAX_TOKEN) return MSA_ERR_INVALID_ARG;
-  if (!std::isfinite(c->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (!std::isfinite(c->softmax_scale) || !(c->softmax_scale > 0.f)) return MSA_ERR_INVALID_ARG;
   if (c->head_dim != MSA_HEAD_DIM || c->block_size != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
   if (c->top_k > MSA_MAX_TOP_K) return MSA_ERR_UNSUPPORTED;
   if (c->num_q_heads / c->num_kv_heads > MSA_MAX_GROUP) return MSA_ERR_UNSUPPORTED;
@@ -117,9 +118,11 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
     if (s_ != MSA_OK) return s_;             \
   } while (0)
 
-// Step 1 on validated arguments; pages (page ids of the kept blocks) is the decode step's extra
+// Step 1 on validated arguments; pages (page ids of the kept blocks) and the appended token
+// (k_new / v_new, nullable) are the decode step's extras
 msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
-                      float* scores, int row_stride, int32_t* idx, int32_t* pages, hipStream_t st) {
+                      float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
+                      const void* v_new, hipStream_t st) {
   const bool bf16 = cfg->q_dtype == MSA_BF16;
   const CacheArgs ca = cache_args(cache);
   MSA_TRY(hip_status(launch_score_decode(bf16, q, ca, B, cfg->num_q_heads, cfg->num_kv_heads, max_len, scores,
@@ -139,7 +142,14 @@ msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   t.table = cache->block_table;
   t.max_blocks = cache->max_blocks;
   t.num_pages = cache->num_pages;
-  return hip_status(launch_topk(t, st));
+  t.k_new = k_new;
+  t.v_new = v_new;
+  t.kpool = cache->k_pages;
+  t.vpool = cache->v_pages;
+  t.S = cache->summaries;
+  t.q = q;
+  t.Hq = cfg->num_q_heads;
+  return hip_status(launch_topk(t, bf16, st));
 }
 
 // Step 2 on validated arguments
@@ -205,6 +215,19 @@ msa_status msa_build_summaries(const msa_config* cfg, const msa_kv_cache* cache,
                                            max_seq_len, (hipStream_t)stream));
 }
 
+msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
+                     int32_t max_seq_len, float* scores_out, void* stream) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, false, true));
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (q == nullptr || scores_out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (batch == 0) return MSA_OK;
+  const int row_stride = (max_seq_len + MSA_BLOCK - 1) / MSA_BLOCK;
+  return hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cache), batch, cfg->num_q_heads,
+                                        cfg->num_kv_heads, max_seq_len, scores_out, row_stride,
+                                        (hipStream_t)stream));
+}
+
 msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
                       int32_t max_seq_len, float* scores_out, int32_t* idx_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -216,7 +239,7 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
-  return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr,
+  return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
                     (hipStream_t)stream);
 }
 
@@ -246,14 +269,10 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
-  const bool bf16 = cfg->q_dtype == MSA_BF16;
-  if (k_new != nullptr)
-    MSA_TRY(hip_status(launch_append_decode(bf16, cache_args(cache), k_new, v_new, batch, cfg->num_kv_heads,
-                                            max_seq_len, st)));
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
   int32_t* pages = at<int32_t>(workspace, L.pages);
-  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx, pages, st));
+  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx, pages, k_new, v_new, st));
   return run_attend(cfg, q, cache, batch, max_seq_len, idx, pages, out, lse_out, L, workspace, st);
 }
 
@@ -294,7 +313,8 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   t.lens = nullptr;
   t.max_len = max_len;
   t.base_blocks = past_blocks;
-  MSA_TRY(hip_status(launch_topk(t, st)));
+  t.k_new = nullptr;   // TopkArgs{} zero-initialises the decode-only fields; no append in prefill
+  MSA_TRY(hip_status(launch_topk(t, true, st)));
   PrefillArgs p{};
   p.q = q;
   p.kpool = cache->k_pages;

@@ -82,7 +82,7 @@ constexpr int kMaxSplit = 256;
 
 template <typename T> __device__ __forceinline__ void store_out2(T* out, long long i, float a, float b);
 template <> __device__ __forceinline__ void store_out2<uint16_t>(uint16_t* out, long long i, float a, float b) {
-  reinterpret_cast<uint32_t*>(out)[i / 2] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  reinterpret_cast<uint32_t*>(out)[i / 2] = pack_bf16x2(a, b);
 }
 template <> __device__ __forceinline__ void store_out2<float>(float* out, long long i, float a, float b) {
   reinterpret_cast<float2*>(out)[i / 2] = make_float2(a, b);
@@ -229,6 +229,18 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ns = a.nsplit;
   const long long unit0 = ((long long)b * a.Hq + g * G) * ns;   // head h, split s -> unit0 + h*ns + s
+  // thread -> float4 column c of G*128/4 and split group sg; its first batch of partial outputs
+  // is requested before the (m, l) phase so that both round trips overlap
+  constexpr int kCols = G * (kD / 4);
+  constexpr int kGroups = 256 / kCols > 0 ? 256 / kCols : 1;
+  constexpr int kBatch = 32;
+  const int c = tid % kCols, sg = tid / kCols;
+  const int hc = c / (kD / 4), c4 = c % (kD / 4);
+  const float* po = a.part_o + (unit0 + hc * ns) * kD + c4 * 4;
+  float4 v[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i)
+    v[i] = *reinterpret_cast<const float4*>(po + (long long)min(sg + kGroups * i, ns - 1) * kD);
   // per-head max and weights: wave w handles heads w, w+4, ...
   for (int h = wave; h < G; h += 4) {
     const float* ml = a.part_ml + (unit0 + h * ns) * 2;
@@ -258,20 +270,16 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
     if (lane == 0) { s_M[h] = mx; s_L[h] = L; }
   }
   __syncthreads();
-  // weighted sum of the partial outputs: thread -> float4 column c of G*128/4, split group sg
-  constexpr int kCols = G * (kD / 4);
-  constexpr int kGroups = 256 / kCols > 0 ? 256 / kCols : 1;
-  constexpr int kBatch = 16;
+  // weighted sum of the partial outputs
+  const int h = hc;
   float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int c = tid % kCols, sg = tid / kCols;
-  const int h = c / (kD / 4), c4 = c % (kD / 4);
   if (sg < kGroups) {
-    const float* po = a.part_o + (unit0 + h * ns) * kD + c4 * 4;
     for (int s0 = sg; s0 < ns; s0 += kGroups * kBatch) {
-      float4 v[kBatch];
+      if (s0 != sg) {
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        v[i] = *reinterpret_cast<const float4*>(po + (long long)min(s0 + kGroups * i, ns - 1) * kD);
+        for (int i = 0; i < kBatch; ++i)
+          v[i] = *reinterpret_cast<const float4*>(po + (long long)min(s0 + kGroups * i, ns - 1) * kD);
+      }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int s2 = s0 + kGroups * i;

@@ -37,9 +37,6 @@ __device__ __forceinline__ int swap_bits23(int x) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
 
 template <int G>
 struct PrefillBlockLoader {
@@ -179,20 +176,23 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[t], 0, 0, 0);
       }
     }
-    // ---- logits (log2 domain), causal mask on the diagonal block, online softmax
+    // ---- online softmax (log2 domain): max on raw scores, p = exp2(s * scale - m)
+    if (is_diag) {  // causal mask inside the diagonal block only
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // C row of register i in lane group c -> S^T row -> key index within the block
+          const int key = swap_bits23(32 * t + 8 * (i >> 2) + 4 * c + (i & 3));
+          if (key > il) s[t][i] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // C row of register i in lane group c -> S^T row -> key index within the block
-        const int key = swap_bits23(32 * t + 8 * (i >> 2) + 4 * c + (i & 3));
-        float z = s[t][i] * a.scale_log2;
-        if (is_diag && key > il) z = -INFINITY;
-        s[t][i] = z;
-        mx = fmaxf(mx, z);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     const float mn = fmaxf(m, mx);
     const float mref = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = fast_exp2(m - mref);        // m = -inf -> 0
@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(s[t][i] - mref);
+        const float p = fast_exp2(fmaf(s[t][i], a.scale_log2, -mref));
         s[t][i] = p;
         psum += p;
       }
@@ -216,8 +216,8 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int t = ks >> 1, b = (ks & 1) * 8;
-      pf[ks] = as_bf16x8(make_uint4(pack_bf16(s[t][b + 0], s[t][b + 1]), pack_bf16(s[t][b + 2], s[t][b + 3]),
-                                    pack_bf16(s[t][b + 4], s[t][b + 5]), pack_bf16(s[t][b + 6], s[t][b + 7])));
+      pf[ks] = as_bf16x8(make_uint4(pack_bf16x2(s[t][b + 0], s[t][b + 1]), pack_bf16x2(s[t][b + 2], s[t][b + 3]),
+                                    pack_bf16x2(s[t][b + 4], s[t][b + 5]), pack_bf16x2(s[t][b + 6], s[t][b + 7])));
     }
     // ---- O^T += V^T P^T: dim tile dt, keys 16ks + 8c .. +7
 #pragma unroll
@@ -242,8 +242,8 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       uint2 pk;
-      pk.x = pack_bf16(o[dt][4 * i4 + 0] * inv, o[dt][4 * i4 + 1] * inv);
-      pk.y = pack_bf16(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
+      pk.x = pack_bf16x2(o[dt][4 * i4 + 0] * inv, o[dt][4 * i4 + 1] * inv);
+      pk.y = pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * c) = pk;
     }
   if (a.lse != nullptr && c == 0)

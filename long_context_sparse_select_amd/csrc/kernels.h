@@ -19,8 +19,6 @@ struct CacheArgs {
 
 // ---- block summaries / append
 hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv, int max_len, hipStream_t st);
-hipError_t launch_append_decode(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new, int B,
-                                int Hkv, int max_len, hipStream_t st);
 hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
                                  int past_blocks, int T, int Hkv, hipStream_t st);
 
@@ -33,7 +31,7 @@ hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past
 
 // ---- Step 1 top-k
 struct TopkArgs {
-  const float* scores;
+  float* scores;       // the decode append path rewrites the last block's score
   int row_stride;
   int32_t* idx;
   int idx_stride;      // top_k (decode) or top_k + 1 (prefill)
@@ -49,8 +47,17 @@ struct TopkArgs {
   const int32_t* table;
   int max_blocks;
   int num_pages;
+  // decode append (nullable k_new): write k_new/v_new [B][Hkv][128] at position seq_len-1,
+  // recompute that block's summary in S and its score for the row's group before selecting
+  const void* k_new;
+  const void* v_new;
+  void* kpool;
+  void* vpool;
+  float* S;
+  const void* q;
+  int Hq;
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, bool bf16, hipStream_t st);
 
 // ---- Step 2, decode
 struct AttendArgs {

@@ -7,11 +7,13 @@
 // (prefill); a block's score is <index query, block summary>, unscaled, in fp32.
 //
 // Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 per sequence), so the
-// kernel is shaped for HBM: a workgroup owns a chunk of 16 logical blocks of one sequence,
+// kernel is shaped for HBM: a workgroup owns a chunk of 8 logical blocks of one sequence,
 // stages the chunk's page ids and the Hkv index queries in LDS, and then walks (block, group)
 // pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 the workgroup reads the
-// chunk's 16 pages as 16 contiguous 4 KiB runs, whatever the page permutation, and each lane
-// has all 16 of its loads in flight before any arithmetic.
+// chunk's 8 pages as 8 contiguous 4 KiB runs, whatever the page permutation, and each lane
+// has all of its loads in flight before any arithmetic. The chunk's scores are staged in LDS
+// and leave as one contiguous run per row. The number of KV heads is a template parameter for
+// the power-of-two cases, so the pair-index arithmetic is shifts, not divisions.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,8 +21,19 @@ namespace msa {
 
 namespace {
 
-constexpr int kChunk = 16;    // logical blocks per workgroup (decode)
-constexpr int kUnroll = 16;   // pairs in flight per 32-lane slot
+constexpr int kChunk = 8;     // logical blocks per workgroup (decode)
+constexpr int kUnroll = 8;    // pairs in flight per 32-lane slot
+
+// 8 consecutive elements as floats, in 16 B vector loads
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  f[0] = bf16lo(w.x); f[1] = bf16hi(w.x); f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+  f[4] = bf16lo(w.z); f[5] = bf16hi(w.z); f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+}
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
 
 template <typename T> __device__ __forceinline__ float ld(const T* p, long long i);
 template <> __device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
@@ -28,13 +41,16 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, lon
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-template <typename TQ>
+// HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
+// shifts); HKV == 0: a runtime count (generic path).
+template <typename TQ, int HKV>
 __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const float* __restrict__ S,
                                                       const int32_t* __restrict__ table,
                                                       const int32_t* __restrict__ lens, int num_pages,
-                                                      int max_blocks, int Hq, int Hkv, int max_len,
+                                                      int max_blocks, int Hq, int hkv_arg, int max_len,
                                                       float* __restrict__ scores, int row_stride) {
-  extern __shared__ float s_qidx[];             // [Hkv][128] index queries
+  const int Hkv = HKV > 0 ? HKV : hkv_arg;
+  extern __shared__ float s_qidx[];             // [Hkv][128] index queries, then [Hkv][kChunk] scores
   __shared__ int s_page[kChunk];
   const int b = blockIdx.y;
   const int j0 = blockIdx.x * kChunk;
@@ -46,27 +62,25 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   // the page ids, the sequence length and the queries are loaded in one round trip: the table
   // read does not wait for the length (j < row_stride <= max_blocks keeps it in bounds)
   const int my_page = table[(long long)b * max_blocks + min(j0 + (tid & (kChunk - 1)), row_stride - 1)];
-  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads
+  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads.
+    // Thread -> (group, 8 dims): its G head rows are loaded as 16 B vectors, all in flight at once.
     const int G = Hq / Hkv;
     const TQ* qb = q + (long long)b * Hq * kD;
-    const int ne = Hkv * kD;
-    for (int e0 = 0; e0 < ne; e0 += 1024) {
-      float v[4][kMaxGroup];
+    for (int c0 = 0; c0 < Hkv * (kD / 8); c0 += 256) {
+      const int cc = min(c0 + tid, Hkv * (kD / 8) - 1);
+      const int g = cc / (kD / 8), d8 = (cc % (kD / 8)) * 8;
+      float v[kMaxGroup][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {     // all loads first (clamped in-bounds indices)
-        const int e = min(e0 + tid + 256 * i, ne - 1);
-        const int g = e / kD, d = e % kD;
+      for (int h = 0; h < kMaxGroup; ++h) load8(qb + (long long)(g * G + min(h, G - 1)) * kD + d8, v[h]);
+      if (c0 + tid < Hkv * (kD / 8)) {
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) v[i][h] = ld(qb, (long long)(g * G + min(h, G - 1)) * kD + d);
-      }
+        for (int e = 0; e < 8; ++e) {
+          float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = e0 + tid + 256 * i;
-        float acc = 0.f;
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h)
-          if (h < G) acc += v[i][h];
-        if (e < ne) s_qidx[e] = acc / (float)G;
+          for (int h = 0; h < kMaxGroup; ++h)
+            if (h < G) acc += v[h][e];
+          s_qidx[g * kD + d8 + e] = acc / (float)G;
+        }
       }
     }
   }
@@ -77,6 +91,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   const int l32 = tid & 31;     // 4 dims per lane
   const int npairs = (jend - j0) * Hkv;
   const bool any_page = num_pages > 0;
+  float* s_sc = s_qidx + Hkv * kD;
   for (int p0 = 0; p0 < npairs; p0 += 8 * kUnroll) {
     float4 sv[kUnroll];
 #pragma unroll
@@ -100,11 +115,14 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       part = fmaf(qv.w, sv[u].w, part);
       part = row16_sum(part);
       part += __shfl_xor(part, 16);
-      if (l32 == 0) {
-        const long long row = (long long)b * Hkv + g;
-        scores[row * row_stride + j] = (j < nb && s_page[jl] >= 0) ? part : -INFINITY;
-      }
+      if (l32 == 0) s_sc[g * kChunk + jl] = (j < nb && s_page[jl] >= 0) ? part : -INFINITY;
     }
+  }
+  __syncthreads();
+  // each row's chunk of scores leaves as one contiguous run
+  for (int e = tid; e < Hkv * kChunk; e += 256) {
+    const int g = e / kChunk, jl = e % kChunk;
+    if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = s_sc[e];
   }
 }
 
@@ -226,21 +244,44 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
   }
 }
 
+
+template <typename TQ>
+void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
+                        int row_stride, hipStream_t st) {
+  const dim3 grid((row_stride + kChunk - 1) / kChunk, B);
+  const size_t lds = (size_t)Hkv * (kD + kChunk) * sizeof(float);
+#define MSA_SCORE_CASE(H)                                                                                  \
+  case H:                                                                                                  \
+    k_score_decode<TQ, H><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, Hkv, \
+                                                  max_len, scores, row_stride);                            \
+    break;
+  switch (Hkv) {
+    MSA_SCORE_CASE(1)
+    MSA_SCORE_CASE(2)
+    MSA_SCORE_CASE(4)
+    MSA_SCORE_CASE(8)
+    MSA_SCORE_CASE(16)
+    MSA_SCORE_CASE(32)
+    MSA_SCORE_CASE(64)
+    default:
+      k_score_decode<TQ, 0><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, Hkv,
+                                                    max_len, scores, row_stride);
+  }
+#undef MSA_SCORE_CASE
+}
+
 }  // namespace
 
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
                                float* scores, int row_stride, hipStream_t st) {
   if (B == 0 || row_stride == 0) return hipSuccess;
-  const dim3 grid((row_stride + kChunk - 1) / kChunk, B);
-  const size_t lds = (size_t)Hkv * kD * sizeof(float);
   if (bf16)
-    k_score_decode<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)q, c.S, c.table, c.lens, c.num_pages,
-                                                     c.max_blocks, Hq, Hkv, max_len, scores, row_stride);
+    launch_score_typed<uint16_t>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
   else
-    k_score_decode<float><<<grid, 256, lds, st>>>((const float*)q, c.S, c.table, c.lens, c.num_pages,
-                                                  c.max_blocks, Hq, Hkv, max_len, scores, row_stride);
+    launch_score_typed<float>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
   return hipGetLastError();
 }
+
 
 hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st) {
   const dim3 grid((T + kP - 1) / kP, Hkv);

@@ -17,34 +17,6 @@ namespace msa {
 
 namespace {
 
-template <typename T> struct Vec8;
-
-template <> struct Vec8<uint16_t> {
-  uint4 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = w; }
-  __device__ __forceinline__ void add_to(float* acc) const {
-    acc[0] += bf16lo(w.x); acc[1] += bf16hi(w.x); acc[2] += bf16lo(w.y); acc[3] += bf16hi(w.y);
-    acc[4] += bf16lo(w.z); acc[5] += bf16hi(w.z); acc[6] += bf16lo(w.w); acc[7] += bf16hi(w.w);
-  }
-};
-
-template <> struct Vec8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
-  __device__ __forceinline__ void store(float* p) const {
-    reinterpret_cast<float4*>(p)[0] = a;
-    reinterpret_cast<float4*>(p)[1] = b;
-  }
-  __device__ __forceinline__ void add_to(float* acc) const {
-    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-  }
-};
-
 // Reduce the per-lane partial sums over the wave's four rows and write the mean.
 __device__ __forceinline__ void write_mean(float* acc, int n, float* dst, int lane) {
 #pragma unroll
@@ -85,43 +57,6 @@ __global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ k
   for (int i = 0; i < 16; ++i)
     if ((lane >> 4) + 4 * i < n) v[i].add_to(acc);
   write_mean(acc, n, S + ((long long)page * Hkv + g) * kD, lane);
-}
-
-// decode append: token seq_lens[b]-1 of every sequence; then that block's summary
-template <typename T>
-__global__ void __launch_bounds__(256) k_append_decode(T* __restrict__ kpool, T* __restrict__ vpool, float* __restrict__ S,
-                                                       const int32_t* __restrict__ table,
-                                                       const int32_t* __restrict__ lens, int num_pages,
-                                                       int max_blocks, const T* __restrict__ k_new,
-                                                       const T* __restrict__ v_new, int B, int Hkv, int max_len) {
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= B * Hkv) return;
-  const int g = unit % Hkv, b = unit / Hkv;
-  const int N = clamp_len(lens[b], max_len);
-  if (N <= 0) return;
-  const int t = N - 1, j = t / kP, slot = t % kP;
-  const int page = table[(long long)b * max_blocks + j];
-  if (!page_ok(page, num_pages)) return;
-  const long long head = ((long long)page * Hkv + g) * kP * kD;
-  const int d0 = (lane & 15) * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (lane < 16) {
-    Vec8<T> kn, vn;
-    kn.load(k_new + (long long)unit * kD + d0);
-    vn.load(v_new + (long long)unit * kD + d0);
-    kn.store(kpool + head + (long long)slot * kD + d0);
-    vn.store(vpool + head + (long long)slot * kD + d0);
-    kn.add_to(acc);  // the new key enters the mean from registers, not from the pool
-  }
-  Vec8<T> v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)  // the block's older rows, all loads in flight (clamped rows)
-    v[i].load(kpool + head + (long long)min((lane >> 4) + 4 * i, max(slot - 1, 0)) * kD + d0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if ((lane >> 4) + 4 * i < slot) v[i].add_to(acc);
-  write_mean(acc, slot + 1, S + ((long long)page * Hkv + g) * kD, lane);
 }
 
 // prefill append: T new tokens after past_len (a multiple of 64) -> whole new blocks
@@ -167,22 +102,6 @@ hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv,
   else
     k_build_summaries<float><<<grid, 256, 0, st>>>((const float*)c.k, c.S, c.table, c.lens, c.num_pages,
                                                    c.max_blocks, B, Hkv, max_len, mb);
-  return hipGetLastError();
-}
-
-hipError_t launch_append_decode(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new, int B,
-                                int Hkv, int max_len, hipStream_t st) {
-  const int units = B * Hkv;
-  if (units == 0) return hipSuccess;
-  const dim3 grid((units + 3) / 4);
-  if (bf16)
-    k_append_decode<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)c.k, (uint16_t*)c.v, c.S, c.table, c.lens,
-                                                    c.num_pages, c.max_blocks, (const uint16_t*)k_new,
-                                                    (const uint16_t*)v_new, B, Hkv, max_len);
-  else
-    k_append_decode<float><<<grid, 256, 0, st>>>((float*)c.k, (float*)c.v, c.S, c.table, c.lens, c.num_pages,
-                                                 c.max_blocks, (const float*)k_new, (const float*)v_new, B, Hkv,
-                                                 max_len);
   return hipGetLastError();
 }
 

@@ -20,6 +20,13 @@
 // for the k_eff-th key over the row in memory, then an ordered compaction.
 // Decode rows also get each kept block's page id (for the attend kernel). The output depends
 // only on the scores.
+//
+// Decode step append (fused here, so the step needs no separate kernel): the workgroup of row
+// (b, g) writes the new token's K/V row of group g at position seq_len-1, recomputes that
+// block's summary from its older rows plus the new key, stores it, and re-scores the block with
+// the group's index query before selecting ("MiniMax goes sparse", §1 Step 1: the index branch
+// scores blocks through their summaries, which must describe the current cache). Its loads are
+// issued together with the row's score loads.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,6 +66,17 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(min(a, b), min(c, d));
 }
 
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+}
+
 // block-wide integer sum (all threads get it); s_tmp holds kWaves ints
 __device__ int block_sum(int v, int* s_tmp) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -92,9 +110,14 @@ __device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
 }
 
 struct TopkShared {
-  unsigned long long comp[kCap + 2];   // survivors: (key << 32) | ~index, larger = better
+  union {
+    unsigned long long comp[kCap + 2]; // survivors: (key << 32) | ~index, larger = better
+    float rows[kWaves][kD];            // decode append: per-wave partial sums of the block's keys
+  };
+  float fsum[2];
   int32_t sel[kMaxK + 4];
   int32_t selpg[kMaxK];
+  int32_t spage[kCap];
   uint32_t hist[kBins];
   uint32_t red[2 * kWaves];
   int tmp[kWaves];
@@ -120,22 +143,24 @@ __device__ __forceinline__ void pad(const TopkArgs& a, int row, int keff, int n,
 }
 
 // exact selection straight from memory: T = k_eff-th largest key, then ordered compaction
-__device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, TopkShared& sh) {
+__device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, int jlast,
+                                float fresh, TopkShared& sh) {
   const int tid = threadIdx.x;
+  auto key_of = [&](int j) { return order_key(j == jlast ? fresh : srow[j]); };
   uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
-    for (int j = tid; j < n; j += kThreads) c += order_key(srow[j]) >= cand;
+    for (int j = tid; j < n; j += kThreads) c += key_of(j) >= cand;
     if (block_sum(c, sh.tmp) >= keff) T = cand;
   }
   int gt = 0;
-  for (int j = tid; j < n; j += kThreads) gt += order_key(srow[j]) > T;
+  for (int j = tid; j < n; j += kThreads) gt += key_of(j) > T;
   const int need_eq = keff - block_sum(gt, sh.tmp);
   int run_eq = 0, run_sel = 0;
   for (int base = 0; base < n; base += kThreads) {
     const int j = base + tid;
-    const uint32_t key = j < n ? order_key(srow[j]) : 0u;
+    const uint32_t key = j < n ? key_of(j) : 0u;
     const bool is_gt = j < n && key > T;
     const bool is_eq = j < n && key == T;
     int tot_eq, tot_sel;
@@ -148,20 +173,104 @@ __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, i
   }
 }
 
+// Decode append for row (b, g): new K/V row at position N-1, the block's fresh summary, and its
+// fresh score for group g (returned, uniform). Thread -> (row r = tid/16 of the block, 8 dims).
+template <typename T>
+__device__ float decode_append(const TopkArgs& a, int row, int N, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = row / a.Hkv, g = row % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int t = N - 1, slot = t % kP;
+  const int page = a.table[(long long)b * a.max_blocks + t / kP];
+  const bool ok = page_ok(page, a.num_pages);                    // uniform
+  const int r = tid >> 4, d0 = (tid & 15) * 8;
+  const long long head = ((long long)(ok ? page : 0) * a.Hkv + g) * kP * kD;
+  const long long nrow = ((long long)b * a.Hkv + g) * kD;
+  Vec8<T> old_k, new_k;
+  const T* knew = reinterpret_cast<const T*>(a.k_new) + nrow + d0;
+  new_k.load(knew);
+  // an older row of the block (a valid address either way: the new key when the page id is bad)
+  old_k.load(ok ? reinterpret_cast<const T*>(a.kpool) + head + (long long)min(r, max(slot - 1, 0)) * kD + d0 : knew);
+  if (ok && r == slot) {   // the new token's row: K and V of this group
+    Vec8<T> new_v;
+    new_v.load(reinterpret_cast<const T*>(a.v_new) + nrow + d0);
+    new_k.store(reinterpret_cast<T*>(a.kpool) + head + (long long)slot * kD + d0);
+    new_v.store(reinterpret_cast<T*>(a.vpool) + head + (long long)slot * kD + d0);
+  }
+  float qv[kMaxGroup];
+  const T* qb = reinterpret_cast<const T*>(a.q) + ((long long)b * a.Hq + g * G) * kD;
+  if (tid < kD) {
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      const T x = qb[(long long)min(h, G - 1) * kD + tid];
+      if constexpr (sizeof(T) == 2) qv[h] = __uint_as_float((uint32_t)x << 16);
+      else qv[h] = x;
+    }
+  }
+  if (!ok) return -INFINITY;                                     // never read, never written
+  float fo[8], fn[8], f[8];
+  old_k.to_f32(fo);
+  new_k.to_f32(fn);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = r < slot ? fo[e] : (r == slot ? fn[e] : 0.f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = across_rows_sum(f[e]);    // the wave's 4 rows
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sh.rows[wave][d0 + e] = f[e];
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += sh.rows[w][tid];
+    const float summary = acc / (float)(slot + 1);
+    a.S[((long long)page * a.Hkv + g) * kD + tid] = summary;
+    float qi = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) qi += qv[h];
+    const float prod = wave_sum_f32((qi / (float)G) * summary);
+    if (lane == 0) sh.fsum[wave] = prod;
+  }
+  __syncthreads();
+  return sh.fsum[0] + sh.fsum[1];
+}
+
+template <typename T>
 __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   __shared__ TopkShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool prefill = a.lens == nullptr;
-  int n;
+  int n, N = 0;
   if (!prefill) {
-    const int N = clamp_len(a.lens[row / a.Hkv], a.max_len);
+    N = clamp_len(a.lens[row / a.Hkv], a.max_len);
     n = (N + kP - 1) / kP;
   } else {
     n = a.base_blocks + row / a.Hkv;
   }
   const int keff = min(a.k, n);
-  const float* srow = a.scores + (long long)row * a.row_stride;
+  float* srow = a.scores + (long long)row * a.row_stride;
+  // the row's score loads go first: clamped in-bounds addresses, masked when used
+  float v[kPer];
+  int pg[kPer];   // decode: the candidates' page ids, loaded with the scores (no later round trip)
+  const int32_t* trow = a.pages != nullptr ? a.table + (long long)(row / a.Hkv) * a.max_blocks : nullptr;
+  if (n <= kMaxFast && n > 0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + kThreads * i, n - 1)];
+    if (trow != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + kThreads * i, n - 1)];
+    }
+  }
+  int jlast = -1;
+  float fresh = 0.f;
+  if (!prefill && a.k_new != nullptr && N > 0) {                 // uniform
+    fresh = decode_append<T>(a, row, N, sh);
+    jlast = n - 1;
+    if (tid == 0) srow[jlast] = fresh;
+  }
 
   if (keff == n) {  // every candidate is kept
     for (int i = tid; i < n; i += kThreads) emit(a, row, i, i);
@@ -171,15 +280,12 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
 
   bool done = false;
   if (n <= kMaxFast) {
-    // every load is issued before any is used: clamped in-bounds addresses, masked afterwards
-    float v[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + kThreads * i, n - 1)];
     uint32_t key[kPer];
     uint32_t cm = 0u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      key[i] = tid + kThreads * i < n ? order_key(v[i]) : 0u;
+      const int j = tid + kThreads * i;
+      key[i] = j < n ? order_key(j == jlast ? fresh : v[i]) : 0u;
       cm = max(cm, key[i]);
     }
     const int ngroups = min(n, kThreads);     // threads holding at least one candidate
@@ -230,13 +336,16 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
     } else {
       __syncthreads();
     }
-    // ---- 2. survivors, as (key, ~index) composites
+    // ---- 2. survivors, as (key, ~index) composites (+ page id)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int j = tid + kThreads * i;
       if (j < n && key[i] >= T0) {
         const int p = atomicAdd(&sh.cnt, 1);
-        if (p < kCap) sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
+        if (p < kCap) {
+          sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
+          if (trow != nullptr) sh.spage[p] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
+        }
       }
     }
     __syncthreads();
@@ -249,14 +358,14 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
       for (int e = tid; e < m; e += kThreads) {
         const unsigned long long ce = sh.comp[e];
         const int je = (int)~(uint32_t)ce;
-        const int pg = a.pages != nullptr ? page_of(a, row, je) : -1;   // latency hidden by the ranking
+        const int pge = trow != nullptr ? sh.spage[e] : -1;
         int rank = 0;
 #pragma unroll 4
         for (int f = 0; f < npair; ++f) {
           const ulonglong2 c2 = cp[f];
           rank += (c2.x > ce) + (c2.y > ce);
         }
-        if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pg; }
+        if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pge; }
       }
       if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
       __syncthreads();
@@ -277,15 +386,18 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
       done = true;
     }
   }
-  if (!done) select_fallback(a, srow, row, n, keff, sh);
+  if (!done) select_fallback(a, srow, row, n, keff, jlast, fresh, sh);
   pad(a, row, keff, n, prefill);
 }
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+hipError_t launch_topk(const TopkArgs& a, bool bf16, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  k_topk<<<a.rows, kThreads, 0, st>>>(a);
+  if (bf16)
+    k_topk<uint16_t><<<a.rows, kThreads, 0, st>>>(a);
+  else
+    k_topk<float><<<a.rows, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ def test_workspace_sizes():
     ("keep_local", 1, L.MSA_ERR_UNSUPPORTED),
     ("q_tile", 32, L.MSA_ERR_UNSUPPORTED),
     ("softmax_scale", float("nan"), L.MSA_ERR_INVALID_ARG),
+    ("softmax_scale", -0.5, L.MSA_ERR_INVALID_ARG),
+    ("softmax_scale", 0.0, L.MSA_ERR_INVALID_ARG),
 ])
 def test_config_validation(field, value, status):
     c = cfg()

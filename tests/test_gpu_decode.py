@@ -263,3 +263,17 @@ def test_full_size_mixed_batch_sampled():
             ref = oracle.decode(idx_in=gi, **inputs)
         assert_close(host_f64(res["o"][b:b + 1]), ref["o"], "bf16", "o b=%d" % b)
         assert_close(res["lse"][b:b + 1].cpu().numpy(), ref["lse"], "bf16", "lse b=%d" % b, lse=True)
+
+
+def test_score_entry_point_matches_select_scores():
+    """msa_score (scoring alone) writes exactly the scores msa_select reports."""
+    c = make_decode_case(B=3, Hq=32, Hkv=8, lens=[9000, 130, 4096], top_k=8, dtype="bf16", seed=32, permute=True)
+    d = to_device(c)
+    mb = (c.max_seq_len + 63) // 64
+    s1 = torch.empty((c.B, c.Hkv, mb), dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
+    msa.msa_score(d.cfg, d.q, d.cache, c.B, c.max_seq_len, s1)
+    msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
