@@ -30,6 +30,10 @@ SMALL = [
     ("f32_g2_tail", dict(B=2, Hq=4, Hkv=2, lens=[2049, 63], top_k=5, dtype="f32", permute=True)),
     ("bf16_g1", dict(B=1, Hq=4, Hkv=4, lens=[3333], top_k=7, dtype="bf16")),
     ("bf16_g8_bigk", dict(B=1, Hq=16, Hkv=2, lens=[20000], top_k=300, dtype="bf16")),
+    # enough (sequence, group) rows that the attend runs four blocks per workgroup; short rows
+    # leave chunks with 1..3 attended blocks
+    ("bf16_g2_wide", dict(B=6, Hq=16, Hkv=8, lens=[70000, 4096, 65, 1, 33333, 9000], top_k=64,
+                          dtype="bf16", permute=True)),
 ]
 
 
