@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--counters", action="store_true",
+                    help="counter pass: eager launches of the scoring kernel over the rotating caches and of a "
+                         "256 MiB device copy (the byte-count calibration), for rocprofv3 --pmc; no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -149,6 +152,12 @@ def main():
         msa.msa_attend(cfg, q_ring[i % R], caches[layer], B, max_len, idx_bufs[layer], out, lse_out=lse,
                        workspace=ws)
 
+    mb = (max_len + 63) // 64
+    sc_buf = torch.empty((B, Hkv, mb), dtype=torch.float32, device=dev)
+    if args.counters:
+        counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
+        return
+
     per_graph = L * R // math.gcd(L, R) if L * R <= 64 else L
     replays = max(1, args.steps // per_graph)
     steps = replays * per_graph
@@ -163,8 +172,6 @@ def main():
     t_step = timed(decode)
     log("decode step: %.2f us" % (t_step * 1e6))
     # stage timings: Step 1 scoring alone (one kernel), Step 1 (score + top-k), Step 2 (attend + merge)
-    mb = (max_len + 63) // 64
-    sc_buf = torch.empty((B, Hkv, mb), dtype=torch.float32, device=dev)
     t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf))
     t_sel = timed(select)
     t_att = timed(attend)
@@ -199,7 +206,7 @@ def main():
         "kv_hbm_frac": kv_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "k_score_decode (msa_score): Step 1 block scoring",
                      "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": score_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": score_gbps / HBM_PEAK_GBPS, "traffic": None, "traffic_detail": None,
                      "bytes_per_launch": score_bytes, "us_per_launch": t_score * 1e6},
         "stages_us": {"score": t_score * 1e6, "select": t_sel * 1e6, "attend_merge": t_att * 1e6,
                       "step": t_step * 1e6},
@@ -207,6 +214,10 @@ def main():
                             "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": kv_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kv_bytes},
     }
+    tr = recorded_traffic(score_bytes)
+    if tr is not None:
+        rec["roofline"]["traffic"] = tr["bytes_per_launch"]
+        rec["roofline"]["traffic_detail"] = tr
     del caches, cases, q_ring, kn_ring, vn_ring, idx_bufs, ws
     torch.cuda.empty_cache()
     if not args.no_batched:
@@ -225,6 +236,59 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(args, c, torch, np)
         del c
     print(json.dumps(rec), flush=True)
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_score_decode_1m_hbm_traffic.md")
+SCORE_SOURCES = ("long_context_sparse_select_amd/csrc/score.hip", "long_context_sparse_select_amd/csrc/common.h")
+
+
+def counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev):
+    """Eager launches for rocprofv3 --pmc: msa_score (one k_score_decode dispatch each) over the
+    rotating caches, then a device copy of COPY_BYTES (its FETCH_SIZE / WRITE_SIZE per dispatch
+    calibrate the counters against a known byte count)."""
+    L, R = len(caches), len(q_ring)
+    n = max(8, args.steps // 10)
+    for i in range(2 * L):
+        msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
+    for i in range(n):
+        msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L, "copy_launches": 4,
+                      "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(algorithmic_bytes):
+    """HBM bytes per k_score_decode launch from the committed rocprofv3 --pmc record, or None when
+    there is no record or the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            for line in f:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("sources_digest") != sources_digest(SCORE_SOURCES):
+                        return None
+                    return {"bytes_per_launch": rec["bytes_per_launch"],
+                            "vs_algorithmic": rec["bytes_per_launch"] / algorithmic_bytes,
+                            "fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+                            "record": os.path.relpath(TRAFFIC_RECORD, ROOT)}
+    except (OSError, ValueError, KeyError):
+        return None
+    return None
 
 
 def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
