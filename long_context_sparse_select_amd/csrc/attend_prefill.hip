@@ -7,17 +7,23 @@
 // tile's diagonal block is always attended, causally (key position <= query position).
 //
 // One workgroup per (tile, KV group): rows = 64 tokens x G heads (256 for G = 4), 2G waves of
-// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). For each selected block (64 keys):
+// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). The diagonal block is attended first,
+// then the selected blocks in list order (the online softmax does not depend on the order).
+// For each block (64 keys):
 //   * K (row-major, padded) and V (transposed, [dim][key], padded) are staged in LDS by the
-//     whole workgroup; the next block's K/V are already in flight into registers while the
-//     current one is computed;
+//     whole workgroup into one of two buffers while the other is read; the loads of the block
+//     after next are already in flight into registers; one barrier per block;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (2 key tiles x 8 k-steps). Each lane owns one
 //     query row (its C column), so the softmax row max needs one exchange with lane ^ 32;
 //   * keys are fed to the A operand in an order with bits 2 and 3 of the key index swapped,
 //     which makes the S^T accumulator registers of a lane, converted to bf16, exactly the
 //     P^T B operand of O^T = V^T P^T (8 consecutive keys per lane and k-step): no LDS round
 //     trip for P;
-//   * online softmax in the log2 domain, fp32 statistics, fp32 accumulation in the MFMA.
+//   * online softmax in the log2 domain, fp32 statistics, fp32 accumulation in the MFMA; the
+//     reference max moves only when a row's max outgrows it by 2^8, so the O rescale is rare;
+//     the causal mask is a branch taken on the diagonal block only.
+// The kernel is bound by LDS fragment reads (each 32-row wave reads the whole K and V^T block:
+// 1 KiB of LDS per 32 KFLOP of MFMA), not by HBM.
 #include "common.h"
 #include "kernels.h"
 
@@ -96,73 +102,21 @@ struct PrefillBlockLoader {
   }
 };
 
+// Online-softmax state of one wave (32 query rows; lane (n, c) holds row n's statistics).
+// The running max used for P moves only when a row's max grows by more than kLazy (log2 units):
+// P = exp2(s * scale - m) then stays <= 2^kLazy and the O/l rescale is skipped for most blocks.
+// The algebra is exact for any reference max; only rounding differs.
+constexpr float kLazy = 8.f;
+
 template <int G>
-__global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
-  __shared__ __align__(16) uint16_t sK[kP * kKPitch];
-  __shared__ __align__(16) uint16_t sV[kD * kVPitch];
-  const int tau = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int n = lane & 31, c = lane >> 5;
-  const int h = w >> 1;
-  const int il = (w & 1) * 32 + n;                 // token within the tile
-  const int i0 = tau * kP;
-  const int rows_valid = min(kP, a.T - i0);
-  const int diag = a.past_len / kP + tau;
-  const bool row_ok = il < rows_valid;
-  const int qhead = g * G + h;
+struct PrefillWave {
+  bf16x8 qf[8];       // Q^T fragments: lane (n, c) holds dims 16kk + 8c .. +7 of its query row
+  f32x16 o[4];        // O^T accumulators: dim tile dt, rows = the wave's 32 queries
+  float m, l;         // reference max (log2 domain) and running sum of this lane's 32 keys
+  int n, c, il;
+  float scale_log2;
 
-  // Q^T fragments: lane (n, c) holds dims 16kk + 8c .. +7 of its query row
-  bf16x8 qf[8];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((long long)(i0 + il) * a.Hq + qhead) * kD;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * c) : make_uint4(0u, 0u, 0u, 0u));
-  }
-
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const int32_t* ids = a.idx + ((long long)tau * a.Hkv + g) * (a.k + 1);
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.kpool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.vpool);
-  auto valid_page = [&](int e, int* page) -> bool {
-    const int j = ids[e];
-    if (j < 0 || j > diag) return false;
-    const int p = a.table[j];
-    *page = p;
-    return page_ok(p, a.num_pages);
-  };
-  auto next_valid = [&](int e, int* page) -> int {
-    while (e <= a.k && !valid_page(e, page)) ++e;
-    return e;
-  };
-
-  PrefillBlockLoader<G> ld;
-  int page = -1;
-  int e = next_valid(0, &page);
-  if (e <= a.k) {
-    const long long head = ((long long)page * a.Hkv + g) * kP * kD;
-    ld.load(kpool + head, vpool + head, tid);
-  }
-  while (e <= a.k) {
-    const int j = ids[e];
-    const bool is_diag = j == diag;
-    const int nvalid = is_diag ? rows_valid : kP;
-    __syncthreads();                               // the previous block's LDS reads are done
-    ld.store(sK, sV, tid, nvalid);
-    __syncthreads();
-    int page2 = -1;
-    const int e2 = next_valid(e + 1, &page2);
-    if (e2 <= a.k) {                               // next block in flight during this one
-      const long long head = ((long long)page2 * a.Hkv + g) * kP * kD;
-      ld.load(kpool + head, vpool + head, tid);
-    }
-
+  __device__ __forceinline__ void step(const uint16_t* sK, const uint16_t* sV, bool diag_block) {
     // ---- S^T = K Q^T: tile t holds keys swap23(32t + row)
     f32x16 s[2];
 #pragma unroll
@@ -176,8 +130,8 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[t], 0, 0, 0);
       }
     }
-    // ---- online softmax (log2 domain): max on raw scores, p = exp2(s * scale - m)
-    if (is_diag) {  // causal mask inside the diagonal block only
+    if (diag_block) {  // causal mask: key position within the block <= query position
+      __builtin_amdgcn_sched_barrier(0);   // keeps the mask a branch, not selects on every block
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -192,25 +146,30 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    const float mn = fmaxf(m, mx);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);        // m = -inf -> 0
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    // move the reference only when the row's max outgrows it by more than kLazy
+    const bool grow = mx > m + kLazy || (m == -INFINITY && mx != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform
+      const float mn = grow ? mx : m;
+      const float alpha = fast_exp2(m - mn);        // 1 for rows that keep m; m = -inf -> 0
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      m = mn;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[t][i], a.scale_log2, -mref));
+        const float p = fast_exp2(fmaf(s[t][i], scale_log2, -mref));
         s[t][i] = p;
         psum += p;
       }
-    l = l * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    l += psum;
     // ---- P^T operands straight from the accumulators: k-step ks uses registers 8(ks%2) .. +7
     bf16x8 pf[4];
 #pragma unroll
@@ -229,25 +188,110 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[ks], o[dt], 0, 0, 0);
       }
     }
-    e = e2;
+  }
+};
+
+constexpr int kKBuf = kP * kKPitch;    // bf16 elements of one staged K block
+constexpr int kVBuf = kD * kVPitch;    // bf16 elements of one staged V^T block
+
+template <int G>
+__global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
+  // two staging buffers: block i is read from buffer i%2 while block i+1 is written to the other,
+  // so one barrier per block separates the two
+  __shared__ __align__(16) uint16_t sK[2 * kKBuf];
+  __shared__ __align__(16) uint16_t sV[2 * kVBuf];
+  const int tau = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int h = w >> 1;
+  const int i0 = tau * kP;
+  const int rows_valid = min(kP, a.T - i0);
+  const int diag = a.past_len / kP + tau;
+  const int qhead = g * G + h;
+
+  PrefillWave<G> wv;
+  PrefillBlockLoader<G> ld;
+  wv.n = lane & 31;
+  wv.c = lane >> 5;
+  wv.il = (w & 1) * 32 + wv.n;                     // token within the tile
+  wv.scale_log2 = a.scale_log2;
+  const bool row_ok = wv.il < rows_valid;
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((long long)(i0 + wv.il) * a.Hq + qhead) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      wv.qf[kk] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * wv.c)
+                                   : make_uint4(0u, 0u, 0u, 0u));
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wv.o[dt][i] = 0.f;
+  wv.m = -INFINITY;
+  wv.l = 0.f;
+
+  const int32_t* ids = a.idx + ((long long)tau * a.Hkv + g) * (a.k + 1);
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.kpool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.vpool);
+  auto block_head = [&](int page) { return ((long long)page * a.Hkv + g) * kP * kD; };
+  // selected entries: indices below the diagonal with a valid page (the list also holds the
+  // diagonal itself and -1 padding, both skipped here)
+  auto next_valid = [&](int e, int* page) -> int {
+    for (; e <= a.k; ++e) {
+      const int j = ids[e];
+      if (j < 0 || j >= diag) continue;
+      const int p = a.table[j];
+      if (page_ok(p, a.num_pages)) { *page = p; return e; }
+    }
+    return e;
+  };
+
+  // Order: the diagonal block first (causal), then the selected blocks; the online softmax does
+  // not depend on the order. The loop stages block i+1 into one LDS buffer while block i is read
+  // from the other, with the loads of block i+2 in flight: one barrier per block.
+  const int pdiag = a.table[diag];
+  int pe = -1;
+  int e;                                           // list position of the staged block; -1 = diagonal
+  if (page_ok(pdiag, a.num_pages)) { e = -1; pe = pdiag; }
+  else e = next_valid(0, &pe);
+  if (e <= a.k) {
+    ld.load(kpool + block_head(pe), vpool + block_head(pe), tid);
+    ld.store(sK, sV, tid, e < 0 ? rows_valid : kP);
+    int pe2 = -1;
+    int e2 = next_valid(e + 1, &pe2);
+    if (e2 <= a.k) ld.load(kpool + block_head(pe2), vpool + block_head(pe2), tid);
+    __syncthreads();
+    int buf = 0;
+    bool diag_block = e < 0;
+    for (;;) {
+      wv.step(sK + buf * kKBuf, sV + buf * kVBuf, diag_block);
+      if (e2 > a.k) break;
+      ld.store(sK + (buf ^ 1) * kKBuf, sV + (buf ^ 1) * kVBuf, tid, kP);
+      int pe3 = -1;
+      const int e3 = next_valid(e2 + 1, &pe3);
+      if (e3 <= a.k) ld.load(kpool + block_head(pe3), vpool + block_head(pe3), tid);
+      e2 = e3;
+      buf ^= 1;
+      diag_block = false;
+      __syncthreads();                             // the staged block is complete; the old one is free
+    }
   }
 
   // ---- normalise and write: lane (n, c) holds dims 32dt + 8(i/4) + 4c + (i%4) of its row
-  const float ltot = l + __shfl_xor(l, 32);
+  const float ltot = wv.l + __shfl_xor(wv.l, 32);
   if (!row_ok) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((long long)(i0 + il) * a.Hq + qhead) * kD;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((long long)(i0 + wv.il) * a.Hq + qhead) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       uint2 pk;
-      pk.x = pack_bf16x2(o[dt][4 * i4 + 0] * inv, o[dt][4 * i4 + 1] * inv);
-      pk.y = pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * c) = pk;
+      pk.x = pack_bf16x2(wv.o[dt][4 * i4 + 0] * inv, wv.o[dt][4 * i4 + 1] * inv);
+      pk.y = pack_bf16x2(wv.o[dt][4 * i4 + 2] * inv, wv.o[dt][4 * i4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * wv.c) = pk;
     }
-  if (a.lse != nullptr && c == 0)
-    a.lse[(long long)(i0 + il) * a.Hq + qhead] = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
+  if (a.lse != nullptr && wv.c == 0)
+    a.lse[(long long)(i0 + wv.il) * a.Hq + qhead] = ltot > 0.f ? (wv.m + log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
