@@ -173,54 +173,75 @@ __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, i
   }
 }
 
-// Decode append for row (b, g): new K/V row at position N-1, the block's fresh summary, and its
-// fresh score for group g (returned, uniform). Thread -> (row r = tid/16 of the block, 8 dims).
+// Decode append for row (b, g): the new token's K/V row goes to position N-1 of its block, the
+// block's summary is recomputed from its older rows plus the new key, and the block is re-scored
+// with the group's index query. Split so that its loads overlap the selection: `issue` (loads,
+// and the K/V row store), `partial` (the wave's sum of the block's rows into LDS; query loads), `final`
+// (after a barrier: summary store and the per-wave product), `fresh` (after another barrier).
+// Thread -> (row r = tid/16 of the block, 8 dims).
 template <typename T>
-__device__ float decode_append(const TopkArgs& a, int row, int N, TopkShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = row / a.Hkv, g = row % a.Hkv;
-  const int G = a.Hq / a.Hkv;
-  const int t = N - 1, slot = t % kP;
-  const int page = a.table[(long long)b * a.max_blocks + t / kP];
-  const bool ok = page_ok(page, a.num_pages);                    // uniform
-  const int r = tid >> 4, d0 = (tid & 15) * 8;
-  const long long head = ((long long)(ok ? page : 0) * a.Hkv + g) * kP * kD;
-  const long long nrow = ((long long)b * a.Hkv + g) * kD;
+struct DecodeAppend {
   Vec8<T> old_k, new_k;
-  const T* knew = reinterpret_cast<const T*>(a.k_new) + nrow + d0;
-  new_k.load(knew);
-  // an older row of the block (a valid address either way: the new key when the page id is bad)
-  old_k.load(ok ? reinterpret_cast<const T*>(a.kpool) + head + (long long)min(r, max(slot - 1, 0)) * kD + d0 : knew);
-  if (ok && r == slot) {   // the new token's row: K and V of this group
-    Vec8<T> new_v;
-    new_v.load(reinterpret_cast<const T*>(a.v_new) + nrow + d0);
-    new_k.store(reinterpret_cast<T*>(a.kpool) + head + (long long)slot * kD + d0);
-    new_v.store(reinterpret_cast<T*>(a.vpool) + head + (long long)slot * kD + d0);
-  }
   float qv[kMaxGroup];
-  const T* qb = reinterpret_cast<const T*>(a.q) + ((long long)b * a.Hq + g * G) * kD;
-  if (tid < kD) {
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      const T x = qb[(long long)min(h, G - 1) * kD + tid];
-      if constexpr (sizeof(T) == 2) qv[h] = __uint_as_float((uint32_t)x << 16);
-      else qv[h] = x;
+  int page, slot, g;
+  bool ok;
+
+  __device__ __forceinline__ void issue(const TopkArgs& a, int row, int N) {
+    const int tid = threadIdx.x;
+    const int b = row / a.Hkv;
+    g = row % a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int t = N - 1;
+    slot = t % kP;
+    page = a.table[(long long)b * a.max_blocks + t / kP];
+    ok = page_ok(page, a.num_pages);                              // uniform
+    const int r = tid >> 4, d0 = (tid & 15) * 8;
+    const long long head = ((long long)(ok ? page : 0) * a.Hkv + g) * kP * kD;
+    const long long nrow = ((long long)b * a.Hkv + g) * kD;
+    const T* knew = reinterpret_cast<const T*>(a.k_new) + nrow + d0;
+    new_k.load(knew);
+    // an older row of the block (a valid address either way: the new key when the page id is bad)
+    old_k.load(ok ? reinterpret_cast<const T*>(a.kpool) + head + (long long)min(r, max(slot - 1, 0)) * kD + d0 : knew);
+    if (ok && r == slot) {   // the new token's row: K and V of this group
+      Vec8<T> new_v;
+      new_v.load(reinterpret_cast<const T*>(a.v_new) + nrow + d0);
+      new_k.store(reinterpret_cast<T*>(a.kpool) + head + (long long)slot * kD + d0);
+      new_v.store(reinterpret_cast<T*>(a.vpool) + head + (long long)slot * kD + d0);
     }
   }
-  if (!ok) return -INFINITY;                                     // never read, never written
-  float fo[8], fn[8], f[8];
-  old_k.to_f32(fo);
-  new_k.to_f32(fn);
+
+  // also requests the group's query heads (used by `final`, after the next barrier)
+  __device__ __forceinline__ void partial(const TopkArgs& a, int row, TopkShared& sh) {
+    if (!ok) return;                                             // uniform
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < kD) {
+      const int G = a.Hq / a.Hkv;
+      const T* qb = reinterpret_cast<const T*>(a.q) + ((long long)(row / a.Hkv) * a.Hq + g * G) * kD;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = r < slot ? fo[e] : (r == slot ? fn[e] : 0.f);
+      for (int h = 0; h < kMaxGroup; ++h) {
+        const T x = qb[(long long)min(h, G - 1) * kD + tid];
+        if constexpr (sizeof(T) == 2) qv[h] = __uint_as_float((uint32_t)x << 16);
+        else qv[h] = x;
+      }
+    }
+    const int r = tid >> 4, d0 = (tid & 15) * 8;
+    float fo[8], fn[8], f[8];
+    old_k.to_f32(fo);
+    new_k.to_f32(fn);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = across_rows_sum(f[e]);    // the wave's 4 rows
-  if (lane < 16) {
+    for (int e = 0; e < 8; ++e) f[e] = r < slot ? fo[e] : (r == slot ? fn[e] : 0.f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sh.rows[wave][d0 + e] = f[e];
+    for (int e = 0; e < 8; ++e) f[e] = across_rows_sum(f[e]);    // the wave's 4 rows
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh.rows[wave][d0 + e] = f[e];
+    }
   }
-  __syncthreads();
-  if (tid < kD) {
+
+  __device__ __forceinline__ void final(const TopkArgs& a, TopkShared& sh) const {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (!ok || tid >= kD) return;
+    const int G = a.Hq / a.Hkv;
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) acc += sh.rows[w][tid];
@@ -233,9 +254,11 @@ __device__ float decode_append(const TopkArgs& a, int row, int N, TopkShared& sh
     const float prod = wave_sum_f32((qi / (float)G) * summary);
     if (lane == 0) sh.fsum[wave] = prod;
   }
-  __syncthreads();
-  return sh.fsum[0] + sh.fsum[1];
-}
+
+  __device__ __forceinline__ float fresh(const TopkShared& sh) const {
+    return ok ? sh.fsum[0] + sh.fsum[1] : -INFINITY;             // never read, never written
+  }
+};
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
@@ -264,127 +287,141 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
       for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + kThreads * i, n - 1)];
     }
   }
-  int jlast = -1;
-  float fresh = 0.f;
-  if (!prefill && a.k_new != nullptr && N > 0) {                 // uniform
-    fresh = decode_append<T>(a, row, N, sh);
-    jlast = n - 1;
-    if (tid == 0) srow[jlast] = fresh;
-  }
+  const bool do_append = !prefill && a.k_new != nullptr && N > 0;   // uniform
+  const int jlast = do_append ? n - 1 : -1;
+  DecodeAppend<T> ap;
+  if (do_append) ap.issue(a, row, N);
 
-  if (keff == n) {  // every candidate is kept
-    for (int i = tid; i < n; i += kThreads) emit(a, row, i, i);
+  const int ngroups = min(n, kThreads);     // threads holding at least one candidate
+  const bool fast = n <= kMaxFast && keff < n && keff <= ngroups;   // uniform
+  if (!fast) {
+    // every candidate kept, or the exact path: finish the append first
+    float fresh = 0.f;
+    if (do_append) {
+      ap.partial(a, row, sh);
+      __syncthreads();
+      ap.final(a, sh);
+      __syncthreads();
+      fresh = ap.fresh(sh);
+      if (tid == 0) srow[jlast] = fresh;
+    }
+    if (keff == n) {
+      for (int i = tid; i < n; i += kThreads) emit(a, row, i, i);
+    } else {
+      select_fallback(a, srow, row, n, keff, jlast, fresh, sh);
+    }
     pad(a, row, keff, n, prefill);
     return;
   }
 
+  // ---- fast path. The appended block's stale score is left out of the bound (key 0 sorts below
+  // every real key) and re-enters as a survivor once its fresh score is known: T0 stays a valid
+  // lower bound of the k_eff-th largest key.
+  uint32_t key[kPer];
+  uint32_t cm = 0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = tid + kThreads * i;
+    key[i] = (j < n && j != jlast) ? order_key(v[i]) : 0u;
+    cm = max(cm, key[i]);
+  }
+  const bool has = tid < ngroups;
+  if (tid == 0) sh.cnt = 0;
+  // ---- 1. range of the group maxima
+  const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
+  if (lane == 0) { sh.red[wave] = wmx; sh.red[kWaves + wave] = wmn; }
+  if (tid < kBins) sh.hist[tid] = 0u;
+  if (tid == 0) sh.bstar = 0;   // bin 0 keeps every group maximum: always a valid bound
+  __syncthreads();
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kWaves + w]); }
+  const unsigned long long span = (unsigned long long)(mx - mn) + 1ull;
+  uint32_t bin = 0u;
+  if (has) {
+    bin = (uint32_t)(((unsigned long long)(cm - mn) * kBins) / span);
+    atomicAdd(&sh.hist[bin], 1u);
+  }
+  if (do_append) ap.partial(a, row, sh);
+  __syncthreads();
+  // ---- bin holding the k_eff-th largest group maximum (wave 0: lane owns bins 4l..4l+3)
+  if (wave == 0) {
+    const uint4 c4 = reinterpret_cast<const uint4*>(sh.hist)[lane];
+    const uint32_t local = c4.x + c4.y + c4.z + c4.w;
+    uint32_t incl = local;  // suffix sum over lanes >= lane
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
+      if (lane + off < 64) incl += y;
+    }
+    uint32_t run = incl - local;
+    const uint32_t cc[4] = {c4.x, c4.y, c4.z, c4.w};
+    for (int i = 3; i >= 0; --i) {
+      if (run < (uint32_t)keff && run + cc[i] >= (uint32_t)keff) sh.bstar = 4 * lane + i;
+      run += cc[i];
+    }
+  }
+  if (do_append) ap.final(a, sh);
+  __syncthreads();
+  // ---- T0 = smallest group maximum in bins >= bstar
+  const uint32_t t0 = wave_min_u32((has && bin >= (uint32_t)sh.bstar) ? cm : 0xffffffffu);
+  if (lane == 0) sh.red[wave] = t0;
+  float fresh = 0.f;
+  if (do_append) {
+    fresh = ap.fresh(sh);
+    if (jlast % kThreads == tid) key[jlast / kThreads] = order_key(fresh);
+  }
+  __syncthreads();
+  if (do_append && tid == 0) srow[jlast] = fresh;
+  uint32_t T0 = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) T0 = min(T0, sh.red[w]);
+  // ---- 2. survivors (keys >= T0) as (key, ~index) composites (+ page id)
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = tid + kThreads * i;
+    if (j < n && key[i] >= T0) {
+      const int p = atomicAdd(&sh.cnt, 1);
+      if (p < kCap) {
+        sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
+        if (trow != nullptr) sh.spage[p] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
+      }
+    }
+  }
+  __syncthreads();
+  const int m = sh.cnt;
   bool done = false;
-  if (n <= kMaxFast) {
-    uint32_t key[kPer];
-    uint32_t cm = 0u;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int j = tid + kThreads * i;
-      key[i] = j < n ? order_key(j == jlast ? fresh : v[i]) : 0u;
-      cm = max(cm, key[i]);
-    }
-    const int ngroups = min(n, kThreads);     // threads holding at least one candidate
-    const bool has = tid < ngroups;
-    uint32_t T0 = 0u;
-    if (tid == 0) sh.cnt = 0;
-    if (keff <= ngroups) {
-      // ---- 1. range of the group maxima
-      const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
-      if (lane == 0) { sh.red[wave] = wmx; sh.red[kWaves + wave] = wmn; }
-      if (tid < kBins) sh.hist[tid] = 0u;
-      if (tid == 0) sh.bstar = 0;   // bin 0 keeps every group maximum: always a valid bound
-      __syncthreads();
-      uint32_t mx = 0u, mn = 0xffffffffu;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kWaves + w]); }
-      const unsigned long long span = (unsigned long long)(mx - mn) + 1ull;
-      uint32_t bin = 0u;
-      if (has) {
-        bin = (uint32_t)(((unsigned long long)(cm - mn) * kBins) / span);
-        atomicAdd(&sh.hist[bin], 1u);
+  if (m >= keff && m <= kCap) {   // uniform; m >= k_eff holds by construction of T0
+    const int npair = (m + 1) >> 1;
+    const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
+    for (int e = tid; e < m; e += kThreads) {
+      const unsigned long long ce = sh.comp[e];
+      const int je = (int)~(uint32_t)ce;
+      const int pge = trow != nullptr ? sh.spage[e] : -1;
+      int rank = 0;
+#pragma unroll 4
+      for (int f = 0; f < npair; ++f) {
+        const ulonglong2 c2 = cp[f];
+        rank += (c2.x > ce) + (2 * f + 1 < m && c2.y > ce);   // comp[m] is not a survivor
       }
-      __syncthreads();
-      // ---- bin holding the k_eff-th largest group maximum (wave 0: lane owns bins 4l..4l+3)
-      if (wave == 0) {
-        const uint4 c4 = reinterpret_cast<const uint4*>(sh.hist)[lane];
-        const uint32_t local = c4.x + c4.y + c4.z + c4.w;
-        uint32_t incl = local;  // suffix sum over lanes >= lane
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
-          if (lane + off < 64) incl += y;
-        }
-        uint32_t run = incl - local;
-        const uint32_t cc[4] = {c4.x, c4.y, c4.z, c4.w};
-        for (int i = 3; i >= 0; --i) {
-          if (run < (uint32_t)keff && run + cc[i] >= (uint32_t)keff) sh.bstar = 4 * lane + i;
-          run += cc[i];
-        }
-      }
-      __syncthreads();
-      // ---- T0 = smallest group maximum in bins >= bstar
-      const uint32_t t0 = wave_min_u32((has && bin >= (uint32_t)sh.bstar) ? cm : 0xffffffffu);
-      if (lane == 0) sh.red[wave] = t0;
-      __syncthreads();
-      T0 = 0xffffffffu;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) T0 = min(T0, sh.red[w]);
-    } else {
-      __syncthreads();
+      if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pge; }
     }
-    // ---- 2. survivors, as (key, ~index) composites (+ page id)
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int j = tid + kThreads * i;
-      if (j < n && key[i] >= T0) {
-        const int p = atomicAdd(&sh.cnt, 1);
-        if (p < kCap) {
-          sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
-          if (trow != nullptr) sh.spage[p] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
-        }
-      }
-    }
+    if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
     __syncthreads();
-    const int m = sh.cnt;
-    if (m >= keff && m <= kCap) {   // uniform; m >= k_eff holds by construction of T0
-      if (tid < 2) sh.comp[m + tid] = 0ull;   // pad: never counts as better
-      __syncthreads();
-      const int npair = (m + 1) >> 1;
-      const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
-      for (int e = tid; e < m; e += kThreads) {
-        const unsigned long long ce = sh.comp[e];
-        const int je = (int)~(uint32_t)ce;
-        const int pge = trow != nullptr ? sh.spage[e] : -1;
-        int rank = 0;
+    // ---- 3. ascending block order
+    const int nq = (keff + 3) >> 2;
+    const int4* sp = reinterpret_cast<const int4*>(sh.sel);
+    for (int e = tid; e < keff; e += kThreads) {
+      const int vj = sh.sel[e];
+      int pos = 0;
 #pragma unroll 4
-        for (int f = 0; f < npair; ++f) {
-          const ulonglong2 c2 = cp[f];
-          rank += (c2.x > ce) + (c2.y > ce);
-        }
-        if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pge; }
+      for (int f = 0; f < nq; ++f) {
+        const int4 q4 = sp[f];
+        pos += (q4.x < vj) + (q4.y < vj) + (q4.z < vj) + (q4.w < vj);
       }
-      if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
-      __syncthreads();
-      // ---- 3. ascending block order
-      const int nq = (keff + 3) >> 2;
-      const int4* sp = reinterpret_cast<const int4*>(sh.sel);
-      for (int e = tid; e < keff; e += kThreads) {
-        const int vj = sh.sel[e];
-        int pos = 0;
-#pragma unroll 4
-        for (int f = 0; f < nq; ++f) {
-          const int4 q4 = sp[f];
-          pos += (q4.x < vj) + (q4.y < vj) + (q4.z < vj) + (q4.w < vj);
-        }
-        a.idx[(long long)row * a.idx_stride + pos] = vj;
-        if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = sh.selpg[e];
-      }
-      done = true;
+      a.idx[(long long)row * a.idx_stride + pos] = vj;
+      if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = sh.selpg[e];
     }
+    done = true;
   }
   if (!done) select_fallback(a, srow, row, n, keff, jlast, fresh, sh);
   pad(a, row, keff, n, prefill);
