@@ -7,11 +7,11 @@
 // (prefill); a block's score is <index query, block summary>, unscaled, in fp32.
 //
 // Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 per sequence), so the
-// kernel is shaped for HBM: a workgroup owns a chunk of 8 logical blocks of one sequence,
-// stages the chunk's page ids and the Hkv index queries in LDS, and then walks (block, group)
-// pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 the workgroup reads the
-// chunk's 8 pages as 8 contiguous 4 KiB runs, whatever the page permutation, and each lane
-// has all of its loads in flight before any arithmetic. The chunk's scores are staged in LDS
+// kernel is shaped for HBM: a workgroup owns a chunk of 8 logical blocks of one sequence and
+// walks (block, group) pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 the
+// workgroup reads the chunk's 8 pages as 8 contiguous 4 KiB runs, whatever the page
+// permutation. Each lane reads its pairs' page ids from the table and issues all of its
+// summary loads first; the Hkv index queries are built in LDS while those loads are in flight. The chunk's scores are staged in LDS
 // and leave as one contiguous run per row. The number of KV heads is a template parameter for
 // the power-of-two cases, so the pair-index arithmetic is shifts, not divisions.
 #include "common.h"
@@ -51,63 +51,91 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
                                                       float* __restrict__ scores, int row_stride) {
   const int Hkv = HKV > 0 ? HKV : hkv_arg;
   extern __shared__ float s_qidx[];             // [Hkv][128] index queries, then [Hkv][kChunk] scores
-  __shared__ int s_page[kChunk];
   const int b = blockIdx.y;
   const int j0 = blockIdx.x * kChunk;
   const int tid = threadIdx.x;
-  const int N = clamp_len(lens[b], max_len);
-  const int nb = (N + kP - 1) / kP;
   const int jend = min(j0 + kChunk, row_stride);
+  const int slot = tid >> 5;    // 8 pair slots per pass
+  const int l32 = tid & 31;     // 4 dims per lane
+  const int npairs = (jend - j0) * Hkv;
+  const int32_t* trow = table + (long long)b * max_blocks;
+  if (num_pages <= 0) {   // an empty pool: every block of the chunk scores -inf (uniform exit)
+    for (int e = tid; e < Hkv * kChunk; e += 256) {
+      const int g = e / kChunk, jl = e % kChunk;
+      if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
+    }
+    return;
+  }
 
-  // the page ids, the sequence length and the queries are loaded in one round trip: the table
-  // read does not wait for the length (j < row_stride <= max_blocks keeps it in bounds)
-  const int my_page = table[(long long)b * max_blocks + min(j0 + (tid & (kChunk - 1)), row_stride - 1)];
-  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads.
-    // Thread -> (group, 8 dims): its G head rows are loaded as 16 B vectors, all in flight at once.
+  // Pass loads: each lane reads the page ids of its own pairs straight from the table (the
+  // workgroup's 8 entries share one cache line), then issues every summary load of the pass.
+  // Nothing else is on the path from the kernel's start to the summary stream.
+  float4 sv[kUnroll];
+  bool live[kUnroll];
+  auto issue = [&](int p0) {
+    int tp[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) tp[u] = trow[min(j0 + (p0 + u * 8 + slot) / Hkv, row_stride - 1)];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {   // branch-free: every load is issued unconditionally
+      const int p = p0 + u * 8 + slot;
+      live[u] = (p < npairs) & (tp[u] >= 0) & (tp[u] < num_pages);   // the length is applied later
+      const int page = live[u] ? tp[u] : 0;   // page 0: a valid address, result unused
+      sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + p % Hkv) * kD + l32 * 4);
+    }
+  };
+  issue(0);
+  const int nb = (clamp_len(lens[b], max_len) + kP - 1) / kP;
+  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads, computed while
+     // the summaries stream in. Thread -> (group, 8 dims): its G head rows are 16 B vector loads.
     const int G = Hq / Hkv;
     const TQ* qb = q + (long long)b * Hq * kD;
     for (int c0 = 0; c0 < Hkv * (kD / 8); c0 += 256) {
       const int cc = min(c0 + tid, Hkv * (kD / 8) - 1);
       const int g = cc / (kD / 8), d8 = (cc % (kD / 8)) * 8;
-      float v[kMaxGroup][8];
+      float acc[8];
+      if constexpr (sizeof(TQ) == 2) {   // heads kept as packed bf16 while in flight
+        uint4 w[kMaxGroup];
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) load8(qb + (long long)(g * G + min(h, G - 1)) * kD + d8, v[h]);
-      if (c0 + tid < Hkv * (kD / 8)) {
+        for (int h = 0; h < kMaxGroup; ++h)
+          w[h] = *reinterpret_cast<const uint4*>(qb + (long long)(g * G + min(h, G - 1)) * kD + d8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h < G) {
+            acc[0] += bf16lo(w[h].x); acc[1] += bf16hi(w[h].x); acc[2] += bf16lo(w[h].y); acc[3] += bf16hi(w[h].y);
+            acc[4] += bf16lo(w[h].z); acc[5] += bf16hi(w[h].z); acc[6] += bf16lo(w[h].w); acc[7] += bf16hi(w[h].w);
+          }
+        }
+      } else {
+        float v[kMaxGroup][8];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) load8(qb + (long long)(g * G + min(h, G - 1)) * kD + d8, v[h]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float acc = 0.f;
+          acc[e] = 0.f;
 #pragma unroll
           for (int h = 0; h < kMaxGroup; ++h)
-            if (h < G) acc += v[h][e];
-          s_qidx[g * kD + d8 + e] = acc / (float)G;
+            if (h < G) acc[e] += v[h][e];
         }
+      }
+      if (c0 + tid < Hkv * (kD / 8)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_qidx[g * kD + d8 + e] = acc[e] / (float)G;
       }
     }
   }
-  if (tid < kChunk) s_page[tid] = (j0 + tid < nb && page_ok(my_page, num_pages)) ? my_page : -1;
   __syncthreads();
 
-  const int slot = tid >> 5;    // 8 pair slots per pass
-  const int l32 = tid & 31;     // 4 dims per lane
-  const int npairs = (jend - j0) * Hkv;
-  const bool any_page = num_pages > 0;
   float* s_sc = s_qidx + Hkv * kD;
   for (int p0 = 0; p0 < npairs; p0 += 8 * kUnroll) {
-    float4 sv[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {   // every load issued before any is used
-      const int p = p0 + u * 8 + slot;
-      const int pg = s_page[min(p / Hkv, kChunk - 1)];
-      const int page = (p < npairs && pg >= 0) ? pg : 0;   // page 0: a valid address, result unused
-      sv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (any_page) sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + p % Hkv) * kD + l32 * 4);
-    }
+    if (p0 > 0) issue(p0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int p = p0 + u * 8 + slot;
       if (p >= npairs) continue;   // uniform across the 32-lane slot
       const int jl = p / Hkv, g = p % Hkv;
-      const int j = j0 + jl;
       const float4 qv = *reinterpret_cast<const float4*>(s_qidx + g * kD + l32 * 4);
       float part = qv.x * sv[u].x;
       part = fmaf(qv.y, sv[u].y, part);
@@ -115,7 +143,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       part = fmaf(qv.w, sv[u].w, part);
       part = row16_sum(part);
       part += __shfl_xor(part, 16);
-      if (l32 == 0) s_sc[g * kChunk + jl] = (j < nb && s_page[jl] >= 0) ? part : -INFINITY;
+      if (l32 == 0) s_sc[g * kChunk + jl] = (live[u] && j0 + jl < nb) ? part : -INFINITY;
     }
   }
   __syncthreads();
