@@ -7,13 +7,14 @@
 // (prefill); a block's score is <index query, block summary>, unscaled, in fp32.
 //
 // Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 per sequence), so the
-// kernel is shaped for HBM: a workgroup owns a chunk of 8 logical blocks of one sequence and
-// walks (block, group) pairs with 32 lanes per pair and 16 B per lane -- for Hkv = 8 the
-// workgroup reads the chunk's 8 pages as 8 contiguous 4 KiB runs, whatever the page
+// kernel is shaped for HBM: a workgroup owns a chunk of 16 logical blocks of one sequence and
+// walks (block, group) pairs with 32 lanes per pair and 16 B per lane, in passes of 8 blocks --
+// for Hkv = 8 it reads the chunk's 16 pages as 16 contiguous 4 KiB runs, whatever the page
 // permutation. Each lane reads its pairs' page ids from the table and issues all of its
-// summary loads first; the Hkv index queries are built in LDS while those loads are in flight. The chunk's scores are staged in LDS
-// and leave as one contiguous run per row. The number of KV heads is a template parameter for
-// the power-of-two cases, so the pair-index arithmetic is shifts, not divisions.
+// summary loads of a pass first; the Hkv index queries are built in LDS while the first pass
+// is in flight. The chunk's scores are staged in LDS and leave as one contiguous run per row.
+// The number of KV heads is a template parameter for the power-of-two cases, so the pair-index
+// arithmetic is shifts, not divisions.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,7 +22,7 @@ namespace msa {
 
 namespace {
 
-constexpr int kChunk = 8;     // logical blocks per workgroup (decode)
+constexpr int kChunk = 16;    // logical blocks per workgroup (decode)
 constexpr int kUnroll = 8;    // pairs in flight per 32-lane slot
 
 // 8 consecutive elements as floats, in 16 B vector loads
