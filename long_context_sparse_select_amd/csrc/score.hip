@@ -188,88 +188,77 @@ __global__ void __launch_bounds__(512) k_tile_query(const TQ* __restrict__ q, in
   }
 }
 
-// prefill scores: a 64-tile x 64-block fp32 product per workgroup, from LDS; tile tau scores
-// the blocks j < past_blocks + tau (its causal candidates), -inf elsewhere in the row.
-// LDS holds both operands transposed ([d][tile], [d][block]) so that the inner loop's reads are
-// broadcast or consecutive, with no bank conflicts.
-constexpr int kPT = 64;   // tiles per workgroup
-constexpr int kPB = 64;   // blocks per workgroup
+// prefill scores: a 64-tile x 64-block fp32 product per workgroup on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 accumulation); tile tau scores the blocks
+// j < past_blocks + tau (its causal candidates), -inf elsewhere in the row.
+// Staging: the 64 tile queries and the 64 block summaries (512 B rows) are read coalesced, 32
+// lanes per row, all 16 loads of a thread in flight at once, and stored to LDS rows padded to
+// 132 floats. Wave w then computes the 32 x 32 output tile (tiles 32*(w/2) .., blocks
+// 32*(w%2) ..): MFMA step s contracts dims s and 64 + s, so lane (i = l%32, h = l/32) reads
+// dims 64h .. 64h+63 of one tile row (A) and one block row (B) as 16 B LDS reads (row pitch
+// 132 floats: the 16 rows a read touches fall on distinct banks).
+constexpr int kPT = 64;     // tiles per workgroup
+constexpr int kPB = 64;     // blocks per workgroup
+constexpr int kRowP = 132;  // LDS row pitch (floats)
+typedef float f32x16s __attribute__((ext_vector_type(16)));
 
 __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__ qtile, const float* __restrict__ S,
                                                        const int32_t* __restrict__ table, int num_pages,
                                                        int past_blocks, int ntiles, int Hkv,
                                                        float* __restrict__ scores, int row_stride) {
-  __shared__ float s_q[kD][kPT];
-  __shared__ float s_s[kD][kPB];
-  const int j0 = blockIdx.x * kPB, g = blockIdx.y, t0 = blockIdx.z * kPT;
-  const int tid = threadIdx.x;
-  const int ncand_max = past_blocks + ntiles - 1;   // candidates of the last tile
+  __shared__ __align__(16) float s_a[kPT * kRowP];
+  __shared__ __align__(16) float s_b[kPB * kRowP];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int g = blockIdx.y;
+  const int tz = blockIdx.z * kPT, jz = blockIdx.x * kPB;
+  const int ncand_max = past_blocks + ntiles - 1;      // candidates of the last tile
   {
-    // staging: all 16 float4 loads of a thread in flight at once, from clamped addresses
-    constexpr int kIt = kPT * (kD / 4) / 256;   // 8 (same for the block operand)
-    float4 qv[kIt], sv[kIt];
-    int pg[kIt];
+    // thread -> rows (tid/32) + 8*it, float4 column tid%32; table entries first, then the rows
+    const int c4 = tid & 31;
+    int pg[8];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = tid + 256 * it;
-      const int t = e % kPT, jl = e % kPB;
-      const int j = min(j0 + jl, max(ncand_max - 1, 0));
-      pg[it] = table[j];
-      qv[it] = *reinterpret_cast<const float4*>(qtile + ((long long)min(t0 + t, ntiles - 1) * Hkv + g) * kD + (e / kPT) * 4);
+    for (int it = 0; it < 8; ++it) pg[it] = table[min(jz + (tid >> 5) + 8 * it, max(ncand_max - 1, 0))];
+    float4 av[8], bv[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (tid >> 5) + 8 * it;
+      av[it] = reinterpret_cast<const float4*>(qtile + ((long long)min(tz + r, ntiles - 1) * Hkv + g) * kD)[c4];
+      const int page = page_ok(pg[it], num_pages) ? pg[it] : 0;   // page 0: a valid address
+      bv[it] = reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD)[c4];
     }
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int page = page_ok(pg[it], num_pages) ? pg[it] : -1;
-      sv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (page >= 0) sv[it] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD + ((tid + 256 * it) / kPB) * 4);
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = tid + 256 * it;
-      const int t = e % kPT, c = e / kPT, jl = e % kPB;
-      const float4 a = t0 + t < ntiles ? qv[it] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 b = j0 + jl < ncand_max ? sv[it] : make_float4(0.f, 0.f, 0.f, 0.f);
-      s_q[c * 4 + 0][t] = a.x; s_q[c * 4 + 1][t] = a.y; s_q[c * 4 + 2][t] = a.z; s_q[c * 4 + 3][t] = a.w;
-      s_s[c * 4 + 0][jl] = b.x; s_s[c * 4 + 1][jl] = b.y; s_s[c * 4 + 2][jl] = b.z; s_s[c * 4 + 3][jl] = b.w;
+    for (int it = 0; it < 8; ++it) {
+      const int r = (tid >> 5) + 8 * it;
+      *reinterpret_cast<float4*>(s_a + r * kRowP + 4 * c4) = av[it];
+      *reinterpret_cast<float4*>(s_b + r * kRowP + 4 * c4) = bv[it];
     }
   }
   __syncthreads();
-  // thread owns tiles ty*4 .. +3 and blocks tx + 16*c, c = 0..3
-  const int ty = tid >> 4, tx = tid & 15;
-  float acc[4][4];
+  const int i = lane & 31, h = lane >> 5;
+  const int ta = 32 * (w >> 1), jb = 32 * (w & 1);
+  const float* arow = s_a + (ta + i) * kRowP + 64 * h;
+  const float* brow = s_b + (jb + i) * kRowP + 64 * h;
+  f32x16s acc;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
-  for (int d = 0; d < kD; ++d) {
-    float qa[4], sb[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) qa[a] = s_q[d][ty * 4 + a];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sb[c] = s_s[d][tx + 16 * c];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(qa[a], sb[c], acc[a][c]);
+  for (int e = 0; e < 16; ++e) {
+    const float4 a4 = *reinterpret_cast<const float4*>(arow + 4 * e);
+    const float4 b4 = *reinterpret_cast<const float4*>(brow + 4 * e);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, b4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, b4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, b4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, b4.w, acc, 0, 0, 0);
   }
-  bool ok[4];
+  // lane l holds block jz + jb + l%32 of tiles tz + ta + 8*(r/4) + 4*(l/32) + r%4
+  const int j = jz + jb + i;
+  if (j >= row_stride) return;
+  const bool ok = j < ncand_max && page_ok(table[min(j, max(ncand_max - 1, 0))], num_pages);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int j = j0 + tx + 16 * c;
-    ok[c] = j < ncand_max && page_ok(table[j], num_pages);
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int tau = t0 + ty * 4 + a;
+  for (int r = 0; r < 16; ++r) {
+    const int tau = tz + ta + 8 * (r >> 2) + 4 * h + (r & 3);
     if (tau >= ntiles) continue;
-    const long long row = (long long)tau * Hkv + g;
-    const int ncand = past_blocks + tau;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tx + 16 * c;
-      if (j >= row_stride) continue;
-      scores[row * row_stride + j] = (j < ncand && ok[c]) ? acc[a][c] : -INFINITY;
-    }
+    scores[((long long)tau * Hkv + g) * row_stride + j] = (ok && j < past_blocks + tau) ? acc[r] : -INFINITY;
   }
 }
 
