@@ -90,6 +90,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the batch-32 mixed-length decode line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
@@ -222,6 +223,10 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_batched:
         rec["batched_attend"] = bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev)
+        torch.cuda.empty_cache()
+    if not args.no_mixed:
+        rec["mixed_batch"] = bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev)
+        torch.cuda.empty_cache()
 
     # ---- prefill
     if not args.no_prefill:
@@ -357,6 +362,55 @@ def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload,
     log("batch-8 attend: %.2f us, %.0f GB/s of selected KV" % (t * 1e6, kv / t / 1e9))
     return {"workload": "decode_bf16_b8_128k", "attend_us": t * 1e6, "kv_GBps": kv / t / 1e9,
             "kv_hbm_frac": kv / t / 1e9 / HBM_PEAK_GBPS, "bytes_per_launch": kv}
+
+
+def bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev):
+    """Batch-32 decode over log-uniform lengths (4096 .. 1,048,576, about 8M tokens in one
+    shuffled page pool, k = min(64, blocks)): whole decode steps, and the scoring and attend
+    stages alone. One cache (32 GiB of K/V): far beyond the infinity cache without rotation."""
+    kw = workload("decode_bf16_mixed_b32", seed=args.seed)
+    c = make_decode_case_torch(device=dev, **kw)
+    table = torch.from_numpy(c.block_table).to(dev)
+    lens = torch.from_numpy(c.seq_lens).to(dev)
+    S = torch.empty((c.num_pages, c.Hkv, c.D), dtype=torch.float32, device=dev)
+    cache = msa.KVCache(c.k_pool, c.v_pool, S, table, lens)
+    cfg = msa.make_config(c.Hq, c.Hkv, c.top_k, dtype="bf16", softmax_scale=c.scale)
+    msa.msa_build_summaries(cfg, cache, c.B, c.max_seq_len)
+    B, R = c.B, 8
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 91)
+    q_ring = [torch.randn((B, c.Hq, c.D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    kn_ring = [torch.randn((B, c.Hkv, c.D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    vn_ring = [torch.randn((B, c.Hkv, c.D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    out = torch.empty((B, c.Hq, c.D), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((B, c.Hkv, c.top_k), dtype=torch.int32, device=dev)
+    mb = (c.max_seq_len + 63) // 64
+    sc = torch.empty((B, c.Hkv, mb), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, c.max_seq_len), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def timed(fn, n=10):
+        g = timed_graph(fn, R, torch)
+        run_graph(g, 2, torch)
+        return run_graph(g, n, torch) / (R * n)
+    t_step = timed(lambda i: msa.msa_decode_step(cfg, q_ring[i], cache, B, c.max_seq_len, out, k_new=kn_ring[i],
+                                                 v_new=vn_ring[i], idx_out=idx, workspace=ws))
+    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i], cache, B, c.max_seq_len, sc))
+    msa.msa_select(cfg, q_ring[0], cache, B, c.max_seq_len, idx, workspace=ws)
+    t_att = timed(lambda i: msa.msa_attend(cfg, q_ring[i], cache, B, c.max_seq_len, idx, out, workspace=ws))
+    torch.cuda.synchronize()
+    kv = float(selected_kv_bytes(idx, c.seq_lens))
+    nb_tot = sum((int(n) + 63) // 64 for n in c.seq_lens)
+    score_bytes = nb_tot * c.Hkv * c.D * 4 + nb_tot * 4 + nb_tot * c.Hkv * 4 + B * c.Hq * c.D * 2
+    log("mixed batch-32 (%d tokens): step %.1f us (%.0f tokens/s); score %.1f us (%.0f GB/s); attend %.1f us "
+        "(%.0f GB/s of selected KV)" % (int(np.sum(c.seq_lens)), t_step * 1e6, B / t_step, t_score * 1e6,
+                                         score_bytes / t_score / 1e9, t_att * 1e6, kv / t_att / 1e9))
+    return {"workload": "decode_bf16_mixed_b32", "batch": B, "total_tokens": int(np.sum(c.seq_lens)),
+            "step_us": t_step * 1e6, "tokens_per_s": B / t_step,
+            "score_us": t_score * 1e6, "score_GBps": score_bytes / t_score / 1e9,
+            "score_hbm_frac": score_bytes / t_score / 1e9 / HBM_PEAK_GBPS,
+            "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9, "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS,
+            "bytes_per_attend": kv, "bytes_per_score": score_bytes}
 
 
 def cpu_baseline(args, case, torch, np):

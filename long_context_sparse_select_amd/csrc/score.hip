@@ -73,10 +73,12 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   // Nothing else is on the path from the kernel's start to the summary stream.
   float4 sv[kUnroll];
   bool live[kUnroll];
-  auto issue = [&](int p0) {
-    int tp[kUnroll];
+  int tp[kUnroll];
+  auto table_loads = [&](int p0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) tp[u] = trow[min(j0 + (p0 + u * 8 + slot) / Hkv, row_stride - 1)];
+  };
+  auto summary_loads = [&](int p0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {   // branch-free: every load is issued unconditionally
       const int p = p0 + u * 8 + slot;
@@ -85,8 +87,16 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + p % Hkv) * kD + l32 * 4);
     }
   };
-  issue(0);
-  const int nb = (clamp_len(lens[b], max_len) + kP - 1) / kP;
+  table_loads(0);
+  const int nb = (clamp_len(lens[b], max_len) + kP - 1) / kP;   // in flight with the table loads
+  if (j0 >= nb) {   // a chunk past the sequence's end (batches of mixed lengths): -inf, no summary reads
+    for (int e = tid; e < Hkv * kChunk; e += 256) {
+      const int g = e / kChunk, jl = e % kChunk;
+      if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
+    }
+    return;
+  }
+  summary_loads(0);
   {  // [MGS §1 Step 1] one index query per group: mean of the group's heads, computed while
      // the summaries stream in. Thread -> (group, 8 dims): its G head rows are 16 B vector loads.
     const int G = Hq / Hkv;
@@ -131,7 +141,10 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
 
   float* s_sc = s_qidx + Hkv * kD;
   for (int p0 = 0; p0 < npairs; p0 += 8 * kUnroll) {
-    if (p0 > 0) issue(p0);
+    if (p0 > 0) {
+      table_loads(p0);
+      summary_loads(p0);
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int p = p0 + u * 8 + slot;
