@@ -34,6 +34,10 @@ SMALL = [
     # leave chunks with 1..3 attended blocks
     ("bf16_g2_wide", dict(B=6, Hq=16, Hkv=8, lens=[70000, 4096, 65, 1, 33333, 9000], top_k=64,
                           dtype="bf16", permute=True)),
+    # 160 (sequence, group) rows: sixteen blocks per workgroup (four chunks of four), ragged rows
+    ("bf16_g4_b20_many_rows", dict(B=20, Hq=32, Hkv=8, lens=[20000, 1, 4100, 64, 65, 127, 8191, 5000, 12345, 300,
+                                                             16384, 2, 999, 4096, 7777, 640, 641, 19999, 3000, 10],
+                                   top_k=64, dtype="bf16", permute=True)),
 ]
 
 
