@@ -34,10 +34,9 @@ namespace msa {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;          // the largest workgroup (rows up to 16384 candidates)
 constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 16;
-constexpr int kMaxFast = kThreads * kPer;
+constexpr int kPer = 16;                // candidates held per thread
 constexpr int kCap = 2048;
 constexpr int kBins = 256;
 constexpr int kMaxK = 4096;
@@ -77,7 +76,8 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 
-// block-wide integer sum (all threads get it); s_tmp holds kWaves ints
+// block-wide integer sum (all threads get it); s_tmp holds NT/64 ints
+template <int NT>
 __device__ int block_sum(int v, int* s_tmp) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -85,12 +85,13 @@ __device__ int block_sum(int v, int* s_tmp) {
   __syncthreads();
   int total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) total += s_tmp[w];
+  for (int w = 0; w < NT / 64; ++w) total += s_tmp[w];
   __syncthreads();
   return total;
 }
 
 // exclusive count of `pred` over threads in index order; *total gets the block's count
+template <int NT>
 __device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const unsigned long long m = __ballot(pred);
@@ -99,7 +100,7 @@ __device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int c = s_tmp[w];
     before += (w < wave) ? c : 0;
     tot += c;
@@ -135,14 +136,16 @@ __device__ __forceinline__ void emit(const TopkArgs& a, int row, int pos, int j)
   if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = page_of(a, row, j);
 }
 
+template <int NT>
 __device__ __forceinline__ void pad(const TopkArgs& a, int row, int keff, int n, bool prefill) {
-  for (int i = keff + threadIdx.x; i < a.idx_stride; i += kThreads) {
+  for (int i = keff + threadIdx.x; i < a.idx_stride; i += NT) {
     a.idx[(long long)row * a.idx_stride + i] = (prefill && i == keff) ? n : -1;
     if (a.pages != nullptr && i < a.k) a.pages[(long long)row * a.k + i] = -1;
   }
 }
 
 // exact selection straight from memory: T = k_eff-th largest key, then ordered compaction
+template <int NT>
 __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, int jlast,
                                 float fresh, TopkShared& sh) {
   const int tid = threadIdx.x;
@@ -151,22 +154,22 @@ __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, i
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
-    for (int j = tid; j < n; j += kThreads) c += key_of(j) >= cand;
-    if (block_sum(c, sh.tmp) >= keff) T = cand;
+    for (int j = tid; j < n; j += NT) c += key_of(j) >= cand;
+    if (block_sum<NT>(c, sh.tmp) >= keff) T = cand;
   }
   int gt = 0;
-  for (int j = tid; j < n; j += kThreads) gt += key_of(j) > T;
-  const int need_eq = keff - block_sum(gt, sh.tmp);
+  for (int j = tid; j < n; j += NT) gt += key_of(j) > T;
+  const int need_eq = keff - block_sum<NT>(gt, sh.tmp);
   int run_eq = 0, run_sel = 0;
-  for (int base = 0; base < n; base += kThreads) {
+  for (int base = 0; base < n; base += NT) {
     const int j = base + tid;
     const uint32_t key = j < n ? key_of(j) : 0u;
     const bool is_gt = j < n && key > T;
     const bool is_eq = j < n && key == T;
     int tot_eq, tot_sel;
-    const int eq_rank = run_eq + block_excl_count(is_eq, sh.tmp, &tot_eq);
+    const int eq_rank = run_eq + block_excl_count<NT>(is_eq, sh.tmp, &tot_eq);
     const bool sel = is_gt || (is_eq && eq_rank < need_eq);
-    const int pos = run_sel + block_excl_count(sel, sh.tmp, &tot_sel);
+    const int pos = run_sel + block_excl_count<NT>(sel, sh.tmp, &tot_sel);
     if (sel) emit(a, row, pos, j);
     run_eq += tot_eq;
     run_sel += tot_sel;
@@ -260,8 +263,11 @@ struct DecodeAppend {
   }
 };
 
-template <typename T>
-__global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
+// NT threads (512 or 1024); the fused decode append needs 1024 (one 16-lane row group per key row)
+template <typename T, int NT>
+__global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
+  constexpr int kW = NT / 64;
+  constexpr int kMaxFast = NT * kPer;
   __shared__ TopkShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -281,18 +287,18 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   const int32_t* trow = a.pages != nullptr ? a.table + (long long)(row / a.Hkv) * a.max_blocks : nullptr;
   if (n <= kMaxFast && n > 0) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + kThreads * i, n - 1)];
+    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + NT * i, n - 1)];
     if (trow != nullptr) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + kThreads * i, n - 1)];
+      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + NT * i, n - 1)];
     }
   }
-  const bool do_append = !prefill && a.k_new != nullptr && N > 0;   // uniform
+  const bool do_append = NT == kThreads && !prefill && a.k_new != nullptr && N > 0;   // uniform
   const int jlast = do_append ? n - 1 : -1;
   DecodeAppend<T> ap;
   if (do_append) ap.issue(a, row, N);
 
-  const int ngroups = min(n, kThreads);     // threads holding at least one candidate
+  const int ngroups = min(n, NT);     // threads holding at least one candidate
   const bool fast = n <= kMaxFast && keff < n && keff <= ngroups;   // uniform
   if (!fast) {
     // every candidate kept, or the exact path: finish the append first
@@ -306,11 +312,11 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
       if (tid == 0) srow[jlast] = fresh;
     }
     if (keff == n) {
-      for (int i = tid; i < n; i += kThreads) emit(a, row, i, i);
+      for (int i = tid; i < n; i += NT) emit(a, row, i, i);
     } else {
-      select_fallback(a, srow, row, n, keff, jlast, fresh, sh);
+      select_fallback<NT>(a, srow, row, n, keff, jlast, fresh, sh);
     }
-    pad(a, row, keff, n, prefill);
+    pad<NT>(a, row, keff, n, prefill);
     return;
   }
 
@@ -321,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   uint32_t cm = 0u;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int j = tid + kThreads * i;
+    const int j = tid + NT * i;
     key[i] = (j < n && j != jlast) ? order_key(v[i]) : 0u;
     cm = max(cm, key[i]);
   }
@@ -329,13 +335,13 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   if (tid == 0) sh.cnt = 0;
   // ---- 1. range of the group maxima
   const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
-  if (lane == 0) { sh.red[wave] = wmx; sh.red[kWaves + wave] = wmn; }
+  if (lane == 0) { sh.red[wave] = wmx; sh.red[kW + wave] = wmn; }
   if (tid < kBins) sh.hist[tid] = 0u;
   if (tid == 0) sh.bstar = 0;   // bin 0 keeps every group maximum: always a valid bound
   __syncthreads();
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kWaves + w]); }
+  for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
   const unsigned long long span = (unsigned long long)(mx - mn) + 1ull;
   uint32_t bin = 0u;
   if (has) {
@@ -368,17 +374,17 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   float fresh = 0.f;
   if (do_append) {
     fresh = ap.fresh(sh);
-    if (jlast % kThreads == tid) key[jlast / kThreads] = order_key(fresh);
+    if (jlast % NT == tid) key[jlast / NT] = order_key(fresh);
   }
   __syncthreads();
   if (do_append && tid == 0) srow[jlast] = fresh;
   uint32_t T0 = 0xffffffffu;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) T0 = min(T0, sh.red[w]);
+  for (int w = 0; w < kW; ++w) T0 = min(T0, sh.red[w]);
   // ---- 2. survivors (keys >= T0) as (key, ~index) composites (+ page id)
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int j = tid + kThreads * i;
+    const int j = tid + NT * i;
     if (j < n && key[i] >= T0) {
       const int p = atomicAdd(&sh.cnt, 1);
       if (p < kCap) {
@@ -393,7 +399,7 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
   if (m >= keff && m <= kCap) {   // uniform; m >= k_eff holds by construction of T0
     const int npair = (m + 1) >> 1;
     const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
-    for (int e = tid; e < m; e += kThreads) {
+    for (int e = tid; e < m; e += NT) {
       const unsigned long long ce = sh.comp[e];
       const int je = (int)~(uint32_t)ce;
       const int pge = trow != nullptr ? sh.spage[e] : -1;
@@ -410,7 +416,7 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
     // ---- 3. ascending block order
     const int nq = (keff + 3) >> 2;
     const int4* sp = reinterpret_cast<const int4*>(sh.sel);
-    for (int e = tid; e < keff; e += kThreads) {
+    for (int e = tid; e < keff; e += NT) {
       const int vj = sh.sel[e];
       int pos = 0;
 #pragma unroll 4
@@ -423,18 +429,26 @@ __global__ void __launch_bounds__(kThreads) k_topk(TopkArgs a) {
     }
     done = true;
   }
-  if (!done) select_fallback(a, srow, row, n, keff, jlast, fresh, sh);
-  pad(a, row, keff, n, prefill);
+  if (!done) select_fallback<NT>(a, srow, row, n, keff, jlast, fresh, sh);
+  pad<NT>(a, row, keff, n, prefill);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, bool bf16, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  if (bf16)
-    k_topk<uint16_t><<<a.rows, kThreads, 0, st>>>(a);
-  else
-    k_topk<float><<<a.rows, kThreads, 0, st>>>(a);
+  // rows of at most 512 * kPer candidates and k <= 512, with no fused append, run on 512 threads
+  // (two workgroups fit a CU); everything else on 1024
+  const bool prefill = a.lens == nullptr;
+  const long long n_max = prefill ? (long long)a.base_blocks + (a.rows - 1) / a.Hkv : ((long long)a.max_len + kP - 1) / kP;
+  const bool small = n_max <= 512 * kPer && a.k <= 512 && (prefill || a.k_new == nullptr);
+  if (bf16) {
+    if (small) k_topk<uint16_t, 512><<<a.rows, 512, 0, st>>>(a);
+    else k_topk<uint16_t, kThreads><<<a.rows, kThreads, 0, st>>>(a);
+  } else {
+    if (small) k_topk<float, 512><<<a.rows, 512, 0, st>>>(a);
+    else k_topk<float, kThreads><<<a.rows, kThreads, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
