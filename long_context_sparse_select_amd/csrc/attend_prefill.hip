@@ -23,7 +23,8 @@
 //     reference max moves only when a row's max outgrows it by 2^8, so the O rescale is rare;
 //     the causal mask is a branch taken on the diagonal block only.
 // The kernel is bound by LDS fragment reads (each 32-row wave reads the whole K and V^T block:
-// 1 KiB of LDS per 32 KFLOP of MFMA), not by HBM.
+// 1 KiB of LDS per 32 KFLOP of MFMA), not by HBM; the fragment reads are issued four MFMAs
+// ahead, and the first V^T fragments are requested before the softmax.
 #include "common.h"
 #include "kernels.h"
 
@@ -117,19 +118,34 @@ struct PrefillWave {
   float scale_log2;
 
   __device__ __forceinline__ void step(const uint16_t* sK, const uint16_t* sV, bool diag_block) {
-    // ---- S^T = K Q^T: tile t holds keys swap23(32t + row)
+    // ---- S^T = K Q^T: tile t holds keys swap23(32t + row). Fragment f = (t = f/8, kk = f%8),
+    // read from LDS four fragments ahead of its MFMA.
+    constexpr int kAhead = 4;
     f32x16 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
-      const uint16_t* krow = sK + swap_bits23(32 * t + n) * kKPitch + 8 * c;
+    const uint16_t* krow0 = sK + swap_bits23(n) * kKPitch + 8 * c;
+    const uint16_t* krow1 = sK + swap_bits23(32 + n) * kKPitch + 8 * c;
+    uint4 kf[kAhead];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * kk));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], s[t], 0, 0, 0);
+    for (int f = 0; f < kAhead; ++f) kf[f] = *reinterpret_cast<const uint4*>((f < 8 ? krow0 : krow1) + 16 * (f % 8));
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const bf16x8 af = as_bf16x8(kf[f % kAhead]);
+      if (f + kAhead < 16) {
+        const int g2 = f + kAhead;
+        kf[f % kAhead] = *reinterpret_cast<const uint4*>((g2 < 8 ? krow0 : krow1) + 16 * (g2 % 8));
       }
+      s[f / 8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[f % 8], s[f / 8], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // first V^T fragments requested before the softmax: fragment f = (dt = f/4, ks = f%4)
+    const uint16_t* vbase = sV + n * kVPitch + 8 * c;
+    uint4 vf[kAhead];
+#pragma unroll
+    for (int f = 0; f < kAhead; ++f) vf[f] = *reinterpret_cast<const uint4*>(vbase + (32 * (f / 4)) * kVPitch + 16 * (f % 4));
     if (diag_block) {  // causal mask: key position within the block <= query position
       __builtin_amdgcn_sched_barrier(0);   // keeps the mask a branch, not selects on every block
 #pragma unroll
@@ -178,15 +194,17 @@ struct PrefillWave {
       pf[ks] = as_bf16x8(make_uint4(pack_bf16x2(s[t][b + 0], s[t][b + 1]), pack_bf16x2(s[t][b + 2], s[t][b + 3]),
                                     pack_bf16x2(s[t][b + 4], s[t][b + 5]), pack_bf16x2(s[t][b + 6], s[t][b + 7])));
     }
-    // ---- O^T += V^T P^T: dim tile dt, keys 16ks + 8c .. +7
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T: dim tile dt, keys 16ks + 8c .. +7; fragments four ahead
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vrow = sV + (32 * dt + n) * kVPitch + 8 * c;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 af = as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 16 * ks));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[ks], o[dt], 0, 0, 0);
+    for (int f = 0; f < 16; ++f) {
+      const bf16x8 af = as_bf16x8(vf[f % kAhead]);
+      if (f + kAhead < 16) {
+        const int g2 = f + kAhead;
+        vf[f % kAhead] = *reinterpret_cast<const uint4*>(vbase + (32 * (g2 / 4)) * kVPitch + 16 * (g2 % 4));
       }
+      o[f / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[f % 4], o[f / 4], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
