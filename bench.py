@@ -91,6 +91,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
     ap.add_argument("--no-mixed", action="store_true", help="skip the batch-32 mixed-length decode line")
+    ap.add_argument("--no-large-k", action="store_true", help="skip the 1M-token k=1024 operating-point line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
@@ -215,6 +216,8 @@ def main():
                             "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": kv_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kv_bytes},
     }
+    if not args.no_large_k:
+        rec["large_k"] = bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph)
     tr = recorded_traffic(score_bytes)
     if tr is not None:
         rec["roofline"]["traffic"] = tr["bytes_per_launch"]
@@ -362,6 +365,41 @@ def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload,
     log("batch-8 attend: %.2f us, %.0f GB/s of selected KV" % (t * 1e6, kv / t / 1e9))
     return {"workload": "decode_bf16_b8_128k", "attend_us": t * 1e6, "kv_GBps": kv / t / 1e9,
             "kv_hbm_frac": kv / t / 1e9 / HBM_PEAK_GBPS, "bytes_per_launch": kv}
+
+
+def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph, k=1024):
+    """The pages' operating point on the same 1M-token caches: k = 1024 of 16,384 blocks (~6 %),
+    256 MiB of selected K/V per step. Whole decode steps, Step 1 (score + top-k) and Step 2."""
+    c0 = cases[0]
+    B, max_len = c0.B, c0.max_seq_len
+    cfg = msa.make_config(c0.Hq, c0.Hkv, k, dtype=c0.dtype, softmax_scale=c0.scale)
+    dev = q_ring[0].device
+    out = torch.empty((B, c0.Hq, c0.D), dtype=q_ring[0].dtype, device=dev)
+    idx_bufs = [torch.empty((B, c0.Hkv, k), dtype=torch.int32, device=dev) for _ in range(L)]
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    n_rep = 10
+
+    def timed(fn):
+        g = timed_graph(fn, per_graph, torch)
+        run_graph(g, 2, torch)
+        return run_graph(g, n_rep, torch) / (per_graph * n_rep)
+    t_step = timed(lambda i: msa.msa_decode_step(cfg, q_ring[i % R], caches[i % L], B, max_len, out,
+                                                 k_new=kn_ring[i % R], v_new=vn_ring[i % R],
+                                                 idx_out=idx_bufs[i % L], workspace=ws))
+    t_sel = timed(lambda i: msa.msa_select(cfg, q_ring[i % R], caches[i % L], B, max_len, idx_bufs[i % L],
+                                           workspace=ws))
+    t_att = timed(lambda i: msa.msa_attend(cfg, q_ring[i % R], caches[i % L], B, max_len, idx_bufs[i % L], out,
+                                           workspace=ws))
+    torch.cuda.synchronize()
+    elem = 2 if c0.dtype == "bf16" else 4
+    kv = float(np.mean([selected_kv_bytes(idx_bufs[l], cases[l].seq_lens, elem=elem) for l in range(L)]))
+    log("1M k=%d: step %.1f us (%.0f tokens/s); select %.1f us; attend %.1f us (%.0f GB/s of selected KV)"
+        % (k, t_step * 1e6, B / t_step, t_sel * 1e6, t_att * 1e6, kv / t_att / 1e9))
+    return {"workload": "decode_bf16_1m_paged", "top_k": k, "step_us": t_step * 1e6, "tokens_per_s": B / t_step,
+            "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9,
+            "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS, "bytes_per_attend": kv,
+            "note": "the pages' ~6 % operating point (16,384 blocks, k = 1024); same caches as the headline"}
 
 
 def bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev):

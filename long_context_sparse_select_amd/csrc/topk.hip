@@ -40,6 +40,8 @@ constexpr int kPer = 16;                // candidates held per thread
 constexpr int kCap = 2048;
 constexpr int kBins = 256;
 constexpr int kMaxK = 4096;
+constexpr int kSmallK = 256;    // k_eff up to this uses the survivor path; larger k the exact select
+constexpr int kLBins = 1024;    // bins per pass of the exact select
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
@@ -120,6 +122,9 @@ struct TopkShared {
   int32_t selpg[kMaxK];
   int32_t spage[kCap];
   uint32_t hist[kBins];
+  uint32_t hbig[kLBins];             // exact select: histogram of the current key range
+  int pre[kPer * kWaves];            // exact select: per (slot, wave) counts, then their prefixes
+  uint32_t range[3];                 // exact select: lo, hi, keys above hi
   uint32_t red[2 * kWaves];
   int tmp[kWaves];
   int cnt;
@@ -173,6 +178,127 @@ __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, i
     if (sel) emit(a, row, pos, j);
     run_eq += tot_eq;
     run_sel += tot_sel;
+  }
+}
+
+// Exclusive prefix, in ascending block order, of per-(slot, wave) counts of `pred` (slot i of
+// thread t holds block t + NT*i, so the order is slot-major, then wave, then lane). Returns this
+// thread's position for slot i in *pos and the block's total. Two barriers.
+template <int NT>
+__device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&pos)[kPer], TopkShared& sh) {
+  constexpr int kW = NT / 64, kE = kPer * kW;   // entries, at most 256
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long bm[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    bm[i] = __ballot(pred[i]);
+    if (lane == 0) sh.pre[i * kW + wave] = __popcll(bm[i]);
+  }
+  __syncthreads();
+  if (wave == 0) {   // lane l scans entries 4l .. 4l+3, then an exclusive scan across lanes
+    int v[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = 4 * lane + e < kE ? sh.pre[4 * lane + e] : 0; sum += v[e]; }
+    int incl = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int run = incl - sum;
+    const int total = __shfl(incl, 63);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (4 * lane + e < kE) sh.pre[4 * lane + e] = run;
+      run += v[e];
+    }
+    if (lane == 0) sh.cnt = total;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    pos[i] = sh.pre[i * kW + wave] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm[i], 0u));
+  return sh.cnt;
+}
+
+// Exact selection for large k on keys held in registers (slot i of thread t = block t + NT*i):
+//  1. the k_eff-th largest key T by range refinement: a 1024-bin histogram of the keys in
+//     [lo, hi], the bin where the count from the top reaches k_eff becomes the next range; a
+//     32-bit key range takes at most 4 passes;
+//  2. ordered compaction: keys > T, then the ties == T with the smallest block indices, written
+//     at their rank in ascending block order (no sort needed).
+template <int NT>
+__device__ void select_large(const TopkArgs& a, int row, int n, int keff, const uint32_t (&key)[kPer],
+                             const int (&pg)[kPer], bool with_pages, TopkShared& sh) {
+  constexpr int kW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool valid[kPer];
+  uint32_t kmx = 0u, kmn = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    valid[i] = tid + NT * i < n;
+    if (valid[i]) { kmx = max(kmx, key[i]); kmn = min(kmn, key[i]); }
+  }
+  kmx = wave_max_u32(kmx);
+  kmn = wave_min_u32(kmn);
+  if (lane == 0) { sh.red[wave] = kmx; sh.red[kW + wave] = kmn; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t mx = 0u, mn = 0xffffffffu;
+    for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
+    sh.range[0] = mn; sh.range[1] = mx; sh.range[2] = 0u;
+  }
+  __syncthreads();
+  uint32_t lo = sh.range[0], hi = sh.range[1], above = 0u;
+  while (lo != hi) {   // uniform
+    for (int b = tid; b < kLBins; b += NT) sh.hbig[b] = 0u;
+    __syncthreads();
+    const unsigned long long span = (unsigned long long)(hi - lo) + 1ull;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (valid[i] && key[i] >= lo && key[i] <= hi)
+        atomicAdd(&sh.hbig[(uint32_t)(((unsigned long long)(key[i] - lo) * kLBins) / span)], 1u);
+    __syncthreads();
+    if (wave == 0) {   // lane l owns bins 16l .. 16l+15; counts from the top
+      uint32_t c[16], local = 0u;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { c[e] = sh.hbig[16 * lane + e]; local += c[e]; }
+      uint32_t incl = local;  // suffix sum over lanes >= lane
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
+        if (lane + off < 64) incl += y;
+      }
+      uint32_t run = above + incl - local;   // keys above this lane's bins
+      for (int e = 15; e >= 0; --e) {
+        if (run < (uint32_t)keff && run + c[e] >= (uint32_t)keff) {
+          const unsigned long long bsel = 16ull * lane + e;
+          // bin b holds keys lo + [ceil(b*span/1024), ceil((b+1)*span/1024) - 1]
+          sh.range[0] = lo + (uint32_t)((bsel * span + kLBins - 1) / kLBins);
+          sh.range[1] = lo + (uint32_t)(((bsel + 1) * span + kLBins - 1) / kLBins) - 1u;
+          sh.range[2] = run;
+        }
+        run += c[e];
+      }
+    }
+    __syncthreads();
+    lo = sh.range[0]; hi = sh.range[1]; above = sh.range[2];
+  }
+  const uint32_t T = lo;
+  const int need_eq = keff - (int)above;   // >= 1 ties at T are kept, smallest block indices first
+  bool eq[kPer];
+  int rk[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) eq[i] = valid[i] && key[i] == T;
+  ordered_prefix<NT>(eq, rk, sh);
+  bool sel[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sel[i] = valid[i] && (key[i] > T || (eq[i] && rk[i] < need_eq));
+  ordered_prefix<NT>(sel, rk, sh);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (sel[i]) {
+      a.idx[(long long)row * a.idx_stride + rk[i]] = tid + NT * i;
+      if (with_pages) a.pages[(long long)row * a.k + rk[i]] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
+    }
   }
 }
 
@@ -299,7 +425,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   if (do_append) ap.issue(a, row, N);
 
   const int ngroups = min(n, NT);     // threads holding at least one candidate
-  const bool fast = n <= kMaxFast && keff < n && keff <= ngroups;   // uniform
+  const bool fast = n <= kMaxFast && keff < n && keff <= ngroups && keff <= kSmallK;   // uniform
   if (!fast) {
     // every candidate kept, or the exact path: finish the append first
     float fresh = 0.f;
@@ -313,6 +439,14 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     }
     if (keff == n) {
       for (int i = tid; i < n; i += NT) emit(a, row, i, i);
+    } else if (n <= kMaxFast) {   // large k: exact select on the keys in registers
+      uint32_t key[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int j = tid + NT * i;
+        key[i] = j < n ? order_key(j == jlast ? fresh : v[i]) : 0u;
+      }
+      select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);
     } else {
       select_fallback<NT>(a, srow, row, n, keff, jlast, fresh, sh);
     }
@@ -429,7 +563,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     }
     done = true;
   }
-  if (!done) select_fallback<NT>(a, srow, row, n, keff, jlast, fresh, sh);
+  if (!done) select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);   // mass ties at T0
   pad<NT>(a, row, keff, n, prefill);
 }
 

@@ -34,6 +34,9 @@ SMALL = [
     # leave chunks with 1..3 attended blocks
     ("bf16_g2_wide", dict(B=6, Hq=16, Hkv=8, lens=[70000, 4096, 65, 1, 33333, 9000], top_k=64,
                           dtype="bf16", permute=True)),
+    # large k: the exact selection path (range-refined threshold + ordered compaction)
+    ("bf16_g4_k1024", dict(B=1, Hq=8, Hkv=2, lens=[262144], top_k=1024, dtype="bf16", permute=True)),
+    ("f32_g2_k700_ragged", dict(B=2, Hq=4, Hkv=2, lens=[100000, 45000], top_k=700, dtype="f32")),
     # 160 (sequence, group) rows: sixteen blocks per workgroup (four chunks of four), ragged rows
     ("bf16_g4_b20_many_rows", dict(B=20, Hq=32, Hkv=8, lens=[20000, 1, 4100, 64, 65, 127, 8191, 5000, 12345, 300,
                                                              16384, 2, 999, 4096, 7777, 640, 641, 19999, 3000, 10],
@@ -242,6 +245,36 @@ def test_full_size_decode(name):
     hit = sum(len(set(v) & set(idx[b, g])) for (b, g), v in c.planted.items())
     tot = sum(len(v) for v in c.planted.values())
     assert hit / tot > 0.8
+
+
+def test_full_size_decode_large_k():
+    """The pages' operating point: 1M tokens, k = 1024 of 16,384 blocks (about 6 %)."""
+    kw = dict(workload("decode_bf16_1m_paged", seed=0), top_k=1024)
+    c = make_decode_case_torch(**kw)
+    d = to_device(c)
+    res = run_decode(d)
+    off = full_decode_check(d, res)
+    print("1M k=1024: %d rows differ from the oracle inside the band" % off)
+
+
+@pytest.mark.parametrize("k", [300, 1500])
+def test_large_k_all_scores_tied(k):
+    """Every block scores exactly 0 (all keys zero): the kept blocks are the k smallest indices."""
+    c = make_decode_case(B=2, Hq=8, Hkv=2, lens=[130000, 64 * 2000 - 5], top_k=k, dtype="bf16", seed=41,
+                         permute=True)
+    d = to_device(c, build=False)
+    d.k.zero_()
+    msa.msa_build_summaries(d.cfg, d.cache, c.B, c.max_seq_len)
+    idx = torch.empty((c.B, c.Hkv, k), dtype=torch.int32, device="cuda")
+    msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(c.B):
+        nb = (int(c.seq_lens[b]) + 63) // 64
+        want = np.arange(min(k, nb), dtype=np.int32)
+        for g in range(c.Hkv):
+            assert np.array_equal(got[b, g, :len(want)], want), (b, g)
+            assert np.all(got[b, g, len(want):] == -1)
 
 
 def test_full_size_mixed_batch_sampled():
