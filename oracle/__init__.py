@@ -56,6 +56,8 @@ def _load():
         lib.orc_summaries.argtypes = [I, I, I, I, I, P, I, P, I, P, P]
         lib.orc_summaries.restype = I
         lib.orc_prefill.argtypes = [I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
+        lib.orc_select_index.argtypes = [I, I, I, I, I, I, P, P, I, P, I, P, P, P]
+        lib.orc_select_index.restype = I
         lib.orc_prefill.restype = I
         _lib = lib
     return _lib
@@ -103,6 +105,28 @@ def summaries(*, k_pool, block_table, seq_lens, Hkv: int, D: int, P: int) -> np.
     if rc != 0:
         raise RuntimeError("orc_summaries failed (%d)" % rc)
     return out
+
+
+def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int = 64) -> dict:
+    """The index branch of [MGS §1 Step 1] (reading R8): token scores of each group's index query
+    against the single-head index keys, Block Max Pool, TopK. q_idx [B][Hkv][Di] and
+    index_keys [num_pages][P][Di] share one storage dtype (float32, or bf16 bits as uint16).
+    Returns scores [B][Hkv][max_blocks] (fp64, -inf past the blocks) and idx [B][Hkv][top_k]."""
+    qi = _c(q_idx)
+    ik = _c(index_keys)
+    if _dtype_code(qi) != _dtype_code(ik):
+        raise ValueError("q_idx and index_keys must share a dtype")
+    table = _c(block_table, np.int32)
+    lens = _c(seq_lens, np.int32)
+    B, Hkv, Di = qi.shape
+    mb = table.shape[1]
+    scores = np.empty((B, Hkv, mb), dtype=np.float64)
+    idx = np.empty((B, Hkv, top_k), dtype=np.int32)
+    rc = _load().orc_select_index(B, Hkv, Di, P, top_k, _dtype_code(qi), _ptr(qi), _ptr(ik), int(ik.shape[0]),
+                                  _ptr(table), mb, _ptr(lens), _ptr(scores), _ptr(idx))
+    if rc != 0:
+        raise RuntimeError("orc_select_index failed (%d)" % rc)
+    return {"scores": scores, "idx": idx}
 
 
 def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k: int,

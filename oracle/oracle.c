@@ -34,6 +34,11 @@
  *                        the tile's diagonal block; the diagonal block is always kept and is
  *                        causally masked inside (key position <= query position).
  *   R7 softmax         = logits scale * <q_h, k_t>; weights exp(z - max) / sum; lse = max + ln sum.
+ *   R8 index branch    = the page's literal Step 1 (orc_select_index): one index key per token,
+ *                        a single head shared by every group (K_idx, dimension d_idx, paged like
+ *                        K); one index query per group (given); token score <q_idx[g], K_idx[t]>,
+ *                        unscaled; a block's score is the maximum of its valid tokens' scores
+ *                        ("Block Max Pool"); then TopK as R3.
  *
  * All arithmetic is fp64 on exact upcasts of the stored inputs (f32 or bf16 bit patterns).
  * Layouts: q [B][Hq][D]; K/V pools [num_pages][Hkv][P][D]; block_table [B][max_blocks].
@@ -461,4 +466,50 @@ int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtyp
     free(jobs);
     free(S);
     return a.status ? a.status : rc;
+}
+
+/* ------------------------------------------------------------------ index branch (Step 1, R8) */
+/* [MGS §1 Step 1] the index branch as the diagram draws it: per group g, token scores
+ * <q_idx[b][g], K_idx[t]> over every valid token t of sequence b, the maximum over each 64-token
+ * block (partial last block: its valid tokens), then TopK per (b, g).
+ * q_idx [B][Hkv][Di]; ikeys [num_pages][P][Di] (one head), pages through block_table.
+ * scores_out (nullable) [B][Hkv][max_blocks] (-inf past the blocks, or for a bad page id);
+ * idx_out [B][Hkv][top_k]. Returns 0 on success. */
+int orc_select_index(int B, int Hkv, int Di, int P, int top_k, int dtype, const void* q_idx,
+                     const void* ikeys, int num_pages, const int32_t* table, int max_blocks,
+                     const int32_t* seq_lens, double* scores_out, int32_t* idx_out) {
+    if (B < 0 || Hkv < 1 || Di < 1 || P < 1 || top_k < 0 || !q_idx || !ikeys || !table || !seq_lens ||
+        !idx_out || (dtype != ORC_F32 && dtype != ORC_BF16))
+        return -1;
+    double* row = (double*)malloc(sizeof(double) * (size_t)(max_blocks > 0 ? max_blocks : 1));
+    if (!row) return -3;
+    for (int b = 0; b < B; ++b) {
+        int N = seq_lens[b];
+        if (N < 0 || N > max_blocks * P) { free(row); return -2; }
+        int nb = (N + P - 1) / P;
+        for (int g = 0; g < Hkv; ++g) {
+            for (int j = 0; j < nb; ++j) {
+                int32_t page = table[(size_t)b * max_blocks + j];
+                double best = -INFINITY;
+                if (page >= 0 && page < num_pages) {
+                    int n_j = N - j * P < P ? N - j * P : P;
+                    for (int t = 0; t < n_j; ++t) {
+                        double s = 0.0;
+                        for (int d = 0; d < Di; ++d)
+                            s += elem(q_idx, dtype, ((size_t)b * Hkv + g) * Di + d) *
+                                 elem(ikeys, dtype, ((size_t)page * P + t) * Di + d);
+                        if (s > best) best = s;
+                    }
+                }
+                row[j] = best;
+            }
+            if (scores_out) {
+                double* srow = scores_out + ((size_t)b * Hkv + g) * max_blocks;
+                for (int j = 0; j < max_blocks; ++j) srow[j] = j < nb ? row[j] : -INFINITY;
+            }
+            if (orc_topk(row, nb, top_k, idx_out + ((size_t)b * Hkv + g) * top_k) < 0) { free(row); return -3; }
+        }
+    }
+    free(row);
+    return 0;
 }

@@ -37,6 +37,13 @@ MUTANTS = [
      "qt[d] = acc / (double)G;", False),
     ("prefill_chunk_values_from_keys", "const void* src = which_v ? a->v_new : a->k_new;",
      "const void* src = a->k_new;", False),
+    ("index_sum_pool_not_max", "if (s > best) best = s;", "best = (t == 0) ? s : best + s;", False),
+    ("index_partial_block_reads_past_length", "int n_j = N - j * P < P ? N - j * P : P;", "int n_j = P;",
+     False),
+    ("index_query_of_group_zero", "elem(q_idx, dtype, ((size_t)b * Hkv + g) * Di + d)",
+     "elem(q_idx, dtype, ((size_t)b * Hkv + 0) * Di + d)", False),
+    ("index_key_first_token_only", "elem(ikeys, dtype, ((size_t)page * P + t) * Di + d)",
+     "elem(ikeys, dtype, ((size_t)page * P + 0) * Di + d)", False),
 ]
 
 

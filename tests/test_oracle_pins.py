@@ -328,3 +328,110 @@ def test_prefill_selection_and_tile_scores():
             np.testing.assert_allclose(r["scores"][tau, g, :d], want, rtol=1e-12, atol=1e-12)
             sel = oracle.topk(want, 3)
             assert list(r["idx"][tau, g]) == list(sel) + [d]
+
+
+# ----------------------------------------------------------------------------- index branch (R8)
+# The pages' literal Step 1: single-head index keys shared by every group, one index query per
+# group, token scores, Block Max Pool, TopK (oracle.select_index).
+def _index_case(lens=(200, 64, 131), Hkv=3, Di=16, seed=5):
+    rng = np.random.default_rng(seed)
+    nb = [(n + 63) // 64 for n in lens]
+    mb = max(nb) + 1
+    num_pages = sum(nb) + 3
+    perm = rng.permutation(num_pages)
+    table = np.full((len(lens), mb), -1, np.int32)
+    p = 0
+    for b, n in enumerate(nb):
+        for j in range(n):
+            table[b, j] = perm[p]
+            p += 1
+    q = rng.standard_normal((len(lens), Hkv, Di)).astype(np.float32)
+    ik = rng.standard_normal((num_pages, 64, Di)).astype(np.float32)
+    return q, ik, table, np.array(lens, np.int32)
+
+
+def _token_value(b, t):
+    return np.float32(10.0 * math.sin(1.7 * t + 0.3 * b) + 0.01 * t)
+
+
+def test_index_max_pool_closed_form():
+    """q_idx[b][g] = (g + 1) e0, so a token scores (g + 1) * K_idx[t][0] and a block scores
+    (g + 1) * max of dim 0 over its valid tokens; slots past the length hold a huge dim 0."""
+    q, ik, table, lens = _index_case()
+    B, Hkv, Di = q.shape
+    q[:] = 0.0
+    q[:, :, 0] = np.arange(1, Hkv + 1, dtype=np.float32)[None, :]
+    ik[:, :, 0] = 1.0e6                                   # never a valid token's value
+    for b in range(B):
+        for t in range(int(lens[b])):
+            ik[table[b, t // 64], t % 64, 0] = _token_value(b, t)
+    r = oracle.select_index(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens, top_k=2)
+    for b in range(B):
+        n = int(lens[b])
+        nb = (n + 63) // 64
+        for g in range(Hkv):
+            for j in range(table.shape[1]):
+                if j < nb:
+                    want = (g + 1) * max(float(_token_value(b, t)) for t in range(64 * j, min(n, 64 * j + 64)))
+                    assert r["scores"][b, g, j] == want
+                else:
+                    assert r["scores"][b, g, j] == -np.inf
+
+
+def test_index_reduces_to_mean_pool_for_constant_blocks():
+    """When every valid token of a block carries the same index key, max pool == mean pool: the
+    mean-pool route (orc_decode's summaries and scores with G = 1, q = q_idx, every group's keys
+    = the index keys) gives the same scores and the same lists."""
+    q, ik, table, lens = _index_case(Hkv=2, Di=8)
+    for b in range(len(lens)):
+        for j in range((int(lens[b]) + 63) // 64):
+            ik[table[b, j], :, :] = ik[table[b, j], 0, :]
+    k = 3
+    r = oracle.select_index(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens, top_k=k)
+    Hkv, Di = q.shape[1], q.shape[2]
+    kp = np.ascontiguousarray(np.repeat(ik[:, None], Hkv, axis=1))      # [pages][Hkv][64][Di]
+    d = oracle.decode(q=q, k_pool=kp, v_pool=kp, block_table=table, seq_lens=lens, Hq=Hkv, Hkv=Hkv,
+                      top_k=k, scale=1.0)
+    for b in range(len(lens)):
+        nb = (int(lens[b]) + 63) // 64
+        assert np.array_equal(r["scores"][b, :, :nb], d["scores"][b, :, :nb])
+    assert np.array_equal(r["idx"], d["idx"])
+
+
+def test_index_invariances():
+    """Reordering the tokens of a full block, or moving blocks to other pages (table updated),
+    changes no score and no list; bf16 storage equals its exact float32 upcast."""
+    q, ik, table, lens = _index_case(lens=(256, 320))
+    base = oracle.select_index(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens, top_k=3)
+    ik2 = ik.copy()
+    rng = np.random.default_rng(1)
+    for page in range(ik.shape[0]):
+        ik2[page] = ik[page][rng.permutation(64)]          # every block of these sequences is full
+    r2 = oracle.select_index(q_idx=q, index_keys=ik2, block_table=table, seq_lens=lens, top_k=3)
+    assert np.array_equal(base["scores"], r2["scores"]) and np.array_equal(base["idx"], r2["idx"])
+    perm = rng.permutation(ik.shape[0])
+    ik3 = np.empty_like(ik)
+    ik3[perm] = ik
+    table3 = np.where(table >= 0, perm[np.maximum(table, 0)], -1).astype(np.int32)
+    r3 = oracle.select_index(q_idx=q, index_keys=ik3, block_table=table3, seq_lens=lens, top_k=3)
+    assert np.array_equal(base["scores"], r3["scores"]) and np.array_equal(base["idx"], r3["idx"])
+    qb, ikb = storage(q, "bf16"), storage(ik, "bf16")
+    rb = oracle.select_index(q_idx=qb, index_keys=ikb, block_table=table, seq_lens=lens, top_k=3)
+    ru = oracle.select_index(q_idx=round_to_bf16(q), index_keys=round_to_bf16(ik), block_table=table,
+                             seq_lens=lens, top_k=3)
+    assert np.array_equal(rb["scores"], ru["scores"]) and np.array_equal(rb["idx"], ru["idx"])
+
+
+def test_index_planted_token_and_bad_page():
+    """A single token planted along group 0's index query makes its block group 0's best block,
+    scoring exactly that token's score; a bad page id scores -inf and is never kept."""
+    q, ik, table, lens = _index_case(lens=(64 * 9,), Hkv=2, Di=8, seed=9)
+    u = q[0, 0] / np.linalg.norm(q[0, 0])
+    ik[table[0, 5], 17] = (40.0 * u).astype(np.float32)
+    table[0, 2] = 10_000                                  # out of range: never read
+    r = oracle.select_index(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens, top_k=8)
+    want = float(np.dot(q[0, 0].astype(np.float64), ik[table[0, 5], 17].astype(np.float64)))
+    assert r["scores"][0, 0, 5] == pytest.approx(want, rel=1e-15)
+    assert np.argmax(r["scores"][0, 0]) == 5
+    assert r["scores"][0, 0, 2] == -np.inf and r["scores"][0, 1, 2] == -np.inf
+    assert 2 not in r["idx"][0, 0] and 2 not in r["idx"][0, 1]
