@@ -92,6 +92,7 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
     ap.add_argument("--no-mixed", action="store_true", help="skip the batch-32 mixed-length decode line")
     ap.add_argument("--no-large-k", action="store_true", help="skip the 1M-token k=1024 operating-point line")
+    ap.add_argument("--no-index", action="store_true", help="skip the 1M-token index-branch select line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
@@ -229,6 +230,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_mixed:
         rec["mixed_batch"] = bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev)
+        torch.cuda.empty_cache()
+    if not args.no_index:
+        rec["index_select"] = bench_index(args, torch, np, msa, dev)
         torch.cuda.empty_cache()
 
     # ---- prefill
@@ -449,6 +453,42 @@ def bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev):
             "score_hbm_frac": score_bytes / t_score / 1e9 / HBM_PEAK_GBPS,
             "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9, "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS,
             "bytes_per_attend": kv, "bytes_per_score": score_bytes}
+
+
+def bench_index(args, torch, np, msa, dev, L=2, R=8):
+    """Step 1 as the diagram's index branch on the 1M-token shape: single-head 128-dim bf16 index
+    keys (256 MiB per cache, two caches rotated), one index query per group (8 groups), Block Max
+    Pool, top-64. Times msa_select_index (scoring kernel + top-k)."""
+    from synth import make_index_case_torch
+    items = []
+    for layer in range(L):
+        c = make_index_case_torch(B=1, Hkv=8, lens=[1 << 20], top_k=64, dtype="bf16", permute=True,
+                                  plant=("count", 16), seed=args.seed + 1000 * layer, device=dev)
+        items.append((c, torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)))
+    c0 = items[0][0]
+    cfg = msa.make_config(c0.Hkv, c0.Hkv, c0.top_k, dtype="bf16")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 93)
+    q_ring = [torch.randn((1, c0.Hkv, c0.Di), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    idx = [torch.empty((1, c0.Hkv, c0.top_k), dtype=torch.int32, device=dev) for _ in range(L)]
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_SELECT, 1, c0.max_seq_len), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    per = L * R // math.gcd(L, R)
+    g = timed_graph(lambda i: msa.msa_select_index(cfg, q_ring[i % R], items[i % L][0].index_keys, items[i % L][1],
+                                                   items[i % L][2], 1, c0.max_seq_len, idx[i % L], workspace=ws),
+                    per, torch)
+    run_graph(g, 2, torch)
+    n = 10
+    t = run_graph(g, n, torch) / (per * n)
+    nb = (c0.max_seq_len + 63) // 64
+    key_bytes = nb * 64 * c0.Di * 2 + nb * 4 + c0.Hkv * c0.Di * 2 + c0.Hkv * nb * 4
+    log("index-branch select (1M, 8 groups, k=64): %.1f us, %.0f GB/s of index keys over the whole select"
+        % (t * 1e6, key_bytes / t / 1e9))
+    return {"workload": "index_bf16_1m_paged", "context": int(c0.max_seq_len), "kv_groups": c0.Hkv,
+            "index_dim": c0.Di, "top_k": c0.top_k, "select_us": t * 1e6,
+            "score_bytes_per_launch": key_bytes, "GBps_over_select": key_bytes / t / 1e9,
+            "note": "single-head index keys paged like K; the top-k time is included in select_us"}
 
 
 def cpu_baseline(args, case, torch, np):

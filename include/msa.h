@@ -65,8 +65,10 @@ typedef enum msa_status {
 
 typedef enum msa_dtype { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 
-/* How blocks are summarised for Step 1. Only MEAN_KEY is implemented; MAX_TOKEN (the page's
- * literal "Block Max Pool" over a single-head index key) returns MSA_ERR_UNSUPPORTED. */
+/* How the config-driven entry points summarise blocks for Step 1: MEAN_KEY only. MAX_TOKEN
+ * (the diagram's Block Max Pool over a single-head index key) needs index keys and index
+ * queries that msa_config does not carry; it is served by msa_select_index, and the other
+ * entry points return MSA_ERR_UNSUPPORTED for it. */
 typedef enum msa_score_mode { MSA_SCORE_MEAN_KEY = 0, MSA_SCORE_MAX_TOKEN = 1 } msa_score_mode;
 
 typedef enum msa_op {
@@ -132,6 +134,27 @@ msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* c
 msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache,
                       int32_t batch, int32_t max_seq_len, float* scores_out, int32_t* idx_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 1 as the diagram draws its index branch ([MGS §1 Step 1]: Index Q/K, token scores,
+ * Block Max Pool, TopK). One index key per cached token, a single head shared by all groups,
+ * paged with the same block_table as K; one index query per (sequence, group):
+ *   scores_out[b][g][j] = max over the valid tokens t of block j of <q_index[b][g], K_idx[t]>
+ * (unscaled, fp32 accumulation) for j < nb_b = ceil(seq_lens[b]/64); -inf for blocks whose
+ * page id is outside [0, num_pages) and for j in [nb_b, ceil(max_seq_len/64)). The top-k
+ * rule, k_eff, list order and padding are those of msa_select.
+ *   q_index     [batch][Hkv][index_dim] q_dtype
+ *   index_keys  [num_pages][64][index_dim] kv_dtype (page p holds the index keys of the
+ *               block that block_table maps to p)
+ *   index_dim   128 (anything else: MSA_ERR_UNSUPPORTED)
+ *   cache       only block_table, seq_lens, num_pages and max_blocks are read; K/V and
+ *               summaries may be null
+ *   scores_out  nullable [batch][Hkv][ceil(max_seq_len/64)] float32
+ *   idx_out     [batch][Hkv][top_k] int32
+ * cfg->score_mode is not read. Workspace: msa_workspace_size(cfg, MSA_OP_SELECT, ...). */
+msa_status msa_select_index(const msa_config* cfg, const void* q_index, const void* index_keys,
+                            int32_t index_dim, const msa_kv_cache* cache, int32_t batch,
+                            int32_t max_seq_len, float* scores_out, int32_t* idx_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 2 ([MGS §1 Step 2]): every head of group g attends over the tokens of the blocks in
  * idx[b][g][:] (entries < 0 or >= nb_b are skipped; entries must not repeat), split-K across

@@ -5,15 +5,15 @@ its C ABI (include/msa.h) with ctypes. torch supplies device memory and the curr
 There is no CPU fallback; calling any entry point without the built library raises.
 
 Entry points (same names as the C ABI):
-  msa_workspace_size, msa_build_summaries, msa_score, msa_select, msa_attend, msa_decode_step,
-  msa_prefill_chunk, msa_status_string
+  msa_workspace_size, msa_build_summaries, msa_score, msa_select, msa_select_index, msa_attend,
+  msa_decode_step, msa_prefill_chunk, msa_status_string
 """
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     MSA_BF16, MSA_F32, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL, MSA_OP_SELECT, KVCache,
     MsaError, library_path, load_library, make_config, msa_attend, msa_build_summaries,
-    msa_decode_step, msa_prefill_chunk, msa_score, msa_select, msa_status_string,
+    msa_decode_step, msa_prefill_chunk, msa_score, msa_select, msa_select_index, msa_status_string,
     msa_workspace_size,
 )
 
@@ -21,5 +21,5 @@ __all__ = [
     "MSA_BF16", "MSA_F32", "MSA_OP_ATTEND", "MSA_OP_DECODE", "MSA_OP_PREFILL", "MSA_OP_SELECT",
     "KVCache", "MsaError", "library_path", "load_library", "make_config", "msa_attend",
     "msa_build_summaries", "msa_decode_step", "msa_prefill_chunk", "msa_score", "msa_select",
-    "msa_status_string", "msa_workspace_size",
+    "msa_select_index", "msa_status_string", "msa_workspace_size",
 ]

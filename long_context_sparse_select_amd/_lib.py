@@ -15,8 +15,8 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_SCORE_MEAN_KEY, MSA_SCORE_MAX_TOKEN = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL = range(4)
 
-EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_score", "msa_select", "msa_attend",
-            "msa_decode_step", "msa_prefill_chunk", "msa_status_string")
+EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_score", "msa_select", "msa_select_index",
+            "msa_attend", "msa_decode_step", "msa_prefill_chunk", "msa_status_string")
 
 
 class MsaConfig(ctypes.Structure):
@@ -62,6 +62,7 @@ def load_library():
         lib.msa_build_summaries.argtypes = [C, K, I, I, V]
         lib.msa_score.argtypes = [C, V, K, I, I, V, V]
         lib.msa_select.argtypes = [C, V, K, I, I, V, V, V, Z, V]
+        lib.msa_select_index.argtypes = [C, V, V, I, K, I, I, V, V, V, Z, V]
         lib.msa_attend.argtypes = [C, V, K, I, I, V, V, V, V, Z, V]
         lib.msa_decode_step.argtypes = [C, V, K, I, I, V, V, V, V, V, V, V, Z, V]
         lib.msa_prefill_chunk.argtypes = [C, V, V, V, K, I, I, V, V, V, V, V, Z, V]
@@ -153,6 +154,19 @@ def msa_select(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: int, 
     _check(load_library().msa_select(ctypes.byref(cfg), _p(q), ctypes.byref(c), batch, max_seq_len,
                                      _p(scores_out), _p(idx_out), _p(ws), nbytes, _stream(stream, q)),
            "msa_select")
+
+
+def msa_select_index(cfg: MsaConfig, q_index, index_keys, block_table, seq_lens, batch: int,
+                     max_seq_len: int, idx_out, scores_out=None, workspace=None, stream=None) -> None:
+    """q_index [batch][Hkv][128], index_keys [num_pages][64][128] (cfg's dtype), paged through
+    block_table [batch][max_blocks]; only the table, lengths and page count reach the cache struct."""
+    ws, nbytes = _workspace(cfg, MSA_OP_SELECT, batch, max_seq_len, 0, workspace, q_index)
+    c = MsaKvCache(None, None, None, _p(block_table), _p(seq_lens), int(index_keys.shape[0]),
+                   int(block_table.shape[-1]))
+    _check(load_library().msa_select_index(ctypes.byref(cfg), _p(q_index), _p(index_keys),
+                                           int(q_index.shape[-1]), ctypes.byref(c), batch, max_seq_len,
+                                           _p(scores_out), _p(idx_out), _p(ws), nbytes,
+                                           _stream(stream, q_index)), "msa_select_index")
 
 
 def msa_attend(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: int, idx, out,

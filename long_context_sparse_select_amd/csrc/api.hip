@@ -30,7 +30,8 @@ struct Layout {
   int bps = 1, nsplit = 0;
 };
 
-msa_status check_config(const msa_config* c) {
+// any_mode: the entry point does not read score_mode (msa_select_index)
+msa_status check_config(const msa_config* c, bool any_mode = false) {
   if (c == nullptr) return MSA_ERR_INVALID_ARG;
   if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->num_q_heads % c->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (c->top_k < 1) return MSA_ERR_INVALID_ARG;
@@ -44,7 +45,7 @@ msa_status check_config(const msa_config* c) {
   if (c->num_q_heads / c->num_kv_heads > MSA_MAX_GROUP) return MSA_ERR_UNSUPPORTED;
   if (c->num_kv_heads > MSA_MAX_KV_HEADS) return MSA_ERR_UNSUPPORTED;
   if (c->kv_dtype != c->q_dtype || c->out_dtype != c->q_dtype) return MSA_ERR_UNSUPPORTED;
-  if (c->score_mode != MSA_SCORE_MEAN_KEY) return MSA_ERR_UNSUPPORTED;
+  if (c->score_mode != MSA_SCORE_MEAN_KEY && !any_mode) return MSA_ERR_UNSUPPORTED;
   if (c->keep_local != 0) return MSA_ERR_UNSUPPORTED;
   if (c->q_tile != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
@@ -120,13 +121,10 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
 
 // Step 1 on validated arguments; pages (page ids of the kept blocks) and the appended token
 // (k_new / v_new, nullable) are the decode step's extras
-msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
-                      float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
-                      const void* v_new, hipStream_t st) {
+msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                    float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
+                    const void* v_new, hipStream_t st) {
   const bool bf16 = cfg->q_dtype == MSA_BF16;
-  const CacheArgs ca = cache_args(cache);
-  MSA_TRY(hip_status(launch_score_decode(bf16, q, ca, B, cfg->num_q_heads, cfg->num_kv_heads, max_len, scores,
-                                         row_stride, st)));
   TopkArgs t{};
   t.scores = scores;
   t.row_stride = row_stride;
@@ -150,6 +148,14 @@ msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   t.q = q;
   t.Hq = cfg->num_q_heads;
   return hip_status(launch_topk(t, bf16, st));
+}
+
+msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                      float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
+                      const void* v_new, hipStream_t st) {
+  MSA_TRY(hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cache), B, cfg->num_q_heads,
+                                         cfg->num_kv_heads, max_len, scores, row_stride, st)));
+  return run_topk(cfg, q, cache, B, max_len, scores, row_stride, idx, pages, k_new, v_new, st);
 }
 
 // Step 2 on validated arguments
@@ -241,6 +247,27 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
                     (hipStream_t)stream);
+}
+
+msa_status msa_select_index(const msa_config* cfg, const void* q_index, const void* index_keys, int32_t index_dim,
+                            const msa_kv_cache* cache, int32_t batch, int32_t max_seq_len, float* scores_out,
+                            int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  MSA_TRY(check_config(cfg, true));
+  if (cache == nullptr || cache->block_table == nullptr || cache->seq_lens == nullptr) return MSA_ERR_INVALID_ARG;
+  if (cache->num_pages < 0 || cache->max_blocks < 1) return MSA_ERR_INVALID_ARG;
+  MSA_TRY(check_batch(cache, batch, max_seq_len));
+  if (q_index == nullptr || index_keys == nullptr || idx_out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (index_dim < 1) return MSA_ERR_INVALID_ARG;
+  if (index_dim != kD) return MSA_ERR_UNSUPPORTED;
+  const Layout L = decode_layout(cfg, MSA_OP_SELECT, batch, max_seq_len);
+  if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
+  if (batch == 0) return MSA_OK;
+  const hipStream_t st = (hipStream_t)stream;
+  float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
+  MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, cache_args(cache), batch,
+                                        cfg->num_kv_heads, max_seq_len, scores, L.row_stride, st)));
+  return run_topk(cfg, nullptr, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
+                  st);
 }
 
 msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,

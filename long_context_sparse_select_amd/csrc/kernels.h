@@ -25,6 +25,10 @@ hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_ne
 // ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats each.
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
                                int max_len, float* scores, int row_stride, hipStream_t st);
+// index branch (single-head index keys [num_pages][64][128], q_index [B][Hkv][128]): block score
+// = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
+hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, const CacheArgs& c, int B,
+                              int Hkv, int max_len, float* scores, int row_stride, hipStream_t st);
 hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st);
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st);

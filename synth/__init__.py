@@ -36,7 +36,7 @@ D_DEFAULT = 128
 PAD_VALUE = 1000.0  # exactly representable in bf16 (0x447A)
 
 # tensor ids for the per-tensor random streams
-_T_Q, _T_K, _T_V, _T_PLANT, _T_PERM, _T_LEN, _T_KNEW, _T_VNEW = range(8)
+_T_Q, _T_K, _T_V, _T_PLANT, _T_PERM, _T_LEN, _T_KNEW, _T_VNEW, _T_QIDX, _T_KIDX, _T_PTOK = range(11)
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -137,6 +137,34 @@ class PrefillCase:
     @property
     def max_blocks(self) -> int:
         return int(self.block_table.shape[1])
+
+
+@dataclasses.dataclass
+class IndexCase:
+    """Inputs of the index branch: one index query per (sequence, group) and one single-head
+    index key per cached token, paged like K."""
+    dtype: str
+    B: int
+    Hkv: int
+    Di: int
+    P: int
+    top_k: int
+    seq_lens: np.ndarray       # [B] int32
+    block_table: np.ndarray    # [B][max_blocks] int32
+    num_pages: int
+    q_idx: object              # [B][Hkv][Di]
+    index_keys: object         # [num_pages][P][Di]
+    planted: Dict[Tuple[int, int], List[int]]  # (b, g) -> logical blocks holding a planted token
+    label: int = 0
+    seed: int = 0
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.B else 0
 
 
 def storage(x, dtype: str):
@@ -269,6 +297,46 @@ def make_prefill_case(*, Hq: int, Hkv: int, past_len: int, T: int, top_k: int,
                        planted=planted, label=label, seed=seed)
 
 
+def _index_plants(q_idx: np.ndarray, lens, nb, table, Hkv: int, P: int, plant, seed: int, label: int,
+                  plant_shift: float):
+    """page -> [(token slot, shift vector)]: one token of each planted block, drawn among the
+    block's valid tokens, is moved by plant_shift along the unit direction of its group's index
+    query (a single token, so only a max over tokens is sure to see it)."""
+    planted = _plant_positions(nb, Hkv, plant, seed, label)
+    by_page: Dict[int, list] = {}
+    for (b, g), blocks in planted.items():
+        u = plant_shift * _unit(q_idx[b, g])
+        for j in blocks:
+            n_j = min(P, int(lens[b]) - j * P)
+            t = int(rng(seed, label, _T_PTOK, b, g, j).integers(n_j))
+            by_page.setdefault(int(table[b, j]), []).append((t, u))
+    return planted, by_page
+
+
+def make_index_case(*, B: int = 1, Hkv: int, lens: Sequence[int], top_k: int, dtype: str = "bf16",
+                    seed: int = 0, label: int = 5, plant=("count", 3), permute: bool = False,
+                    Di: int = D_DEFAULT, P: int = P_DEFAULT, plant_shift: float = 10.0) -> IndexCase:
+    """Index-branch inputs with numpy: q_idx and K_idx ~ N(0,1); planted blocks get one token
+    shifted along their group's index query; slots past a sequence's length hold PAD_VALUE."""
+    assert len(lens) == B
+    nb, num_pages, table = _layout(lens, P, permute, seed, label)
+    rnd = (lambda a: a) if dtype == "f32" else round_to_bf16
+    q_idx = rnd(rng(seed, label, _T_QIDX).standard_normal((B, Hkv, Di), dtype=np.float32))
+    keys = rng(seed, label, _T_KIDX).standard_normal((num_pages, P, Di), dtype=np.float32)
+    planted, by_page = _index_plants(q_idx, lens, nb, table, Hkv, P, plant, seed, label, plant_shift)
+    for page, items in by_page.items():
+        for t, u in items:
+            keys[page, t, :] += u
+    keys = rnd(keys)
+    for b in range(B):
+        n = int(lens[b])
+        if n > 0 and n % P:
+            keys[table[b, (n - 1) // P], n % P:, :] = PAD_VALUE
+    return IndexCase(dtype=dtype, B=B, Hkv=Hkv, Di=Di, P=P, top_k=top_k,
+                     seq_lens=np.asarray(lens, dtype=np.int32), block_table=table, num_pages=num_pages,
+                     q_idx=q_idx, index_keys=keys, planted=planted, label=label, seed=seed)
+
+
 # ---------------------------------------------------------------------------
 # torch-on-device generator (gigabyte caches); same recipe, torch RNG for the bulk draws
 # ---------------------------------------------------------------------------
@@ -329,6 +397,41 @@ def make_decode_case_torch(*, B: int = 1, Hq: int, Hkv: int, lens: Sequence[int]
                       seq_lens=np.asarray(lens, dtype=np.int32), block_table=table,
                       num_pages=num_pages, q=q, k_pool=k_pool, v_pool=v_pool,
                       planted=planted, label=label, seed=seed)
+
+
+def make_index_case_torch(*, B: int = 1, Hkv: int, lens: Sequence[int], top_k: int, dtype: str = "bf16",
+                          seed: int = 0, label: int = 5, plant=("count", 3), permute: bool = False,
+                          Di: int = D_DEFAULT, P: int = P_DEFAULT, plant_shift: float = 10.0,
+                          device="cuda", chunk_pages: int = 16384) -> IndexCase:
+    """The recipe of make_index_case with the bulk draws made by torch on `device`; q_idx and
+    index_keys are torch tensors (float32 or bfloat16)."""
+    import torch
+    assert len(lens) == B
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    nb, num_pages, table = _layout(lens, P, permute, seed, label)
+    q_idx = _torch_normal((B, Hkv, Di), (seed, label, _T_QIDX), device, torch).to(tdt)
+    planted, by_page = _index_plants(q_idx.float().cpu().numpy(), lens, nb, table, Hkv, P, plant, seed,
+                                     label, plant_shift)
+    pad_at = {}
+    for b in range(B):
+        n = int(lens[b])
+        if n > 0 and n % P:
+            pad_at[int(table[b, (n - 1) // P])] = n % P
+    keys = torch.empty((num_pages, P, Di), dtype=tdt, device=device)
+    for c0 in range(0, num_pages, chunk_pages):
+        c1 = min(num_pages, c0 + chunk_pages)
+        kc = _torch_normal((c1 - c0, P, Di), (seed, label, _T_KIDX, c0), device, torch)
+        for page in range(c0, c1):
+            for t, u in by_page.get(page, ()):
+                kc[page - c0, t, :] += torch.from_numpy(u).to(device)
+        for page, s in pad_at.items():
+            if c0 <= page < c1:
+                kc[page - c0, s:, :] = PAD_VALUE
+        keys[c0:c1] = kc.to(tdt)
+        del kc
+    return IndexCase(dtype=dtype, B=B, Hkv=Hkv, Di=Di, P=P, top_k=top_k,
+                     seq_lens=np.asarray(lens, dtype=np.int32), block_table=table, num_pages=num_pages,
+                     q_idx=q_idx, index_keys=keys, planted=planted, label=label, seed=seed)
 
 
 def make_prefill_case_torch(*, Hq: int, Hkv: int, past_len: int, T: int, top_k: int,

@@ -144,3 +144,33 @@ def test_prefill_errors():
     assert call(cfg(), q=None) == L.MSA_ERR_INVALID_ARG
     assert call(cfg(dtype="f32")) == L.MSA_ERR_UNSUPPORTED       # prefill is bf16 only
     assert call(cfg(), nbytes=100) == L.MSA_ERR_WORKSPACE
+
+
+def test_select_index_errors():
+    """The index branch reads only the table, lengths and page count of the cache; index_dim
+    other than 128 is unsupported; score_mode is not read."""
+    lib = L.load_library()
+    bare = fake_cache(k_pages=None, v_pages=None, summaries=None)
+
+    def call(c=None, qi=FAKE, ik=FAKE, di=128, cache=bare, B=1, max_len=1024, idx=FAKE, nbytes=1 << 30, ws=FAKE):
+        c = cfg() if c is None else c
+        return lib.msa_select_index(ctypes.byref(c), qi, ik, di, ctypes.byref(cache), B, max_len, None, idx, ws,
+                                    nbytes, None)
+    assert call(qi=None) == L.MSA_ERR_INVALID_ARG
+    assert call(ik=None) == L.MSA_ERR_INVALID_ARG
+    assert call(idx=None) == L.MSA_ERR_INVALID_ARG
+    assert call(di=0) == L.MSA_ERR_INVALID_ARG
+    assert call(di=64) == L.MSA_ERR_UNSUPPORTED
+    assert call(cache=fake_cache(seq_lens=None)) == L.MSA_ERR_INVALID_ARG
+    assert call(cache=fake_cache(block_table=None)) == L.MSA_ERR_INVALID_ARG
+    assert call(max_len=16 * 64 + 1) == L.MSA_ERR_INVALID_ARG
+    assert call(B=-1) == L.MSA_ERR_INVALID_ARG
+    assert call(nbytes=8) == L.MSA_ERR_WORKSPACE
+    assert call(ws=None) == L.MSA_ERR_WORKSPACE
+    assert call(c=cfg(top_k=0)) == L.MSA_ERR_INVALID_ARG
+    # a valid call with no sequences enqueues nothing and succeeds, in either score mode
+    assert call(B=0) == L.MSA_OK
+    assert call(B=0, c=cfg(score_mode=1)) == L.MSA_OK
+    # the config-driven select still refuses the max-token mode
+    assert lib.msa_select(ctypes.byref(cfg(score_mode=1)), FAKE, ctypes.byref(fake_cache()), 1, 1024, None, FAKE,
+                          FAKE, 1 << 30, None) == L.MSA_ERR_UNSUPPORTED
