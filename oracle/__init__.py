@@ -51,12 +51,14 @@ def _load():
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.orc_topk.argtypes = [P, I, I, P]
         lib.orc_topk.restype = I
-        lib.orc_decode.argtypes = [I, I, I, I, I, I, D, I, P, P, P, I, P, I, P, P, P, P, P, P, P, P, I]
+        lib.orc_topk_forced.argtypes = [P, I, I, I, I, P]
+        lib.orc_topk_forced.restype = I
+        lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, D, I, P, P, P, I, P, I, P, P, P, P, P, P, P, P, I]
         lib.orc_decode.restype = I
         lib.orc_summaries.argtypes = [I, I, I, I, I, P, I, P, I, P, P]
         lib.orc_summaries.restype = I
-        lib.orc_prefill.argtypes = [I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
-        lib.orc_select_index.argtypes = [I, I, I, I, I, I, P, P, I, P, I, P, P, P]
+        lib.orc_prefill.argtypes = [I, I, I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
+        lib.orc_select_index.argtypes = [I, I, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
         lib.orc_select_index.restype = I
         lib.orc_prefill.restype = I
         _lib = lib
@@ -83,11 +85,15 @@ def default_threads() -> int:
     return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
 
 
-def topk(scores: np.ndarray, k: int) -> np.ndarray:
-    """k_eff = min(k, n) block indices by (score desc, index asc), ascending, padded with -1."""
+def topk(scores: np.ndarray, k: int, keep_sink: int = 0, keep_local: int = 0) -> np.ndarray:
+    """k_eff = min(k, n) block indices by (score desc, index asc), ascending, padded with -1.
+    keep_sink / keep_local (reading R9): the first / last blocks that are always kept."""
     s = _c(scores, np.float64)
     out = np.empty(k, dtype=np.int32)
-    rc = _load().orc_topk(_ptr(s), int(s.shape[0]), int(k), _ptr(out))
+    if keep_sink or keep_local:
+        rc = _load().orc_topk_forced(_ptr(s), int(s.shape[0]), int(k), int(keep_sink), int(keep_local), _ptr(out))
+    else:
+        rc = _load().orc_topk(_ptr(s), int(s.shape[0]), int(k), _ptr(out))
     if rc < 0:
         raise RuntimeError("orc_topk failed")
     return out
@@ -107,7 +113,8 @@ def summaries(*, k_pool, block_table, seq_lens, Hkv: int, D: int, P: int) -> np.
     return out
 
 
-def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int = 64) -> dict:
+def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int = 64, keep_sink: int = 0,
+                 keep_local: int = 0) -> dict:
     """The index branch of [MGS §1 Step 1] (reading R8): token scores of each group's index query
     against the single-head index keys, Block Max Pool, TopK. q_idx [B][Hkv][Di] and
     index_keys [num_pages][P][Di] share one storage dtype (float32, or bf16 bits as uint16).
@@ -122,7 +129,7 @@ def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int
     mb = table.shape[1]
     scores = np.empty((B, Hkv, mb), dtype=np.float64)
     idx = np.empty((B, Hkv, top_k), dtype=np.int32)
-    rc = _load().orc_select_index(B, Hkv, Di, P, top_k, _dtype_code(qi), _ptr(qi), _ptr(ik), int(ik.shape[0]),
+    rc = _load().orc_select_index(B, Hkv, Di, P, top_k, int(keep_sink), int(keep_local), _dtype_code(qi), _ptr(qi), _ptr(ik), int(ik.shape[0]),
                                   _ptr(table), mb, _ptr(lens), _ptr(scores), _ptr(idx))
     if rc != 0:
         raise RuntimeError("orc_select_index failed (%d)" % rc)
@@ -132,7 +139,7 @@ def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int
 def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k: int,
            scale: float, P: int = 64, summaries_in: Optional[np.ndarray] = None,
            idx_in: Optional[np.ndarray] = None, want_weights: bool = False,
-           nthreads: Optional[int] = None) -> dict:
+           nthreads: Optional[int] = None, keep_sink: int = 0, keep_local: int = 0) -> dict:
     """Decode step over B sequences. Returns scores [B][Hkv][max_blocks], idx [B][Hkv][top_k],
     o [B][Hq][D], lse [B][Hq] (fp64) and, if asked, w [B][Hq][top_k*P]."""
     q, k_pool, v_pool = _c(q), _c(k_pool), _c(v_pool)
@@ -149,7 +156,7 @@ def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k
     w = np.empty((B, Hq, top_k * P), dtype=np.float64) if want_weights else None
     s_in = None if summaries_in is None else _c(summaries_in, np.float64)
     i_in = None if idx_in is None else _c(idx_in, np.int32)
-    rc = _load().orc_decode(B, Hq, Hkv, D, P, top_k, float(scale), dt, _ptr(q), _ptr(k_pool),
+    rc = _load().orc_decode(B, Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), float(scale), dt, _ptr(q), _ptr(k_pool),
                             _ptr(v_pool), int(k_pool.shape[0]), _ptr(table), mb, _ptr(lens),
                             _ptr(s_in), _ptr(i_in), _ptr(scores), _ptr(idx), _ptr(o), _ptr(lse),
                             _ptr(w), int(nthreads or default_threads()))
@@ -163,7 +170,8 @@ def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k
 
 def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: int, Hkv: int,
             top_k: int, scale: float, P: int = 64, tiles: Optional[tuple] = None,
-            idx_in: Optional[np.ndarray] = None, nthreads: Optional[int] = None) -> dict:
+            idx_in: Optional[np.ndarray] = None, nthreads: Optional[int] = None, keep_sink: int = 0,
+            keep_local: int = 0) -> dict:
     """Prefill chunk of T tokens on one sequence. Returns scores [ntiles][Hkv][max_blocks],
     idx [ntiles][Hkv][top_k+1], o [T][Hq][D], lse [T][Hq]; only tiles [lo, hi) are computed
     (rows of other tiles are NaN). idx_in ([ntiles][Hkv][top_k+1]) replaces the selection."""
@@ -178,7 +186,7 @@ def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: 
     idx = np.full((ntiles, Hkv, top_k + 1), -2, dtype=np.int32)
     o = np.full((T, Hq, D), np.nan)
     lse = np.full((T, Hq), np.nan)
-    rc = _load().orc_prefill(Hq, Hkv, D, P, top_k, float(scale), dt, _ptr(q), _ptr(k_new),
+    rc = _load().orc_prefill(Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), float(scale), dt, _ptr(q), _ptr(k_new),
                              _ptr(v_new), _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
                              _ptr(table), mb, int(past_len), int(T), int(lo), int(hi),
                              _ptr(None if idx_in is None else _c(idx_in, np.int32)),

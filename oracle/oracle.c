@@ -39,6 +39,12 @@
  *                        K); one index query per group (given); token score <q_idx[g], K_idx[t]>,
  *                        unscaled; a block's score is the maximum of its valid tokens' scores
  *                        ("Block Max Pool"); then TopK as R3.
+ *   R9 forced blocks   = optional, off by default: the first `sink` and the last `local` of a
+ *                        row's n candidates are always kept (decode: of the sequence's blocks;
+ *                        prefill: of the blocks before the diagonal) and count toward k_eff;
+ *                        the other k_eff - |F| come from the remaining candidates under R3.
+ *                        The page guesses that an attention sink plus a local block replaced
+ *                        NSA's sliding window ([MGS §2], "third subtraction").
  *
  * All arithmetic is fp64 on exact upcasts of the stored inputs (f32 or bf16 bit patterns).
  * Layouts: q [B][Hq][D]; K/V pools [num_pages][Hkv][P][D]; block_table [B][max_blocks].
@@ -93,9 +99,33 @@ int orc_topk(const double* s, int n, int k, int32_t* out) {
     return keff;
 }
 
+/* R9: forced set F = {j < sink} U {j >= n - local} (of the n candidates), then the best
+ * k_eff - |F| of the others under R3; the union in ascending order, padded with -1 to k.
+ * Needs sink + local <= k, so that F fits in k_eff = min(k, n). Returns k_eff, or -1. */
+int orc_topk_forced(const double* s, int n, int k, int sink, int local, int32_t* out) {
+    if (n < 0 || k < 0 || sink < 0 || local < 0 || sink + local > k) return -1;
+    int keff = n < k ? n : k;
+    char* forced = (char*)calloc((size_t)(n > 0 ? n : 1), 1);
+    scored_t* rest = (scored_t*)malloc(sizeof(scored_t) * (size_t)(n > 0 ? n : 1));
+    if (!forced || !rest) { free(forced); free(rest); return -1; }
+    int nf = 0, m = 0;
+    for (int j = 0; j < n; ++j) {
+        forced[j] = (char)(j < sink || j >= n - local);
+        if (forced[j]) out[nf++] = j;
+        else { rest[m].s = s[j]; rest[m].j = j; ++m; }
+    }
+    qsort(rest, (size_t)m, sizeof(scored_t), by_score_then_index);
+    for (int i = 0; i < keff - nf; ++i) out[nf + i] = rest[i].j;
+    qsort(out, (size_t)keff, sizeof(int32_t), ascending_i32);
+    for (int i = keff; i < k; ++i) out[i] = -1;
+    free(forced);
+    free(rest);
+    return keff;
+}
+
 /* ------------------------------------------------------------------ decode */
 typedef struct {
-    int B, Hq, Hkv, D, P, top_k, dtype, num_pages, max_blocks;
+    int B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks;
     double scale;
     const void *q, *k_pool, *v_pool;
     const int32_t *block_table, *seq_lens, *idx_in;
@@ -165,7 +195,7 @@ static int decode_unit(const decode_args* a, int b, int g) {
     /* [MGS §1 Step 1] TopK, or an index list supplied by the caller */
     if (a->idx_in) {
         memcpy(sel, a->idx_in + ((size_t)b * a->Hkv + g) * K, sizeof(int32_t) * (size_t)K);
-    } else if (orc_topk(s, nb, K, sel) < 0) { rc = -3; goto done; }
+    } else if (orc_topk_forced(s, nb, K, a->keep_sink, a->keep_local, sel) < 0) { rc = -3; goto done; }
     if (a->idx_out) memcpy(a->idx_out + ((size_t)b * a->Hkv + g) * K, sel, sizeof(int32_t) * (size_t)K);
 
     /* [MGS §1 Step 2] every head of the group attends over the selected blocks' real K/V */
@@ -258,7 +288,8 @@ static int run_threads(void* (*fn)(void*), void* jobs, size_t job_size, int nthr
  * o_out [B][Hq][D], lse_out [B][Hq], w_out (nullable) [B][Hq][top_k*P] weights of the attended
  * tokens in ascending token order, zero-padded.
  * Returns 0, or a negative code (bad argument, page id out of range, allocation failure). */
-int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, double scale, int dtype,
+int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int keep_local,
+               double scale, int dtype,
                const void* q, const void* k_pool, const void* v_pool, int num_pages,
                const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
                const double* summaries, const int32_t* idx_in, double* scores_out,
@@ -266,7 +297,8 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, double scale, in
     if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P < 1 || top_k < 1 || !q || !k_pool ||
         !v_pool || !block_table || !seq_lens || !o_out || !lse_out || (dtype != ORC_F32 && dtype != ORC_BF16))
         return -1;
-    decode_args a = {B, Hq, Hkv, D, P, top_k, dtype, num_pages, max_blocks, scale, q, k_pool,
+    if (keep_sink < 0 || keep_local < 0 || keep_sink + keep_local > top_k) return -1;
+    decode_args a = {B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, scale, q, k_pool,
                      v_pool, block_table, seq_lens, idx_in, summaries, scores_out, o_out,
                      lse_out, w_out, idx_out, 0};
     if (nthreads < 1) nthreads = 1;
@@ -300,7 +332,8 @@ int orc_summaries(int B, int Hkv, int D, int P, int dtype, const void* k_pool, i
 
 /* ------------------------------------------------------------------ prefill (R6) */
 typedef struct {
-    int Hq, Hkv, D, P, top_k, dtype, num_pages, max_blocks, past_len, T, tile_lo, tile_hi;
+    int Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, past_len, T, tile_lo,
+        tile_hi;
     double scale;
     const void *q, *k_new, *v_new, *k_pool, *v_pool;
     const int32_t* table;        /* one sequence: [max_blocks] */
@@ -354,7 +387,7 @@ static int prefill_unit(const prefill_args* a, int tau, int g) {
         double* row = a->scores_out + ((size_t)tau * a->Hkv + g) * a->max_blocks;
         for (int j = 0; j < a->max_blocks; ++j) row[j] = j < diag ? s[j] : -INFINITY;
     }
-    int keff = orc_topk(s, diag, K, sel);
+    int keff = orc_topk_forced(s, diag, K, a->keep_sink, a->keep_local, sel);
     if (keff < 0) { rc = -3; goto done; }
     sel[keff] = diag;                                  /* the diagonal block is always kept */
     for (int e = keff + 1; e <= K; ++e) sel[e] = -1;
@@ -440,8 +473,8 @@ static void* prefill_worker(void* p) {
  * idx_in (nullable) [ntiles][Hkv][top_k+1]: lists to attend over instead of the selection.
  * scores_out (nullable) [ntiles][Hkv][max_blocks]; idx_out (nullable) [ntiles][Hkv][top_k+1];
  * o_out [T][Hq][D] and lse_out [T][Hq] (rows of the computed tiles are written). */
-int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtype,
-                const void* q, const void* k_new, const void* v_new, const void* k_pool,
+int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int keep_local, double scale,
+                int dtype, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                 const void* v_pool, int num_pages, const int32_t* table, int max_blocks,
                 int past_len, int T, int tile_lo, int tile_hi, const int32_t* idx_in,
                 double* scores_out, int32_t* idx_out, double* o_out, double* lse_out, int nthreads) {
@@ -449,12 +482,13 @@ int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtyp
     if (Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P < 1 || top_k < 0 || T < 1 || past_len < 0 ||
         past_len % P || !q || !k_new || !v_new || !k_pool || !v_pool || !table || !o_out ||
         !lse_out || tile_lo < 0 || tile_hi > ntiles || tile_lo > tile_hi ||
-        past_len / P + ntiles > max_blocks || (dtype != ORC_F32 && dtype != ORC_BF16))
+        past_len / P + ntiles > max_blocks || (dtype != ORC_F32 && dtype != ORC_BF16) ||
+        keep_sink < 0 || keep_local < 0 || keep_sink + keep_local > top_k)
         return -1;
     int nblocks = past_len / P + ntiles;
     double* S = (double*)malloc(sizeof(double) * (size_t)nblocks * Hkv * D);
     if (!S) return -3;
-    prefill_args a = {Hq, Hkv, D, P, top_k, dtype, num_pages, max_blocks, past_len, T, tile_lo,
+    prefill_args a = {Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, past_len, T, tile_lo,
                       tile_hi, scale, q, k_new, v_new, k_pool, v_pool, table, idx_in, S,
                       scores_out, o_out, lse_out, idx_out, 0};
     if (nthreads < 1) nthreads = 1;
@@ -475,11 +509,12 @@ int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, double scale, int dtyp
  * q_idx [B][Hkv][Di]; ikeys [num_pages][P][Di] (one head), pages through block_table.
  * scores_out (nullable) [B][Hkv][max_blocks] (-inf past the blocks, or for a bad page id);
  * idx_out [B][Hkv][top_k]. Returns 0 on success. */
-int orc_select_index(int B, int Hkv, int Di, int P, int top_k, int dtype, const void* q_idx,
-                     const void* ikeys, int num_pages, const int32_t* table, int max_blocks,
+int orc_select_index(int B, int Hkv, int Di, int P, int top_k, int keep_sink, int keep_local, int dtype,
+                     const void* q_idx, const void* ikeys, int num_pages, const int32_t* table, int max_blocks,
                      const int32_t* seq_lens, double* scores_out, int32_t* idx_out) {
     if (B < 0 || Hkv < 1 || Di < 1 || P < 1 || top_k < 0 || !q_idx || !ikeys || !table || !seq_lens ||
-        !idx_out || (dtype != ORC_F32 && dtype != ORC_BF16))
+        !idx_out || (dtype != ORC_F32 && dtype != ORC_BF16) || keep_sink < 0 || keep_local < 0 ||
+        keep_sink + keep_local > top_k)
         return -1;
     double* row = (double*)malloc(sizeof(double) * (size_t)(max_blocks > 0 ? max_blocks : 1));
     if (!row) return -3;
@@ -507,7 +542,10 @@ int orc_select_index(int B, int Hkv, int Di, int P, int top_k, int dtype, const 
                 double* srow = scores_out + ((size_t)b * Hkv + g) * max_blocks;
                 for (int j = 0; j < max_blocks; ++j) srow[j] = j < nb ? row[j] : -INFINITY;
             }
-            if (orc_topk(row, nb, top_k, idx_out + ((size_t)b * Hkv + g) * top_k) < 0) { free(row); return -3; }
+            if (orc_topk_forced(row, nb, top_k, keep_sink, keep_local, idx_out + ((size_t)b * Hkv + g) * top_k) < 0) {
+                free(row);
+                return -3;
+            }
         }
     }
     free(row);

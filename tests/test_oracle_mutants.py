@@ -44,6 +44,17 @@ MUTANTS = [
      "elem(q_idx, dtype, ((size_t)b * Hkv + 0) * Di + d)", False),
     ("index_key_first_token_only", "elem(ikeys, dtype, ((size_t)page * P + t) * Di + d)",
      "elem(ikeys, dtype, ((size_t)page * P + 0) * Di + d)", False),
+    ("forced_local_off_by_one", "forced[j] = (char)(j < sink || j >= n - local);",
+     "forced[j] = (char)(j < sink || j > n - local);", False),
+    ("forced_sink_ignored", "forced[j] = (char)(j < sink || j >= n - local);",
+     "forced[j] = (char)(j < 0 || j >= n - local);", False),
+    ("forced_rest_in_index_order", "qsort(rest, (size_t)m, sizeof(scored_t), by_score_then_index);", "", False),
+    ("decode_forced_dropped", "orc_topk_forced(s, nb, K, a->keep_sink, a->keep_local, sel)",
+     "orc_topk_forced(s, nb, K, 0, 0, sel)", False),
+    ("index_forced_dropped", "orc_topk_forced(row, nb, top_k, keep_sink, keep_local,",
+     "orc_topk_forced(row, nb, top_k, 0, 0,", False),
+    ("prefill_forced_dropped", "orc_topk_forced(s, diag, K, a->keep_sink, a->keep_local, sel)",
+     "orc_topk_forced(s, diag, K, 0, 0, sel)", False),
 ]
 
 

@@ -435,3 +435,147 @@ def test_index_planted_token_and_bad_page():
     assert np.argmax(r["scores"][0, 0]) == 5
     assert r["scores"][0, 0, 2] == -np.inf and r["scores"][0, 1, 2] == -np.inf
     assert 2 not in r["idx"][0, 0] and 2 not in r["idx"][0, 1]
+
+
+# ----------------------------------------------------------------------------- forced blocks (R9)
+# Optional sink / local blocks: the first keep_sink and the last keep_local candidates are always
+# kept and count toward k_eff; the rest of the list is the usual top-k of the other candidates.
+def _brute_force_forced(s, k, sink, local):
+    """The unique k_eff-subset S that holds F = {j < sink} U {j >= n - local} and where every
+    i in S \\ F beats every candidate j outside S: s_i > s_j, or s_i == s_j and i < j."""
+    n = len(s)
+    keff = min(k, n)
+    F = {j for j in range(n) if j < sink or j >= n - local}
+    winners = []
+    for S in itertools.combinations(range(n), keff):
+        inside = set(S)
+        if not F <= inside:
+            continue
+        if all((s[i] > s[j]) or (s[i] == s[j] and i < j)
+               for i in inside - F for j in range(n) if j not in inside):
+            winners.append(list(S))
+    assert len(winners) == 1
+    return winners[0] + [-1] * (k - keff)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_forced_topk_brute_force(seed):
+    r = np.random.default_rng(500 + seed)
+    n = int(r.integers(1, 12))
+    sink, local = int(r.integers(0, 3)), int(r.integers(0, 3))
+    k = sink + local + int(r.integers(0, 4))
+    if k == 0:
+        k = 1
+    s = r.integers(-3, 4, size=n).astype(np.float64)   # frequent ties
+    got = oracle.topk(s, k, keep_sink=sink, keep_local=local)
+    assert list(got) == _brute_force_forced(list(s), k, sink, local), (n, k, sink, local)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_forced_topk_equals_plain_topk_with_forced_scores_raised(seed):
+    """Raising the forced blocks' scores above every other score (they tie among themselves, so
+    the index order keeps them all) and taking the plain top-k gives the same list."""
+    r = np.random.default_rng(600 + seed)
+    n = int(r.integers(20, 3000))
+    sink, local = int(r.integers(0, 4)), int(r.integers(0, 4))
+    k = sink + local + int(r.integers(0, 100))
+    k = max(k, 1)
+    s = np.round(r.standard_normal(n), 2)
+    raised = s.copy()
+    raised[:sink] = np.inf
+    raised[max(0, n - local):] = np.inf
+    np.testing.assert_array_equal(oracle.topk(s, k, keep_sink=sink, keep_local=local), oracle.topk(raised, k))
+
+
+def test_forced_topk_special_cases():
+    s = np.array([9.0, 1.0, 8.0, 7.0, 0.5, 2.0])
+    np.testing.assert_array_equal(oracle.topk(s, 2, keep_sink=1, keep_local=1), [0, 5])   # exactly F
+    np.testing.assert_array_equal(oracle.topk(s, 3, keep_sink=1, keep_local=1), [0, 2, 5])  # + best other
+    np.testing.assert_array_equal(oracle.topk(s, 3, keep_local=2), [0, 4, 5])
+    np.testing.assert_array_equal(oracle.topk(s, 9, keep_sink=2, keep_local=2), [0, 1, 2, 3, 4, 5, -1, -1, -1])
+    np.testing.assert_array_equal(oracle.topk(s[:1], 2, keep_sink=1, keep_local=1), [0, -1])  # F overlaps
+    with pytest.raises(RuntimeError):
+        oracle.topk(s, 1, keep_sink=1, keep_local=1)                  # F does not fit in k
+
+
+def test_decode_forced_local_block_is_local_attention():
+    """k = 1 with the last block forced: every head attends exactly the last (partial) block."""
+    c = make_decode_case(B=2, Hq=4, Hkv=2, lens=[1000, 130], top_k=1, dtype="f32", seed=31, permute=True)
+    r = oracle.decode(keep_local=1, **decode_inputs(c))
+    G = 2
+    for b in range(c.B):
+        N = int(c.seq_lens[b])
+        nb = (N + 63) // 64
+        K = logical_kv(c.k_pool, c.block_table, b, N).astype(np.float64)
+        V = logical_kv(c.v_pool, c.block_table, b, N).astype(np.float64)
+        mask = np.arange(N) >= (nb - 1) * 64
+        for g in range(c.Hkv):
+            assert list(r["idx"][b, g]) == [nb - 1]
+            o, lse = dense_gqa(c.q[b, g * G:(g + 1) * G].astype(np.float64), K[:, g:g + 1], V[:, g:g + 1], c.scale,
+                               mask=mask)
+            np.testing.assert_allclose(r["o"][b, g * G:(g + 1) * G], o, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(r["lse"][b, g * G:(g + 1) * G], lse, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_forced_blocks_join_the_selection():
+    """sink + local forced, k = 5: the list is {0, nb-1} plus the plain top-3 of the other blocks'
+    scores (the scores themselves do not change)."""
+    c = make_decode_case(B=1, Hq=8, Hkv=2, lens=[3000], top_k=5, dtype="bf16", seed=32, plant=("count", 3))
+    kw = decode_inputs(c)
+    plain = oracle.decode(**kw)
+    r = oracle.decode(keep_sink=1, keep_local=1, **kw)
+    np.testing.assert_array_equal(r["scores"], plain["scores"])
+    nb = (3000 + 63) // 64
+    for g in range(c.Hkv):
+        s = plain["scores"][0, g, :nb]
+        others = oracle.topk(s[1:nb - 1], 3) + 1
+        assert list(r["idx"][0, g]) == sorted([0, nb - 1] + list(others))
+
+
+def test_prefill_forced_sink_block():
+    """k = 1 with block 0 forced: each tile with cached blocks attends block 0 plus its diagonal
+    block (causal); the first tile of a chunk starting at 0 has no candidate, so only its diagonal."""
+    c = make_prefill_case(Hq=4, Hkv=1, past_len=256, T=130, top_k=1, dtype="f32", seed=33)
+    r = oracle.prefill(keep_sink=1, **prefill_inputs(c))
+    K = np.concatenate([logical_kv(c.k_pool, c.block_table, 0, 256), c.k_new]).astype(np.float64)
+    V = np.concatenate([logical_kv(c.v_pool, c.block_table, 0, 256), c.v_new]).astype(np.float64)
+    for tau in range(3):
+        rows = np.arange(tau * 64, min(130, tau * 64 + 64))
+        d = 4 + tau
+        assert list(r["idx"][tau, 0]) == [0, d]
+        pos = 256 + rows
+        t = np.arange(K.shape[0])
+        mask = ((t[None, :] < 64) | (t[None, :] >= d * 64)) & (t[None, :] <= pos[:, None])
+        o, lse = dense_gqa(c.q[rows].astype(np.float64), K, V, c.scale, mask=mask)
+        np.testing.assert_allclose(r["o"][rows], o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][rows], lse, rtol=1e-12, atol=1e-12)
+    c0 = make_prefill_case(Hq=4, Hkv=1, past_len=0, T=100, top_k=1, dtype="f32", seed=34)
+    r0 = oracle.prefill(keep_sink=1, **prefill_inputs(c0))
+    assert list(r0["idx"][0, 0]) == [0, -1] and list(r0["idx"][1, 0]) == [0, 1]
+
+
+def test_prefill_forced_local_block():
+    """keep_local = 1: the block just before each tile's diagonal is kept."""
+    c = make_prefill_case(Hq=8, Hkv=2, past_len=640, T=200, top_k=3, dtype="bf16", seed=35)
+    kw = prefill_inputs(c)
+    plain = oracle.prefill(**kw)
+    r = oracle.prefill(keep_local=1, **kw)
+    for tau in range(4):
+        d = 10 + tau
+        for g in range(2):
+            s = plain["scores"][tau, g, :d]
+            want = sorted(list(oracle.topk(s[:d - 1], 2)) + [d - 1])
+            assert list(r["idx"][tau, g]) == want + [d]
+
+
+def test_index_branch_forced_blocks():
+    q, ik, table, lens = _index_case()
+    kw = dict(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens)
+    plain = oracle.select_index(top_k=3, **kw)
+    r = oracle.select_index(top_k=3, keep_sink=1, keep_local=1, **kw)
+    for b in range(len(lens)):
+        nb = (int(lens[b]) + 63) // 64
+        for g in range(r["idx"].shape[1]):
+            want = oracle.topk(plain["scores"][b, g, :nb], 3, keep_sink=1, keep_local=1)
+            np.testing.assert_array_equal(r["idx"][b, g], want)
+            assert 0 in r["idx"][b, g] and nb - 1 in r["idx"][b, g]
