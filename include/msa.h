@@ -20,6 +20,12 @@
  *   - decode: all seq_lens[b] cached tokens are visible (the cache already holds the current
  *     token); prefill: candidates are the blocks strictly before a tile's diagonal block, the
  *     diagonal block is always appended, and key position <= query position inside it;
+ *   - forced blocks ([MGS §2], third subtraction: the page guesses that an attention sink and a
+ *     local block replaced the sliding window): off by default. With keep_sink = s and
+ *     keep_local = l, candidates j < s and j >= n - l of a row's n candidates (decode: the
+ *     sequence's blocks; prefill: the blocks before the diagonal) are always kept and count
+ *     toward k_eff; the remaining k_eff - |forced| are chosen by the order above among the
+ *     other candidates. s, l >= 0 and s + l <= top_k, else MSA_ERR_INVALID_ARG;
  *   - softmax: logits = softmax_scale * <q_h, k_t>, fp32 accumulation, lse in natural log.
  *
  * Conventions for every entry point
@@ -92,8 +98,9 @@ typedef struct msa_config {
     int32_t kv_dtype;         /* msa_dtype of the K/V pools; must equal q_dtype */
     int32_t out_dtype;        /* msa_dtype of out; must equal q_dtype */
     int32_t score_mode;       /* msa_score_mode; MEAN_KEY */
-    int32_t keep_local;       /* decode: force the last block; must be 0 */
+    int32_t keep_local;       /* forced local blocks: the last keep_local candidates are always kept */
     int32_t q_tile;           /* prefill selection tile in query rows; must be 64 */
+    int32_t keep_sink;        /* forced sink blocks: the first keep_sink candidates are always kept */
 } msa_config;
 
 typedef struct msa_kv_cache {

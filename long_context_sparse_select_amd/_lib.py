@@ -25,7 +25,8 @@ class MsaConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("score_mode", ctypes.c_int32),
-                ("keep_local", ctypes.c_int32), ("q_tile", ctypes.c_int32)]
+                ("keep_local", ctypes.c_int32), ("q_tile", ctypes.c_int32),
+                ("keep_sink", ctypes.c_int32)]
 
 
 class MsaKvCache(ctypes.Structure):
@@ -81,11 +82,11 @@ def msa_status_string(status: int) -> str:
 def make_config(num_q_heads: int, num_kv_heads: int, top_k: int, dtype: str = "bf16",
                 softmax_scale: Optional[float] = None, head_dim: int = 128, block_size: int = 64,
                 score_mode: int = MSA_SCORE_MEAN_KEY, keep_local: int = 0,
-                q_tile: int = 64) -> MsaConfig:
+                q_tile: int = 64, keep_sink: int = 0) -> MsaConfig:
     dt = {"f32": MSA_F32, "bf16": MSA_BF16}[dtype]
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
     return MsaConfig(num_q_heads, num_kv_heads, head_dim, block_size, top_k, scale, dt, dt, dt,
-                     score_mode, keep_local, q_tile)
+                     score_mode, keep_local, q_tile, keep_sink)
 
 
 @dataclasses.dataclass

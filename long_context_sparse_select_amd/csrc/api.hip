@@ -35,6 +35,8 @@ msa_status check_config(const msa_config* c, bool any_mode = false) {
   if (c == nullptr) return MSA_ERR_INVALID_ARG;
   if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->num_q_heads % c->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (c->top_k < 1) return MSA_ERR_INVALID_ARG;
+  if (c->keep_sink < 0 || c->keep_local < 0 || (long long)c->keep_sink + c->keep_local > c->top_k)
+    return MSA_ERR_INVALID_ARG;
   if (c->q_dtype != MSA_F32 && c->q_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->kv_dtype != MSA_F32 && c->kv_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->out_dtype != MSA_F32 && c->out_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
@@ -46,7 +48,6 @@ msa_status check_config(const msa_config* c, bool any_mode = false) {
   if (c->num_kv_heads > MSA_MAX_KV_HEADS) return MSA_ERR_UNSUPPORTED;
   if (c->kv_dtype != c->q_dtype || c->out_dtype != c->q_dtype) return MSA_ERR_UNSUPPORTED;
   if (c->score_mode != MSA_SCORE_MEAN_KEY && !any_mode) return MSA_ERR_UNSUPPORTED;
-  if (c->keep_local != 0) return MSA_ERR_UNSUPPORTED;
   if (c->q_tile != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
@@ -136,6 +137,8 @@ msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* ca
   t.lens = cache->seq_lens;
   t.max_len = max_len;
   t.base_blocks = 0;
+  t.keep_sink = cfg->keep_sink;
+  t.keep_local = cfg->keep_local;
   t.pages = pages;
   t.table = cache->block_table;
   t.max_blocks = cache->max_blocks;
@@ -340,6 +343,8 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   t.lens = nullptr;
   t.max_len = max_len;
   t.base_blocks = past_blocks;
+  t.keep_sink = cfg->keep_sink;
+  t.keep_local = cfg->keep_local;
   t.k_new = nullptr;   // TopkArgs{} zero-initialises the decode-only fields; no append in prefill
   MSA_TRY(hip_status(launch_topk(t, true, st)));
   PrefillArgs p{};

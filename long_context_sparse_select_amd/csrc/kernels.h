@@ -45,6 +45,10 @@ struct TopkArgs {
   const int32_t* lens; // decode: n = ceil(clamp(lens[row / Hkv]) / 64); null -> prefill mode
   int max_len;
   int base_blocks;     // prefill: n = base_blocks + row / Hkv, and block n is appended
+  // forced blocks: candidates j < keep_sink or j >= n - keep_local are always kept (counted in
+  // k_eff; keep_sink + keep_local <= k)
+  int keep_sink;
+  int keep_local;
   // decode only (nullable): page ids of the kept blocks [rows][k] (-1 for padding or a bad page
   // id), translated through table [B][max_blocks]
   int32_t* pages;

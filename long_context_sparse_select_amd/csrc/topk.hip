@@ -131,6 +131,14 @@ struct TopkShared {
   int bstar;
 };
 
+// A forced block's key sits above every order key (even a NaN's), so every selection path keeps
+// it; forced blocks tie among themselves and fit in k_eff, so all of them are kept.
+constexpr uint32_t kForcedKey = 0xffffffffu;
+
+__device__ __forceinline__ uint32_t select_key(const TopkArgs& a, int j, int n, float s) {
+  return (j < a.keep_sink || j >= n - a.keep_local) ? kForcedKey : order_key(s);
+}
+
 __device__ __forceinline__ int page_of(const TopkArgs& a, int row, int j) {
   const int p = a.table[(long long)(row / a.Hkv) * a.max_blocks + j];
   return page_ok(p, a.num_pages) ? p : -1;
@@ -154,7 +162,7 @@ template <int NT>
 __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, int jlast,
                                 float fresh, TopkShared& sh) {
   const int tid = threadIdx.x;
-  auto key_of = [&](int j) { return order_key(j == jlast ? fresh : srow[j]); };
+  auto key_of = [&](int j) { return select_key(a, j, n, j == jlast ? fresh : srow[j]); };
   uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
@@ -444,7 +452,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int j = tid + NT * i;
-        key[i] = j < n ? order_key(j == jlast ? fresh : v[i]) : 0u;
+        key[i] = j < n ? select_key(a, j, n, j == jlast ? fresh : v[i]) : 0u;
       }
       select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);
     } else {
@@ -462,7 +470,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = tid + NT * i;
-    key[i] = (j < n && j != jlast) ? order_key(v[i]) : 0u;
+    key[i] = (j < n && j != jlast) ? select_key(a, j, n, v[i]) : 0u;
     cm = max(cm, key[i]);
   }
   const bool has = tid < ngroups;
@@ -508,7 +516,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   float fresh = 0.f;
   if (do_append) {
     fresh = ap.fresh(sh);
-    if (jlast % NT == tid) key[jlast / NT] = order_key(fresh);
+    if (jlast % NT == tid) key[jlast / NT] = select_key(a, jlast, n, fresh);
   }
   __syncthreads();
   if (do_append && tid == 0) srow[jlast] = fresh;

@@ -90,7 +90,7 @@ def oracle_inputs(d: Dev) -> dict:
     c = d.case
     return dict(q=host_store(d.q), k_pool=host_store(d.k), v_pool=host_store(d.v),
                 block_table=c.block_table, seq_lens=c.seq_lens, Hq=c.Hq, Hkv=c.Hkv, top_k=c.top_k,
-                scale=c.scale, P=c.P)
+                scale=c.scale, P=c.P, keep_sink=int(d.cfg.keep_sink), keep_local=int(d.cfg.keep_local))
 
 
 def run_decode(d: Dev, max_len=None, k_new=None, v_new=None):
@@ -130,7 +130,27 @@ def check_scores(gpu_scores: np.ndarray, ref_scores: np.ndarray, bound: np.ndarr
     return worst
 
 
-def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k):
+def check_band(chosen, r, keff, bound_max, keep_sink=0, keep_local=0, where=""):
+    """R17 band rule on one row: the forced blocks (if any) are all chosen; among the other
+    candidates, blocks clearly above the threshold of the remaining k_eff - |F| slots are in and
+    blocks clearly below it are out."""
+    n = len(r)
+    j = np.arange(n)
+    forced = (j < keep_sink) | (j >= n - keep_local)
+    assert set(j[forced]) <= set(chosen), "forced block missing " + where
+    rest = r[~forced]
+    kr = keff - int(forced.sum())
+    if kr <= 0:
+        return
+    tau = np.sort(rest)[::-1][kr - 1]
+    w = SCORE_RTOL * max(abs(tau), bound_max)
+    must = j[~forced][rest > tau + w]
+    never = j[~forced][rest < tau - w]
+    assert set(must) <= set(chosen), "band: a clearly-in block is missing " + where
+    assert not (set(never) & set(chosen)), "band: a clearly-out block was selected " + where
+
+
+def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k, keep_sink=0, keep_local=0):
     """Exact same-precision selection plus the band rule against the fp64 scores.
     Returns a boolean array [B][Hkv]: True where the GPU set equals the oracle's."""
     B, Hkv, _ = gpu_idx.shape
@@ -140,7 +160,8 @@ def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k):
         keff = min(k, n)
         for g in range(Hkv):
             sel = gpu_idx[b, g]
-            np.testing.assert_array_equal(sel, oracle.topk(gpu_scores[b, g, :n].astype(np.float64), k))
+            np.testing.assert_array_equal(sel, oracle.topk(gpu_scores[b, g, :n].astype(np.float64), k,
+                                                           keep_sink=keep_sink, keep_local=keep_local))
             chosen = sel[:keff]
             assert np.all(sel[keff:] == -1)
             assert np.all(np.diff(chosen) > 0)
@@ -148,13 +169,8 @@ def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k):
                 same[b, g] = True
                 continue
             r = ref_scores[b, g, :n]
-            tau = np.sort(r)[::-1][keff - 1]
-            w = SCORE_RTOL * max(abs(tau), float(bound[b, g, :n].max()))
-            must = np.nonzero(r > tau + w)[0]
-            never = np.nonzero(r < tau - w)[0]
-            assert set(must) <= set(chosen), "band: a clearly-in block is missing (b=%d g=%d)" % (b, g)
-            assert not (set(never) & set(chosen)), "band: a clearly-out block was selected (b=%d g=%d)" % (b, g)
-            same[b, g] = np.array_equal(chosen, oracle.topk(r, k)[:keff])
+            check_band(chosen, r, keff, float(bound[b, g, :n].max()), keep_sink, keep_local, "(b=%d g=%d)" % (b, g))
+            same[b, g] = np.array_equal(chosen, oracle.topk(r, k, keep_sink=keep_sink, keep_local=keep_local)[:keff])
     return same
 
 
@@ -186,7 +202,8 @@ def full_decode_check(d: Dev, res: dict, S64=None):
     gpu_scores = res["scores"].cpu().numpy()
     check_scores(gpu_scores, ref["scores"][:, :, :mb], bound, nb)
     gpu_idx = res["idx"].cpu().numpy()
-    same = check_index_sets(gpu_idx, gpu_scores, ref["scores"], bound, nb, c.top_k)
+    same = check_index_sets(gpu_idx, gpu_scores, ref["scores"], bound, nb, c.top_k, inputs["keep_sink"],
+                            inputs["keep_local"])
     if not same.all():
         ref = oracle.decode(idx_in=gpu_idx, **inputs)   # stage 2 on the GPU's own selection
     assert_close(host_f64(res["o"]), ref["o"], c.dtype, "o")

@@ -75,9 +75,13 @@ def test_workspace_sizes():
     ("block_size", 128, L.MSA_ERR_UNSUPPORTED),
     ("q_dtype", 7, L.MSA_ERR_INVALID_ARG),
     ("kv_dtype", 0, L.MSA_ERR_UNSUPPORTED),            # mixed q / kv types
-    ("score_mode", 1, L.MSA_ERR_UNSUPPORTED),          # block max pool: not implemented
+    ("score_mode", 1, L.MSA_ERR_UNSUPPORTED),          # block max pool: msa_select_index only
     ("score_mode", 5, L.MSA_ERR_INVALID_ARG),
-    ("keep_local", 1, L.MSA_ERR_UNSUPPORTED),
+    ("keep_local", -1, L.MSA_ERR_INVALID_ARG),
+    ("keep_sink", -1, L.MSA_ERR_INVALID_ARG),
+    ("keep_local", 65, L.MSA_ERR_INVALID_ARG),         # forced blocks beyond top_k = 64
+    ("keep_sink", 64, L.MSA_OK),
+    ("keep_local", 64, L.MSA_OK),
     ("q_tile", 32, L.MSA_ERR_UNSUPPORTED),
     ("softmax_scale", float("nan"), L.MSA_ERR_INVALID_ARG),
     ("softmax_scale", -0.5, L.MSA_ERR_INVALID_ARG),
@@ -87,6 +91,11 @@ def test_config_validation(field, value, status):
     c = cfg()
     setattr(c, field, value)
     assert ws_size(c, L.MSA_OP_DECODE)[0] == status
+
+
+def test_forced_blocks_must_fit_in_k():
+    assert ws_size(cfg(top_k=4, keep_sink=2, keep_local=2), L.MSA_OP_DECODE)[0] == L.MSA_OK
+    assert ws_size(cfg(top_k=4, keep_sink=3, keep_local=2), L.MSA_OP_DECODE)[0] == L.MSA_ERR_INVALID_ARG
 
 
 def fake_cache(max_blocks=16, num_pages=16, **kw):

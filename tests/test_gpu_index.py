@@ -91,14 +91,15 @@ def check_index_scores(gs, ref, bound, nb):
         assert np.all(np.isneginf(gs[b, :, n:]))
 
 
-def full_check(c, gi, gs, qs, ks, table=None):
+def full_check(c, gi, gs, qs, ks, table=None, keep_sink=0, keep_local=0):
     table = c.block_table if table is None else table
-    ref = oracle.select_index(q_idx=qs, index_keys=ks, block_table=table, seq_lens=c.seq_lens, top_k=c.top_k)
+    ref = oracle.select_index(q_idx=qs, index_keys=ks, block_table=table, seq_lens=c.seq_lens, top_k=c.top_k,
+                              keep_sink=keep_sink, keep_local=keep_local)
     mb = gs.shape[2]
     nb = (c.seq_lens.astype(np.int64) + 63) // 64
     bound = token_abs_bound(qs, ks, table, c.seq_lens, c.num_pages)
     check_index_scores(gs, ref["scores"][:, :, :mb], bound[:, :, :mb], nb)
-    same = check_index_sets(gi, gs, ref["scores"], bound, nb, c.top_k)
+    same = check_index_sets(gi, gs, ref["scores"], bound, nb, c.top_k, keep_sink, keep_local)
     return ref, same
 
 

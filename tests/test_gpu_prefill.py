@@ -9,7 +9,7 @@ import torch
 import long_context_sparse_select_amd as msa
 import oracle
 from synth import bf16_bits_to_f32, make_prefill_case, make_prefill_case_torch, storage, workload
-from gpu_util import (SCORE_RTOL, assert_close, dev_tensor, host_f64, host_store, require_gpu)
+from gpu_util import (SCORE_RTOL, assert_close, check_band, dev_tensor, host_f64, host_store, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def _gpu():
     require_gpu()
 
 
-def to_dev(p):
+def to_dev(p, keep_sink=0, keep_local=0):
     if isinstance(p.q, torch.Tensor):
         q, kn, vn, k, v = p.q, p.k_new, p.v_new, p.k_pool, p.v_pool
     else:
@@ -27,7 +27,8 @@ def to_dev(p):
     table = torch.from_numpy(p.block_table).cuda()
     S = torch.full((p.num_pages, p.Hkv, p.D), float("nan"), dtype=torch.float32, device="cuda")
     lens = torch.tensor([p.past_len], dtype=torch.int32, device="cuda")
-    cfg = msa.make_config(p.Hq, p.Hkv, p.top_k, dtype=p.dtype, softmax_scale=p.scale)
+    cfg = msa.make_config(p.Hq, p.Hkv, p.top_k, dtype=p.dtype, softmax_scale=p.scale, keep_sink=keep_sink,
+                          keep_local=keep_local)
     cache = msa.KVCache(k, v, S, table, lens)
     if p.past_len:
         msa.msa_build_summaries(cfg, cache, 1, p.past_len)
@@ -67,7 +68,8 @@ def check_prefill(p, d, res, k_pool_before, v_pool_before, tiles=None):
     lo, hi = tiles if tiles is not None else (0, ntiles)
     kw = dict(q=host_store(d["q"]), k_new=host_store(d["kn"]), v_new=host_store(d["vn"]),
               k_pool=k_pool_before, v_pool=v_pool_before, block_table=p.block_table,
-              past_len=p.past_len, Hq=p.Hq, Hkv=p.Hkv, top_k=p.top_k, scale=p.scale, P=p.P)
+              past_len=p.past_len, Hq=p.Hq, Hkv=p.Hkv, top_k=p.top_k, scale=p.scale, P=p.P,
+              keep_sink=int(d["cfg"].keep_sink), keep_local=int(d["cfg"].keep_local))
     ref = oracle.prefill(tiles=(lo, hi), **kw)
     G = p.Hq // p.Hkv
     q64 = host_f64(d["q"])
@@ -86,14 +88,12 @@ def check_prefill(p, d, res, k_pool_before, v_pool_before, tiles=None):
             assert np.all(np.abs(g_s - r_s) <= tol), "prefill score mismatch tau=%d g=%d" % (tau, g)
             assert np.all(np.isneginf(res["scores"][tau, g, n:]))
             sel = res["idx"][tau, g]
-            want = oracle.topk(g_s, p.top_k)
+            want = oracle.topk(g_s, p.top_k, keep_sink=kw["keep_sink"], keep_local=kw["keep_local"])
             np.testing.assert_array_equal(sel[:keff], want[:keff])
             assert sel[keff] == n and np.all(sel[keff + 1:] == -1)
             if keff:
-                t_k = np.sort(r_s)[::-1][keff - 1]
-                w = SCORE_RTOL * max(abs(t_k), float(bound.max()))
-                assert set(np.nonzero(r_s > t_k + w)[0]) <= set(sel[:keff])
-                assert not (set(np.nonzero(r_s < t_k - w)[0]) & set(sel[:keff]))
+                check_band(sel[:keff], r_s, keff, float(bound.max()), kw["keep_sink"], kw["keep_local"],
+                           "(tau=%d g=%d)" % (tau, g))
             same_all &= bool(np.array_equal(sel, ref["idx"][tau, g]))
     if not same_all:
         ref = oracle.prefill(tiles=(lo, hi), idx_in=res["idx"], **kw)
