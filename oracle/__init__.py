@@ -53,11 +53,11 @@ def _load():
         lib.orc_topk.restype = I
         lib.orc_topk_forced.argtypes = [P, I, I, I, I, P]
         lib.orc_topk_forced.restype = I
-        lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, D, I, P, P, P, I, P, I, P, P, P, P, P, P, P, P, I]
+        lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, I, D, I, P, P, P, I, P, I, P, P, P, P, P, P, P, P, I]
         lib.orc_decode.restype = I
-        lib.orc_summaries.argtypes = [I, I, I, I, I, P, I, P, I, P, P]
+        lib.orc_summaries.argtypes = [I, I, I, I, I, I, P, I, P, I, P, P]
         lib.orc_summaries.restype = I
-        lib.orc_prefill.argtypes = [I, I, I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
+        lib.orc_prefill.argtypes = [I, I, I, I, I, I, I, I, D, I, P, P, P, P, P, I, P, I, I, I, I, I, P, P, P, P, P, I]
         lib.orc_select_index.argtypes = [I, I, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
         lib.orc_select_index.restype = I
         lib.orc_prefill.restype = I
@@ -81,6 +81,10 @@ def _c(a, dt=None):
     return np.ascontiguousarray(a if dt is None else np.asarray(a, dtype=dt))
 
 
+def _summary_flag(summary_dtype: str) -> int:
+    return {"f32": 0, "bf16": 1}[summary_dtype]
+
+
 def default_threads() -> int:
     return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
 
@@ -99,14 +103,15 @@ def topk(scores: np.ndarray, k: int, keep_sink: int = 0, keep_local: int = 0) ->
     return out
 
 
-def summaries(*, k_pool, block_table, seq_lens, Hkv: int, D: int, P: int) -> np.ndarray:
-    """Block summaries [B][max_blocks][Hkv][D] (fp64), zero past each sequence's blocks."""
+def summaries(*, k_pool, block_table, seq_lens, Hkv: int, D: int, P: int, summary_dtype: str = "f32") -> np.ndarray:
+    """Block summaries [B][max_blocks][Hkv][D] (fp64), zero past each sequence's blocks;
+    summary_dtype "bf16" rounds each one to bf16 (reading R10)."""
     k_pool = _c(k_pool)
     table = _c(block_table, np.int32)
     lens = _c(seq_lens, np.int32)
     B, mb = table.shape
     out = np.empty((B, mb, Hkv, D), dtype=np.float64)
-    rc = _load().orc_summaries(B, Hkv, D, P, _dtype_code(k_pool), _ptr(k_pool),
+    rc = _load().orc_summaries(B, Hkv, D, P, _dtype_code(k_pool), _summary_flag(summary_dtype), _ptr(k_pool),
                                int(k_pool.shape[0]), _ptr(table), mb, _ptr(lens), _ptr(out))
     if rc != 0:
         raise RuntimeError("orc_summaries failed (%d)" % rc)
@@ -139,7 +144,8 @@ def select_index(*, q_idx, index_keys, block_table, seq_lens, top_k: int, P: int
 def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k: int,
            scale: float, P: int = 64, summaries_in: Optional[np.ndarray] = None,
            idx_in: Optional[np.ndarray] = None, want_weights: bool = False,
-           nthreads: Optional[int] = None, keep_sink: int = 0, keep_local: int = 0) -> dict:
+           nthreads: Optional[int] = None, keep_sink: int = 0, keep_local: int = 0,
+           summary_dtype: str = "f32") -> dict:
     """Decode step over B sequences. Returns scores [B][Hkv][max_blocks], idx [B][Hkv][top_k],
     o [B][Hq][D], lse [B][Hq] (fp64) and, if asked, w [B][Hq][top_k*P]."""
     q, k_pool, v_pool = _c(q), _c(k_pool), _c(v_pool)
@@ -156,7 +162,8 @@ def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k
     w = np.empty((B, Hq, top_k * P), dtype=np.float64) if want_weights else None
     s_in = None if summaries_in is None else _c(summaries_in, np.float64)
     i_in = None if idx_in is None else _c(idx_in, np.int32)
-    rc = _load().orc_decode(B, Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), float(scale), dt, _ptr(q), _ptr(k_pool),
+    rc = _load().orc_decode(B, Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), _summary_flag(summary_dtype),
+                            float(scale), dt, _ptr(q), _ptr(k_pool),
                             _ptr(v_pool), int(k_pool.shape[0]), _ptr(table), mb, _ptr(lens),
                             _ptr(s_in), _ptr(i_in), _ptr(scores), _ptr(idx), _ptr(o), _ptr(lse),
                             _ptr(w), int(nthreads or default_threads()))
@@ -171,7 +178,7 @@ def decode(*, q, k_pool, v_pool, block_table, seq_lens, Hq: int, Hkv: int, top_k
 def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: int, Hkv: int,
             top_k: int, scale: float, P: int = 64, tiles: Optional[tuple] = None,
             idx_in: Optional[np.ndarray] = None, nthreads: Optional[int] = None, keep_sink: int = 0,
-            keep_local: int = 0) -> dict:
+            keep_local: int = 0, summary_dtype: str = "f32") -> dict:
     """Prefill chunk of T tokens on one sequence. Returns scores [ntiles][Hkv][max_blocks],
     idx [ntiles][Hkv][top_k+1], o [T][Hq][D], lse [T][Hq]; only tiles [lo, hi) are computed
     (rows of other tiles are NaN). idx_in ([ntiles][Hkv][top_k+1]) replaces the selection."""
@@ -186,7 +193,8 @@ def prefill(*, q, k_new, v_new, k_pool, v_pool, block_table, past_len: int, Hq: 
     idx = np.full((ntiles, Hkv, top_k + 1), -2, dtype=np.int32)
     o = np.full((T, Hq, D), np.nan)
     lse = np.full((T, Hq), np.nan)
-    rc = _load().orc_prefill(Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), float(scale), dt, _ptr(q), _ptr(k_new),
+    rc = _load().orc_prefill(Hq, Hkv, D, P, top_k, int(keep_sink), int(keep_local), _summary_flag(summary_dtype),
+                             float(scale), dt, _ptr(q), _ptr(k_new),
                              _ptr(v_new), _ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]),
                              _ptr(table), mb, int(past_len), int(T), int(lo), int(hi),
                              _ptr(None if idx_in is None else _c(idx_in, np.int32)),

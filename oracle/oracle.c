@@ -45,6 +45,9 @@
  *                        the other k_eff - |F| come from the remaining candidates under R3.
  *                        The page guesses that an attention sink plus a local block replaced
  *                        NSA's sliding window ([MGS §2], "third subtraction").
+ *   R10 bf16 summaries = optional, off by default: the summary pool is stored in bf16; a block
+ *                        summary is then its mean (R1) rounded once to the nearest bf16 value,
+ *                        ties to even, and every score uses the rounded summary.
  *
  * All arithmetic is fp64 on exact upcasts of the stored inputs (f32 or bf16 bit patterns).
  * Layouts: q [B][Hq][D]; K/V pools [num_pages][Hkv][P][D]; block_table [B][max_blocks].
@@ -56,6 +59,16 @@
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* R10: x rounded to the nearest value with 8 significant bits (bf16), ties to even; one
+ * rounding from the fp64 value. Zero and non-finite values pass through; the means rounded here
+ * stay far inside bf16's exponent range. */
+static double round_to_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);                  /* x = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexp(rint(ldexp(m, 8)), e - 8);   /* rint: the default mode, nearest-even */
+}
 
 /* exact upcast of one stored element */
 static double elem(const void* base, int dtype, size_t i) {
@@ -125,7 +138,7 @@ int orc_topk_forced(const double* s, int n, int k, int sink, int local, int32_t*
 
 /* ------------------------------------------------------------------ decode */
 typedef struct {
-    int B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks;
+    int B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, summary_bf16;
     double scale;
     const void *q, *k_pool, *v_pool;
     const int32_t *block_table, *seq_lens, *idx_in;
@@ -154,6 +167,8 @@ static int block_summary(const decode_args* a, int b, int N, int j, int g, doubl
             S[d] += elem(a->k_pool, a->dtype, (size_t)i);
         }
     for (int d = 0; d < a->D; ++d) S[d] /= (double)n;
+    if (a->summary_bf16)
+        for (int d = 0; d < a->D; ++d) S[d] = round_to_bf16(S[d]);
     return 0;
 }
 
@@ -289,7 +304,7 @@ static int run_threads(void* (*fn)(void*), void* jobs, size_t job_size, int nthr
  * tokens in ascending token order, zero-padded.
  * Returns 0, or a negative code (bad argument, page id out of range, allocation failure). */
 int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int keep_local,
-               double scale, int dtype,
+               int summary_bf16, double scale, int dtype,
                const void* q, const void* k_pool, const void* v_pool, int num_pages,
                const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
                const double* summaries, const int32_t* idx_in, double* scores_out,
@@ -298,7 +313,8 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, int keep_sink, i
         !v_pool || !block_table || !seq_lens || !o_out || !lse_out || (dtype != ORC_F32 && dtype != ORC_BF16))
         return -1;
     if (keep_sink < 0 || keep_local < 0 || keep_sink + keep_local > top_k) return -1;
-    decode_args a = {B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, scale, q, k_pool,
+    decode_args a = {B, Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, summary_bf16 != 0,
+                     scale, q, k_pool,
                      v_pool, block_table, seq_lens, idx_in, summaries, scores_out, o_out,
                      lse_out, w_out, idx_out, 0};
     if (nthreads < 1) nthreads = 1;
@@ -310,13 +326,15 @@ int orc_decode(int B, int Hq, int Hkv, int D, int P, int top_k, int keep_sink, i
     return a.status ? a.status : rc;
 }
 
-/* R1 for every block of every sequence: out [B][max_blocks][Hkv][D] fp64, zero past nb. */
-int orc_summaries(int B, int Hkv, int D, int P, int dtype, const void* k_pool, int num_pages,
+/* R1 for every block of every sequence: out [B][max_blocks][Hkv][D] fp64, zero past nb
+ * (summary_bf16: each value rounded as R10). */
+int orc_summaries(int B, int Hkv, int D, int P, int dtype, int summary_bf16, const void* k_pool, int num_pages,
                   const int32_t* block_table, int max_blocks, const int32_t* seq_lens, double* out) {
     decode_args a;
     memset(&a, 0, sizeof a);
     a.B = B; a.Hq = Hkv; a.Hkv = Hkv; a.D = D; a.P = P; a.dtype = dtype; a.k_pool = k_pool;
     a.num_pages = num_pages; a.block_table = block_table; a.max_blocks = max_blocks;
+    a.summary_bf16 = summary_bf16 != 0;
     memset(out, 0, sizeof(double) * (size_t)B * max_blocks * Hkv * D);
     for (int b = 0; b < B; ++b) {
         int N = seq_lens[b] > 0 ? seq_lens[b] : 0;
@@ -332,8 +350,8 @@ int orc_summaries(int B, int Hkv, int D, int P, int dtype, const void* k_pool, i
 
 /* ------------------------------------------------------------------ prefill (R6) */
 typedef struct {
-    int Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, past_len, T, tile_lo,
-        tile_hi;
+    int Hq, Hkv, D, P, top_k, keep_sink, keep_local, summary_bf16, dtype, num_pages, max_blocks, past_len, T,
+        tile_lo, tile_hi;
     double scale;
     const void *q, *k_new, *v_new, *k_pool, *v_pool;
     const int32_t* table;        /* one sequence: [max_blocks] */
@@ -453,6 +471,8 @@ static void* prefill_summary_worker(void* p) {
                 S[d] += v;
             }
         for (int d = 0; d < a->D; ++d) S[d] /= (double)(t1 - t0);
+        if (a->summary_bf16)
+            for (int d = 0; d < a->D; ++d) S[d] = round_to_bf16(S[d]);
     }
     return NULL;
 }
@@ -473,8 +493,8 @@ static void* prefill_worker(void* p) {
  * idx_in (nullable) [ntiles][Hkv][top_k+1]: lists to attend over instead of the selection.
  * scores_out (nullable) [ntiles][Hkv][max_blocks]; idx_out (nullable) [ntiles][Hkv][top_k+1];
  * o_out [T][Hq][D] and lse_out [T][Hq] (rows of the computed tiles are written). */
-int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int keep_local, double scale,
-                int dtype, const void* q, const void* k_new, const void* v_new, const void* k_pool,
+int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int keep_local, int summary_bf16,
+                double scale, int dtype, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                 const void* v_pool, int num_pages, const int32_t* table, int max_blocks,
                 int past_len, int T, int tile_lo, int tile_hi, const int32_t* idx_in,
                 double* scores_out, int32_t* idx_out, double* o_out, double* lse_out, int nthreads) {
@@ -488,7 +508,7 @@ int orc_prefill(int Hq, int Hkv, int D, int P, int top_k, int keep_sink, int kee
     int nblocks = past_len / P + ntiles;
     double* S = (double*)malloc(sizeof(double) * (size_t)nblocks * Hkv * D);
     if (!S) return -3;
-    prefill_args a = {Hq, Hkv, D, P, top_k, keep_sink, keep_local, dtype, num_pages, max_blocks, past_len, T, tile_lo,
+    prefill_args a = {Hq, Hkv, D, P, top_k, keep_sink, keep_local, summary_bf16 != 0, dtype, num_pages, max_blocks, past_len, T, tile_lo,
                       tile_hi, scale, q, k_new, v_new, k_pool, v_pool, table, idx_in, S,
                       scores_out, o_out, lse_out, idx_out, 0};
     if (nthreads < 1) nthreads = 1;

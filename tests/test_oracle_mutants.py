@@ -53,6 +53,14 @@ MUTANTS = [
      "orc_topk_forced(s, nb, K, 0, 0, sel)", False),
     ("index_forced_dropped", "orc_topk_forced(row, nb, top_k, keep_sink, keep_local,",
      "orc_topk_forced(row, nb, top_k, 0, 0,", False),
+    ("bf16_summary_rounding_dropped", "if (a->summary_bf16)\n        for (int d = 0; d < a->D; ++d) S[d] = round_to_bf16(S[d]);",
+     "if (0)\n        for (int d = 0; d < a->D; ++d) S[d] = round_to_bf16(S[d]);", False),
+    ("bf16_round_half_up", "return ldexp(rint(ldexp(m, 8)), e - 8);", "return ldexp(floor(ldexp(m, 8) + 0.5), e - 8);",
+     False),
+    ("bf16_truncate", "return ldexp(rint(ldexp(m, 8)), e - 8);", "return ldexp(trunc(ldexp(m, 8)), e - 8);", False),
+    ("bf16_seven_bits", "return ldexp(rint(ldexp(m, 8)), e - 8);", "return ldexp(rint(ldexp(m, 7)), e - 7);", False),
+    ("bf16_prefill_rounding_dropped", "        if (a->summary_bf16)\n            for",
+     "        if (0)\n            for", False),
     ("prefill_forced_dropped", "orc_topk_forced(s, diag, K, a->keep_sink, a->keep_local, sel)",
      "orc_topk_forced(s, diag, K, 0, 0, sel)", False),
 ]

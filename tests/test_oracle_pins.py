@@ -20,6 +20,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from synth import make_decode_case, make_prefill_case, storage, round_to_bf16
@@ -579,3 +580,94 @@ def test_index_branch_forced_blocks():
             want = oracle.topk(plain["scores"][b, g, :nb], 3, keep_sink=1, keep_local=1)
             np.testing.assert_array_equal(r["idx"][b, g], want)
             assert 0 in r["idx"][b, g] and nb - 1 in r["idx"][b, g]
+
+
+# ----------------------------------------------------------------------------- bf16 summaries (R10)
+# Optional bf16 summary pool: a summary is its block's mean rounded once to bf16, ties to even.
+def _one_block_pool(values, Hkv=1, D=128):
+    """fp32 pool of one page whose first len(values) tokens hold the given per-token vectors."""
+    n = len(values)
+    k = np.zeros((1, Hkv, 64, D), np.float32)
+    k[0, :, :n, :] = np.asarray(values, np.float32)[None]
+    return k, np.zeros((1, 1), np.int32), np.array([n], np.int32)
+
+
+def test_bf16_summary_of_one_token_is_ieee_rounding():
+    """n = 1: the summary is the key itself, so R10 is fp32 -> bf16 round-to-nearest-even, which
+    torch's conversion computes; ties (low half exactly 0x8000) are included."""
+    r = np.random.default_rng(70)
+    x = r.standard_normal(128).astype(np.float32) * np.float32(3.0)
+    bits = x.view(np.uint32)
+    bits[:32] = (bits[:32] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exact ties, odd and even
+    bits[32:40] = (bits[32:40] & np.uint32(0xFFFF0000)) | np.uint32(0x7FFF)
+    bits[40:48] = (bits[40:48] & np.uint32(0xFFFF0000)) | np.uint32(0x8001)
+    x = bits.view(np.float32)
+    k, table, lens = _one_block_pool([x])
+    S = oracle.summaries(k_pool=k, block_table=table, seq_lens=lens, Hkv=1, D=128, P=64, summary_dtype="bf16")
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(S[0, 0, 0], want)
+
+
+def test_bf16_summary_rounds_the_exact_mean_ties_to_even():
+    """Means that fall exactly halfway between two bf16 values round to the even one."""
+    h = 2.0 ** -8
+    rows = [np.full(128, 1.0), np.full(128, 1.0), np.full(128, 1.0 + 3 * h)]        # mean 1 + 2^-8
+    rows2 = [np.full(128, 1.0 + 2 * h), np.full(128, 1.0 + 4 * h)]                   # mean 1 + 3*2^-8
+    for vals, mean, want in ((rows, 1.0 + h, 1.0), (rows2, 1.0 + 3 * h, 1.0 + 4 * h)):
+        k, table, lens = _one_block_pool(vals)
+        S = oracle.summaries(k_pool=k, block_table=table, seq_lens=lens, Hkv=1, D=128, P=64, summary_dtype="bf16")
+        exact = oracle.summaries(k_pool=k, block_table=table, seq_lens=lens, Hkv=1, D=128, P=64)
+        np.testing.assert_array_equal(exact[0, 0, 0], np.full(128, mean))   # the tie itself
+        np.testing.assert_array_equal(S[0, 0, 0], np.full(128, want))
+
+
+def test_bf16_summaries_are_the_rounded_means():
+    c = make_decode_case(B=2, Hq=8, Hkv=2, lens=[1000, 130], top_k=4, dtype="bf16", seed=71, permute=True)
+    kw = dict(k_pool=storage(c.k_pool, "bf16"), block_table=c.block_table, seq_lens=c.seq_lens, Hkv=2, D=128, P=64)
+    exact = oracle.summaries(**kw)
+    rounded = oracle.summaries(summary_dtype="bf16", **kw)
+    want = torch.from_numpy(exact).to(torch.bfloat16).to(torch.float64).numpy()   # fp64 -> bf16, one rounding
+    np.testing.assert_array_equal(rounded, want)
+    for b, n in enumerate(c.seq_lens):         # the rounding really happened on the real blocks
+        nb = (int(n) + 63) // 64
+        assert np.mean(rounded[b, :nb] != exact[b, :nb]) > 0.5   # short blocks often average to bf16 values
+
+
+def test_bf16_summaries_change_nothing_when_means_are_bf16_values():
+    """Every block holds one repeated bf16 key per group: its mean is already a bf16 value, so
+    the bf16 mode gives the fp32 mode's scores, lists, outputs and lse exactly."""
+    c = make_decode_case(B=2, Hq=8, Hkv=2, lens=[900, 300], top_k=3, dtype="bf16", seed=72)
+    k = c.k_pool.copy()
+    k[:] = k[:, :, :1, :]          # token 0 of each page repeated over the page
+    c.k_pool = k
+    kw = decode_inputs(c)
+    a = oracle.decode(**kw)
+    b = oracle.decode(summary_dtype="bf16", **kw)
+    for key in ("scores", "idx", "o", "lse"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_bf16_summaries_scores_use_the_rounded_summaries():
+    """Decode and prefill scores in the bf16 mode equal the fp32-mode scores computed from
+    summaries that were rounded first (decode: through the precomputed-summary input)."""
+    c = make_decode_case(B=2, Hq=8, Hkv=2, lens=[2000, 700], top_k=5, dtype="bf16", seed=73, permute=True)
+    kw = decode_inputs(c)
+    S = oracle.summaries(k_pool=kw["k_pool"], block_table=c.block_table, seq_lens=c.seq_lens, Hkv=2, D=128, P=64,
+                         summary_dtype="bf16")
+    a = oracle.decode(summary_dtype="bf16", **kw)
+    b = oracle.decode(summaries_in=S, **kw)
+    np.testing.assert_array_equal(a["scores"], b["scores"])
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    p = make_prefill_case(Hq=8, Hkv=2, past_len=640, T=200, top_k=3, dtype="bf16", seed=74)
+    pk = prefill_inputs(p)
+    r = oracle.prefill(summary_dtype="bf16", **pk)
+    K = as_f64(storage(np.concatenate([logical_kv(p.k_pool, p.block_table, 0, 640), p.k_new]), "bf16"))
+    q = as_f64(pk["q"])
+    for tau in range(4):
+        rows = slice(tau * 64, min(200, tau * 64 + 64))
+        d = 10 + tau
+        for g in range(2):
+            qt = q[rows, g * 4:(g + 1) * 4].reshape(-1, 128).mean(axis=0)
+            means = np.array([K[j * 64:(j + 1) * 64, g].mean(axis=0) for j in range(d)])
+            Sb = torch.from_numpy(means).to(torch.bfloat16).to(torch.float64).numpy()
+            np.testing.assert_allclose(r["scores"][tau, g, :d], Sb @ qt, rtol=1e-12, atol=1e-12)
