@@ -93,6 +93,7 @@ def main():
     ap.add_argument("--no-mixed", action="store_true", help="skip the batch-32 mixed-length decode line")
     ap.add_argument("--no-large-k", action="store_true", help="skip the 1M-token k=1024 operating-point line")
     ap.add_argument("--no-index", action="store_true", help="skip the 1M-token index-branch select line")
+    ap.add_argument("--no-bf16-summaries", action="store_true", help="skip the 1M-token bf16 summary-pool line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
@@ -219,6 +220,9 @@ def main():
     }
     if not args.no_large_k:
         rec["large_k"] = bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph)
+    if not args.no_bf16_summaries:
+        rec["bf16_summaries"] = bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L,
+                                                     R, per_graph)
     tr = recorded_traffic(score_bytes)
     if tr is not None:
         rec["roofline"]["traffic"] = tr["bytes_per_launch"]
@@ -404,6 +408,48 @@ def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring,
             "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9,
             "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS, "bytes_per_attend": kv,
             "note": "the pages' ~6 % operating point (16,384 blocks, k = 1024); same caches as the headline"}
+
+
+def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph):
+    """The 1M-token decode with a bf16 summary pool (32 MiB instead of 64 MiB read by Step 1) on
+    the same rotated K/V caches: whole decode steps and the scoring kernel alone."""
+    c0 = cases[0]
+    B, max_len = c0.B, c0.max_seq_len
+    cfg = msa.make_config(c0.Hq, c0.Hkv, c0.top_k, dtype=c0.dtype, softmax_scale=c0.scale, summary_dtype="bf16")
+    dev = q_ring[0].device
+    bcaches = []
+    for l in range(L):
+        S = torch.empty((c0.num_pages, c0.Hkv, c0.D), dtype=torch.bfloat16, device=dev)
+        cb = msa.KVCache(caches[l].k_pages, caches[l].v_pages, S, caches[l].block_table, caches[l].seq_lens)
+        msa.msa_build_summaries(cfg, cb, B, max_len)
+        bcaches.append(cb)
+    out = torch.empty((B, c0.Hq, c0.D), dtype=q_ring[0].dtype, device=dev)
+    idx = [torch.empty((B, c0.Hkv, c0.top_k), dtype=torch.int32, device=dev) for _ in range(L)]
+    mb = (max_len + 63) // 64
+    sc = torch.empty((B, c0.Hkv, mb), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    n_rep = 10
+
+    def timed(fn):
+        g = timed_graph(fn, per_graph, torch)
+        run_graph(g, 2, torch)
+        return run_graph(g, n_rep, torch) / (per_graph * n_rep)
+    t_step = timed(lambda i: msa.msa_decode_step(cfg, q_ring[i % R], bcaches[i % L], B, max_len, out,
+                                                 k_new=kn_ring[i % R], v_new=vn_ring[i % R], idx_out=idx[i % L],
+                                                 workspace=ws))
+    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], bcaches[i % L], B, max_len, sc))
+    torch.cuda.synchronize()
+    nb = sum((int(n) + 63) // 64 for n in c0.seq_lens)
+    score_bytes = nb * c0.Hkv * c0.D * 2 + nb * 4 + nb * c0.Hkv * 4 + B * c0.Hq * c0.D * 2
+    log("1M bf16 summaries: step %.1f us (%.0f tokens/s); score %.2f us (%.0f GB/s)"
+        % (t_step * 1e6, B / t_step, t_score * 1e6, score_bytes / t_score / 1e9))
+    del bcaches
+    return {"workload": "decode_bf16_1m_paged", "summary_dtype": "bf16", "step_us": t_step * 1e6,
+            "tokens_per_s": B / t_step, "score_us": t_score * 1e6, "score_bytes_per_launch": score_bytes,
+            "score_GBps": score_bytes / t_score / 1e9, "score_hbm_frac": score_bytes / t_score / 1e9 / HBM_PEAK_GBPS,
+            "note": "same caches and queries as the headline; summaries rounded to bf16 (a different, coarser "
+                    "ranking input, so not the headline number)"}
 
 
 def bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev):

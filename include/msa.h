@@ -26,6 +26,10 @@
  *     sequence's blocks; prefill: the blocks before the diagonal) are always kept and count
  *     toward k_eff; the remaining k_eff - |forced| are chosen by the order above among the
  *     other candidates. s, l >= 0 and s + l <= top_k, else MSA_ERR_INVALID_ARG;
+ *   - summary pool precision: fp32 by default. With summary_dtype = MSA_BF16 the pool holds bf16:
+ *     a summary is the fp32 mean of the block's keys rounded to the nearest bf16 value (ties to
+ *     even), and every score is computed from the stored bf16 summary. Halves the bytes Step 1
+ *     reads in decode; the ranking then sees summaries rounded to 8 significant bits;
  *   - softmax: logits = softmax_scale * <q_h, k_t>, fp32 accumulation, lse in natural log.
  *
  * Conventions for every entry point
@@ -46,8 +50,9 @@
  * Layouts (row-major, element type per msa_config):
  *   q            decode [B][Hq][D]; prefill [T][Hq][D]
  *   K/V pools    [num_pages][Hkv][block_size][D]   (one page = one 64-token block of all heads)
- *   summaries    [num_pages][Hkv][D] float32       (kept equal to the block means by
- *                                                   msa_build_summaries and the append paths)
+ *   summaries    [num_pages][Hkv][D] float32 or bf16 (summary_dtype; kept equal to the block
+ *                                                   means by msa_build_summaries and the append
+ *                                                   paths)
  *   block_table  [B][max_blocks] int32             logical block -> page id
  *   seq_lens     [B] int32                         visible tokens per sequence
  */
@@ -101,12 +106,13 @@ typedef struct msa_config {
     int32_t keep_local;       /* forced local blocks: the last keep_local candidates are always kept */
     int32_t q_tile;           /* prefill selection tile in query rows; must be 64 */
     int32_t keep_sink;        /* forced sink blocks: the first keep_sink candidates are always kept */
+    int32_t summary_dtype;    /* msa_dtype of the summary pool: MSA_F32 (default) or MSA_BF16 */
 } msa_config;
 
 typedef struct msa_kv_cache {
     void* k_pages;            /* [num_pages][Hkv][64][128] kv_dtype */
     void* v_pages;            /* same */
-    float* summaries;         /* [num_pages][Hkv][128] float32 */
+    void* summaries;          /* [num_pages][Hkv][128] of cfg->summary_dtype (float32 or bf16) */
     const int32_t* block_table; /* [B][max_blocks] */
     const int32_t* seq_lens;  /* [B]; decode/select/attend/build only */
     int32_t num_pages;

@@ -26,7 +26,7 @@ class MsaConfig(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("score_mode", ctypes.c_int32),
                 ("keep_local", ctypes.c_int32), ("q_tile", ctypes.c_int32),
-                ("keep_sink", ctypes.c_int32)]
+                ("keep_sink", ctypes.c_int32), ("summary_dtype", ctypes.c_int32)]
 
 
 class MsaKvCache(ctypes.Structure):
@@ -82,11 +82,11 @@ def msa_status_string(status: int) -> str:
 def make_config(num_q_heads: int, num_kv_heads: int, top_k: int, dtype: str = "bf16",
                 softmax_scale: Optional[float] = None, head_dim: int = 128, block_size: int = 64,
                 score_mode: int = MSA_SCORE_MEAN_KEY, keep_local: int = 0,
-                q_tile: int = 64, keep_sink: int = 0) -> MsaConfig:
+                q_tile: int = 64, keep_sink: int = 0, summary_dtype: str = "f32") -> MsaConfig:
     dt = {"f32": MSA_F32, "bf16": MSA_BF16}[dtype]
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
     return MsaConfig(num_q_heads, num_kv_heads, head_dim, block_size, top_k, scale, dt, dt, dt,
-                     score_mode, keep_local, q_tile, keep_sink)
+                     score_mode, keep_local, q_tile, keep_sink, {"f32": MSA_F32, "bf16": MSA_BF16}[summary_dtype])
 
 
 @dataclasses.dataclass
@@ -94,7 +94,7 @@ class KVCache:
     """Device tensors of a paged cache (see msa.h for layouts)."""
     k_pages: object       # [num_pages][Hkv][64][128]
     v_pages: object
-    summaries: object     # [num_pages][Hkv][128] float32
+    summaries: object     # [num_pages][Hkv][128] float32 or bfloat16 (the config's summary_dtype)
     block_table: object   # [B][max_blocks] int32
     seq_lens: object = None  # [B] int32
 

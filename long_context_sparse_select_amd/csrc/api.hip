@@ -40,6 +40,7 @@ msa_status check_config(const msa_config* c, bool any_mode = false) {
   if (c->q_dtype != MSA_F32 && c->q_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->kv_dtype != MSA_F32 && c->kv_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->out_dtype != MSA_F32 && c->out_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
+  if (c->summary_dtype != MSA_F32 && c->summary_dtype != MSA_BF16) return MSA_ERR_INVALID_ARG;
   if (c->score_mode != MSA_SCORE_MEAN_KEY && c->score_mode != MSA_SCORE_MAX_TOKEN) return MSA_ERR_INVALID_ARG;
   if (!std::isfinite(c->softmax_scale) || !(c->softmax_scale > 0.f)) return MSA_ERR_INVALID_ARG;
   if (c->head_dim != MSA_HEAD_DIM || c->block_size != MSA_BLOCK) return MSA_ERR_UNSUPPORTED;
@@ -108,8 +109,9 @@ msa_status check_batch(const msa_kv_cache* cache, int B, int max_len) {
   return MSA_OK;
 }
 
-CacheArgs cache_args(const msa_kv_cache* c) {
-  return CacheArgs{c->k_pages, c->v_pages, c->summaries, c->block_table, c->seq_lens, c->num_pages, c->max_blocks};
+CacheArgs cache_args(const msa_config* cfg, const msa_kv_cache* c) {
+  return CacheArgs{c->k_pages, c->v_pages, c->summaries, cfg->summary_dtype == MSA_BF16, c->block_table, c->seq_lens,
+                   c->num_pages, c->max_blocks};
 }
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
@@ -148,6 +150,7 @@ msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* ca
   t.kpool = cache->k_pages;
   t.vpool = cache->v_pages;
   t.S = cache->summaries;
+  t.s_bf16 = cfg->summary_dtype == MSA_BF16;
   t.q = q;
   t.Hq = cfg->num_q_heads;
   return hip_status(launch_topk(t, bf16, st));
@@ -156,7 +159,7 @@ msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* ca
 msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
                       float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
                       const void* v_new, hipStream_t st) {
-  MSA_TRY(hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cache), B, cfg->num_q_heads,
+  MSA_TRY(hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), B, cfg->num_q_heads,
                                          cfg->num_kv_heads, max_len, scores, row_stride, st)));
   return run_topk(cfg, q, cache, B, max_len, scores, row_stride, idx, pages, k_new, v_new, st);
 }
@@ -220,7 +223,7 @@ msa_status msa_build_summaries(const msa_config* cfg, const msa_kv_cache* cache,
   if (cache->k_pages == nullptr) return MSA_ERR_INVALID_ARG;
   MSA_TRY(check_batch(cache, batch, max_seq_len));
   if (batch == 0) return MSA_OK;
-  return hip_status(launch_build_summaries(cfg->kv_dtype == MSA_BF16, cache_args(cache), batch, cfg->num_kv_heads,
+  return hip_status(launch_build_summaries(cfg->kv_dtype == MSA_BF16, cache_args(cfg, cache), batch, cfg->num_kv_heads,
                                            max_seq_len, (hipStream_t)stream));
 }
 
@@ -232,7 +235,7 @@ msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* c
   if (q == nullptr || scores_out == nullptr) return MSA_ERR_INVALID_ARG;
   if (batch == 0) return MSA_OK;
   const int row_stride = (max_seq_len + MSA_BLOCK - 1) / MSA_BLOCK;
-  return hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cache), batch, cfg->num_q_heads,
+  return hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), batch, cfg->num_q_heads,
                                         cfg->num_kv_heads, max_seq_len, scores_out, row_stride,
                                         (hipStream_t)stream));
 }
@@ -267,7 +270,7 @@ msa_status msa_select_index(const msa_config* cfg, const void* q_index, const vo
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
-  MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, cache_args(cache), batch,
+  MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, cache_args(cfg, cache), batch,
                                         cfg->num_kv_heads, max_seq_len, scores, L.row_stride, st)));
   return run_topk(cfg, nullptr, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
                   st);
@@ -323,7 +326,7 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   const hipStream_t st = (hipStream_t)stream;
   const int Hkv = cfg->num_kv_heads, Hq = cfg->num_q_heads;
   const int past_blocks = past_len / kP, ntiles = (T + kP - 1) / kP;
-  const CacheArgs ca = cache_args(cache);
+  const CacheArgs ca = cache_args(cfg, cache);
   float* qtile = at<float>(workspace, L.qtile);
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);

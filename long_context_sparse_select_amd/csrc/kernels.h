@@ -10,7 +10,8 @@ namespace msa {
 struct CacheArgs {
   void* k;               // [num_pages][Hkv][64][128]
   void* v;
-  float* S;              // [num_pages][Hkv][128]
+  void* S;               // [num_pages][Hkv][128] summaries: float, or bf16 when s_bf16
+  bool s_bf16;
   const int32_t* table;  // [B][max_blocks]
   const int32_t* lens;   // [B] (decode paths)
   int num_pages;
@@ -61,7 +62,8 @@ struct TopkArgs {
   const void* v_new;
   void* kpool;
   void* vpool;
-  float* S;
+  void* S;              // summaries, float or bf16 (s_bf16)
+  bool s_bf16;
   const void* q;
   int Hq;
 };

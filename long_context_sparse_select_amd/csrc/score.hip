@@ -6,11 +6,11 @@
 // mean of the group's query heads (decode) or of the tile's 64 rows x the group's heads
 // (prefill); a block's score is <index query, block summary>, unscaled, in fp32.
 //
-// Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 per sequence), so the
-// kernel is shaped for HBM: a workgroup owns a chunk of 16 logical blocks of one sequence and
-// walks (block, group) pairs with 32 lanes per pair and 16 B per lane, in passes of 8 blocks --
-// for Hkv = 8 it reads the chunk's 16 pages as 16 contiguous 4 KiB runs, whatever the page
-// permutation. Each lane reads its pairs' page ids from the table and issues all of its
+// Decode is a streaming read of the summary pool (nb x Hkv x 128 fp32 or bf16 per sequence), so
+// the kernel is shaped for HBM: a workgroup owns a chunk of 16 logical blocks of one sequence and
+// walks (block, group) pairs with 16 B per lane -- 32 lanes per fp32 pair, in passes of 8 blocks,
+// or 16 lanes per bf16 pair, in one pass of 16 -- so for Hkv = 8 it reads the chunk's 16 pages
+// as 16 contiguous 4 KiB (2 KiB) runs, whatever the page permutation. Each lane reads its pairs' page ids from the table and issues all of its
 // summary loads of a pass first; the Hkv index queries are built in LDS while the first pass
 // is in flight. The chunk's scores are staged in LDS and leave as one contiguous run per row.
 // The number of KV heads is a template parameter for the power-of-two cases, so the pair-index
@@ -43,9 +43,9 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, lon
 }
 
 // HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
-// shifts); HKV == 0: a runtime count (generic path).
-template <typename TQ, int HKV>
-__global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const float* __restrict__ S,
+// shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
+template <typename TQ, int HKV, bool SB>
+__global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const void* __restrict__ S,
                                                       const int32_t* __restrict__ table,
                                                       const int32_t* __restrict__ lens, int num_pages,
                                                       int max_blocks, int Hq, int hkv_arg, int max_len,
@@ -56,8 +56,10 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   const int j0 = blockIdx.x * kChunk;
   const int tid = threadIdx.x;
   const int jend = min(j0 + kChunk, row_stride);
-  const int slot = tid >> 5;    // 8 pair slots per pass
-  const int l32 = tid & 31;     // 4 dims per lane
+  constexpr int kLanes = SB ? 16 : 32;   // lanes per (block, group) pair, 16 B each
+  constexpr int kSlots = 256 / kLanes;   // pairs per load round
+  const int slot = tid / kLanes;
+  const int lp = tid % kLanes;           // 8 (bf16) or 4 (fp32) dims per lane
   const int npairs = (jend - j0) * Hkv;
   const int32_t* trow = table + (long long)b * max_blocks;
   if (num_pages <= 0) {   // an empty pool: every block of the chunk scores -inf (uniform exit)
@@ -71,20 +73,21 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   // Pass loads: each lane reads the page ids of its own pairs straight from the table (the
   // workgroup's 8 entries share one cache line), then issues every summary load of the pass.
   // Nothing else is on the path from the kernel's start to the summary stream.
-  float4 sv[kUnroll];
+  uint4 sv[kUnroll];
   bool live[kUnroll];
   int tp[kUnroll];
   auto table_loads = [&](int p0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) tp[u] = trow[min(j0 + (p0 + u * 8 + slot) / Hkv, row_stride - 1)];
+    for (int u = 0; u < kUnroll; ++u) tp[u] = trow[min(j0 + (p0 + u * kSlots + slot) / Hkv, row_stride - 1)];
   };
   auto summary_loads = [&](int p0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {   // branch-free: every load is issued unconditionally
-      const int p = p0 + u * 8 + slot;
+      const int p = p0 + u * kSlots + slot;
       live[u] = (p < npairs) & (tp[u] >= 0) & (tp[u] < num_pages);   // the length is applied later
       const int page = live[u] ? tp[u] : 0;   // page 0: a valid address, result unused
-      sv[u] = *reinterpret_cast<const float4*>(S + ((long long)page * Hkv + p % Hkv) * kD + l32 * 4);
+      const long long row = (long long)page * Hkv + p % Hkv;   // 16 B per lane, either pool type
+      sv[u] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(S) + row * kD * (SB ? 2 : 4))[lp];
     }
   };
   table_loads(0);
@@ -140,24 +143,41 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   __syncthreads();
 
   float* s_sc = s_qidx + Hkv * kD;
-  for (int p0 = 0; p0 < npairs; p0 += 8 * kUnroll) {
+  for (int p0 = 0; p0 < npairs; p0 += kSlots * kUnroll) {
     if (p0 > 0) {
       table_loads(p0);
       summary_loads(p0);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int p = p0 + u * 8 + slot;
-      if (p >= npairs) continue;   // uniform across the 32-lane slot
+      const int p = p0 + u * kSlots + slot;
+      if (p >= npairs) continue;   // uniform across the pair's lanes
       const int jl = p / Hkv, g = p % Hkv;
-      const float4 qv = *reinterpret_cast<const float4*>(s_qidx + g * kD + l32 * 4);
-      float part = qv.x * sv[u].x;
-      part = fmaf(qv.y, sv[u].y, part);
-      part = fmaf(qv.z, sv[u].z, part);
-      part = fmaf(qv.w, sv[u].w, part);
-      part = row16_sum(part);
-      part += __shfl_xor(part, 16);
-      if (l32 == 0) s_sc[g * kChunk + jl] = (live[u] && j0 + jl < nb) ? part : -INFINITY;
+      float part;
+      if constexpr (SB) {
+        const float4* qp = reinterpret_cast<const float4*>(s_qidx + g * kD + lp * 8);
+        const float4 qa = qp[0], qb = qp[1];
+        const uint4 w = sv[u];
+        part = qa.x * bf16lo(w.x);
+        part = fmaf(qa.y, bf16hi(w.x), part);
+        part = fmaf(qa.z, bf16lo(w.y), part);
+        part = fmaf(qa.w, bf16hi(w.y), part);
+        part = fmaf(qb.x, bf16lo(w.z), part);
+        part = fmaf(qb.y, bf16hi(w.z), part);
+        part = fmaf(qb.z, bf16lo(w.w), part);
+        part = fmaf(qb.w, bf16hi(w.w), part);
+        part = row16_sum(part);
+      } else {
+        const float4 qv = *reinterpret_cast<const float4*>(s_qidx + g * kD + lp * 4);
+        const float4 f = __builtin_bit_cast(float4, sv[u]);
+        part = qv.x * f.x;
+        part = fmaf(qv.y, f.y, part);
+        part = fmaf(qv.z, f.z, part);
+        part = fmaf(qv.w, f.w, part);
+        part = row16_sum(part);
+        part += __shfl_xor(part, 16);
+      }
+      if (lp == 0) s_sc[g * kChunk + jl] = (live[u] && j0 + jl < nb) ? part : -INFINITY;
     }
   }
   __syncthreads();
@@ -215,7 +235,8 @@ constexpr int kPB = 64;     // blocks per workgroup
 constexpr int kRowP = 132;  // LDS row pitch (floats)
 typedef float f32x16s __attribute__((ext_vector_type(16)));
 
-__global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__ qtile, const float* __restrict__ S,
+template <bool SB>
+__global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__ qtile, const void* __restrict__ S,
                                                        const int32_t* __restrict__ table, int num_pages,
                                                        int past_blocks, int ntiles, int Hkv,
                                                        float* __restrict__ scores, int row_stride) {
@@ -237,7 +258,13 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
       const int r = (tid >> 5) + 8 * it;
       av[it] = reinterpret_cast<const float4*>(qtile + ((long long)min(tz + r, ntiles - 1) * Hkv + g) * kD)[c4];
       const int page = page_ok(pg[it], num_pages) ? pg[it] : 0;   // page 0: a valid address
-      bv[it] = reinterpret_cast<const float4*>(S + ((long long)page * Hkv + g) * kD)[c4];
+      const long long srow = (long long)page * Hkv + g;
+      if constexpr (SB) {   // 4 bf16 values widened exactly to fp32
+        const uint2 w = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(S) + srow * kD)[c4];
+        bv[it] = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+      } else {
+        bv[it] = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(S) + srow * kD)[c4];
+      }
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -276,15 +303,15 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
 }
 
 
-template <typename TQ>
+template <typename TQ, bool SB>
 void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
                         int row_stride, hipStream_t st) {
   const dim3 grid((row_stride + kChunk - 1) / kChunk, B);
   const size_t lds = (size_t)Hkv * (kD + kChunk) * sizeof(float);
 #define MSA_SCORE_CASE(H)                                                                                  \
   case H:                                                                                                  \
-    k_score_decode<TQ, H><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, Hkv, \
-                                                  max_len, scores, row_stride);                            \
+    k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \
+                                                      Hkv, max_len, scores, row_stride);                   \
     break;
   switch (Hkv) {
     MSA_SCORE_CASE(1)
@@ -295,8 +322,8 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
     MSA_SCORE_CASE(32)
     MSA_SCORE_CASE(64)
     default:
-      k_score_decode<TQ, 0><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, Hkv,
-                                                    max_len, scores, row_stride);
+      k_score_decode<TQ, 0, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq,
+                                                        Hkv, max_len, scores, row_stride);
   }
 #undef MSA_SCORE_CASE
 }
@@ -306,10 +333,13 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
                                float* scores, int row_stride, hipStream_t st) {
   if (B == 0 || row_stride == 0) return hipSuccess;
-  if (bf16)
-    launch_score_typed<uint16_t>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
-  else
-    launch_score_typed<float>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+  if (bf16) {
+    if (c.s_bf16) launch_score_typed<uint16_t, true>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+    else launch_score_typed<uint16_t, false>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+  } else {
+    if (c.s_bf16) launch_score_typed<float, true>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+    else launch_score_typed<float, false>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+  }
   return hipGetLastError();
 }
 
@@ -326,8 +356,12 @@ hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, f
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st) {
   const dim3 grid((row_stride + kPB - 1) / kPB, Hkv, (ntiles + kPT - 1) / kPT);
-  k_score_prefill<<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
-                                        row_stride);
+  if (c.s_bf16)
+    k_score_prefill<true><<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
+                                                row_stride);
+  else
+    k_score_prefill<false><<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
+                                                 row_stride);
   return hipGetLastError();
 }
 

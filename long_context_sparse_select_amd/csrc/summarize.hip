@@ -4,7 +4,8 @@
 // from a single diagram", §1 Step 1). Its summary of a block here is the fp32 mean of the
 // block's valid keys per KV head (the mean-pooled reading), stored next to the paged cache as
 // summaries[page][g][0..127] and recomputed from the tokens whenever a block changes, so it
-// always equals its definition.
+// always equals its definition. The pool holds fp32, or bf16 (the fp32 mean rounded to nearest
+// even on store), which halves what the decode scoring pass reads.
 //
 // Work mapping: one wavefront per (block, KV head). A wave reads a 64 x 128 block as 16
 // loads of 4 rows; lane l owns dims 8*(l%16) .. +7 of rows l/16, l/16+4, ... so each load
@@ -17,22 +18,31 @@ namespace msa {
 
 namespace {
 
-// Reduce the per-lane partial sums over the wave's four rows and write the mean.
-__device__ __forceinline__ void write_mean(float* acc, int n, float* dst, int lane) {
+// Reduce the per-lane partial sums over the wave's four rows and write the mean (row `row` of
+// the summary pool; bf16 pools store it rounded to nearest even).
+template <bool SB>
+__device__ __forceinline__ void write_mean(float* acc, int n, void* S, long long row, int lane) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = across_rows_sum(acc[e]);
   if (lane < 16) {
     const float fn = (float)n;
-    float4 lo = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
-    float4 hi = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
-    reinterpret_cast<float4*>(dst + lane * 8)[0] = lo;
-    reinterpret_cast<float4*>(dst + lane * 8)[1] = hi;
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = acc[e] / fn;
+    if constexpr (SB) {
+      reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(S) + row * kD)[lane] =
+          make_uint4(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7]));
+    } else {
+      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(S) + row * kD + lane * 8);
+      dst[0] = make_float4(m[0], m[1], m[2], m[3]);
+      dst[1] = make_float4(m[4], m[5], m[6], m[7]);
+    }
   }
 }
 
 // summaries of every block j < nb_b of every sequence b < B
-template <typename T>
-__global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ kpool, float* __restrict__ S,
+template <typename T, bool SB>
+__global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ kpool, void* __restrict__ S,
                                                          const int32_t* __restrict__ table,
                                                          const int32_t* __restrict__ lens, int num_pages,
                                                          int max_blocks, int B, int Hkv, int max_len, int mb) {
@@ -56,12 +66,12 @@ __global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ k
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     if ((lane >> 4) + 4 * i < n) v[i].add_to(acc);
-  write_mean(acc, n, S + ((long long)page * Hkv + g) * kD, lane);
+  write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
 // prefill append: T new tokens after past_len (a multiple of 64) -> whole new blocks
-template <typename T>
-__global__ void __launch_bounds__(256) k_append_prefill(T* __restrict__ kpool, T* __restrict__ vpool, float* __restrict__ S,
+template <typename T, bool SB>
+__global__ void __launch_bounds__(256) k_append_prefill(T* __restrict__ kpool, T* __restrict__ vpool, void* __restrict__ S,
                                                         const int32_t* __restrict__ table, int num_pages,
                                                         const T* __restrict__ k_new, const T* __restrict__ v_new,
                                                         int past_blocks, int T_new, int Hkv) {
@@ -86,7 +96,7 @@ __global__ void __launch_bounds__(256) k_append_prefill(T* __restrict__ kpool, T
     vv.store(vpool + head + (long long)r * kD + d0);
     kv.add_to(acc);
   }
-  write_mean(acc, n, S + ((long long)page * Hkv + g) * kD, lane);
+  write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
 }  // namespace
@@ -96,12 +106,15 @@ hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv,
   const long long units = (long long)B * mb * Hkv;
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)((units + 3) / 4));
-  if (bf16)
-    k_build_summaries<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)c.k, c.S, c.table, c.lens, c.num_pages,
-                                                      c.max_blocks, B, Hkv, max_len, mb);
-  else
-    k_build_summaries<float><<<grid, 256, 0, st>>>((const float*)c.k, c.S, c.table, c.lens, c.num_pages,
-                                                   c.max_blocks, B, Hkv, max_len, mb);
+#define MSA_BUILD(T, SB)                                                                                       \
+  k_build_summaries<T, SB><<<grid, 256, 0, st>>>((const T*)c.k, c.S, c.table, c.lens, c.num_pages, c.max_blocks, \
+                                                 B, Hkv, max_len, mb)
+  if (bf16) {
+    if (c.s_bf16) MSA_BUILD(uint16_t, true); else MSA_BUILD(uint16_t, false);
+  } else {
+    if (c.s_bf16) MSA_BUILD(float, true); else MSA_BUILD(float, false);
+  }
+#undef MSA_BUILD
   return hipGetLastError();
 }
 
@@ -110,13 +123,15 @@ hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_ne
   const int units = ((T + kP - 1) / kP) * Hkv;
   if (units == 0) return hipSuccess;
   const dim3 grid((units + 3) / 4);
-  if (bf16)
-    k_append_prefill<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)c.k, (uint16_t*)c.v, c.S, c.table, c.num_pages,
-                                                     (const uint16_t*)k_new, (const uint16_t*)v_new,
-                                                     past_blocks, T, Hkv);
-  else
-    k_append_prefill<float><<<grid, 256, 0, st>>>((float*)c.k, (float*)c.v, c.S, c.table, c.num_pages,
-                                                  (const float*)k_new, (const float*)v_new, past_blocks, T, Hkv);
+#define MSA_APPEND(TT, SB)                                                                                    \
+  k_append_prefill<TT, SB><<<grid, 256, 0, st>>>((TT*)c.k, (TT*)c.v, c.S, c.table, c.num_pages, (const TT*)k_new, \
+                                                 (const TT*)v_new, past_blocks, T, Hkv)
+  if (bf16) {
+    if (c.s_bf16) MSA_APPEND(uint16_t, true); else MSA_APPEND(uint16_t, false);
+  } else {
+    if (c.s_bf16) MSA_APPEND(float, true); else MSA_APPEND(float, false);
+  }
+#undef MSA_APPEND
   return hipGetLastError();
 }
 

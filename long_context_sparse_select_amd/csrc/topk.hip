@@ -382,8 +382,15 @@ struct DecodeAppend {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) acc += sh.rows[w][tid];
-    const float summary = acc / (float)(slot + 1);
-    a.S[((long long)page * a.Hkv + g) * kD + tid] = summary;
+    float summary = acc / (float)(slot + 1);
+    const long long si = ((long long)page * a.Hkv + g) * kD + tid;
+    if (a.s_bf16) {   // uniform: the pool stores the rounded mean, and the score uses what is stored
+      const uint32_t h = pack_bf16x2(summary, 0.f) & 0xffffu;
+      reinterpret_cast<uint16_t*>(a.S)[si] = (uint16_t)h;
+      summary = bf16lo(h);
+    } else {
+      reinterpret_cast<float*>(a.S)[si] = summary;
+    }
     float qi = 0.f;
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h)

@@ -130,10 +130,20 @@ def check_scores(gpu_scores: np.ndarray, ref_scores: np.ndarray, bound: np.ndarr
     return worst
 
 
-def check_band(chosen, r, keff, bound_max, keep_sink=0, keep_local=0, where=""):
+def bf16_step(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at x (8 significant bits): 2^(floor(log2 |x|) - 7); zero at 0."""
+    x = np.asarray(x, np.float64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    out[nz] = np.ldexp(1.0, (np.floor(np.log2(np.abs(x[nz]))) - 7).astype(int))
+    return out
+
+
+def check_band(chosen, r, keff, bound_max, keep_sink=0, keep_local=0, where="", slack=0.0):
     """R17 band rule on one row: the forced blocks (if any) are all chosen; among the other
     candidates, blocks clearly above the threshold of the remaining k_eff - |F| slots are in and
-    blocks clearly below it are out."""
+    blocks clearly below it are out. `slack` widens the band by a known bound on how far the
+    GPU's scores may sit from the oracle's for another reason (bf16 summary rounding)."""
     n = len(r)
     j = np.arange(n)
     forced = (j < keep_sink) | (j >= n - keep_local)
@@ -143,14 +153,14 @@ def check_band(chosen, r, keff, bound_max, keep_sink=0, keep_local=0, where=""):
     if kr <= 0:
         return
     tau = np.sort(rest)[::-1][kr - 1]
-    w = SCORE_RTOL * max(abs(tau), bound_max)
+    w = SCORE_RTOL * max(abs(tau), bound_max) + slack
     must = j[~forced][rest > tau + w]
     never = j[~forced][rest < tau - w]
     assert set(must) <= set(chosen), "band: a clearly-in block is missing " + where
     assert not (set(never) & set(chosen)), "band: a clearly-out block was selected " + where
 
 
-def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k, keep_sink=0, keep_local=0):
+def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k, keep_sink=0, keep_local=0, slack=None):
     """Exact same-precision selection plus the band rule against the fp64 scores.
     Returns a boolean array [B][Hkv]: True where the GPU set equals the oracle's."""
     B, Hkv, _ = gpu_idx.shape
@@ -169,7 +179,8 @@ def check_index_sets(gpu_idx, gpu_scores, ref_scores, bound, nb, k, keep_sink=0,
                 same[b, g] = True
                 continue
             r = ref_scores[b, g, :n]
-            check_band(chosen, r, keff, float(bound[b, g, :n].max()), keep_sink, keep_local, "(b=%d g=%d)" % (b, g))
+            check_band(chosen, r, keff, float(bound[b, g, :n].max()), keep_sink, keep_local, "(b=%d g=%d)" % (b, g),
+                       0.0 if slack is None else float(slack[b, g]))
             same[b, g] = np.array_equal(chosen, oracle.topk(r, k, keep_sink=keep_sink, keep_local=keep_local)[:keff])
     return same
 

@@ -183,3 +183,10 @@ def test_select_index_errors():
     # the config-driven select still refuses the max-token mode
     assert lib.msa_select(ctypes.byref(cfg(score_mode=1)), FAKE, ctypes.byref(fake_cache()), 1, 1024, None, FAKE,
                           FAKE, 1 << 30, None) == L.MSA_ERR_UNSUPPORTED
+
+
+def test_summary_dtype_validation():
+    assert ws_size(cfg(summary_dtype="bf16"), L.MSA_OP_DECODE)[0] == L.MSA_OK
+    c = cfg()
+    c.summary_dtype = 7
+    assert ws_size(c, L.MSA_OP_DECODE)[0] == L.MSA_ERR_INVALID_ARG

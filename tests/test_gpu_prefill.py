@@ -9,7 +9,7 @@ import torch
 import long_context_sparse_select_amd as msa
 import oracle
 from synth import bf16_bits_to_f32, make_prefill_case, make_prefill_case_torch, storage, workload
-from gpu_util import (SCORE_RTOL, assert_close, check_band, dev_tensor, host_f64, host_store, require_gpu)
+from gpu_util import (SCORE_RTOL, assert_close, bf16_step, check_band, dev_tensor, host_f64, host_store, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,16 +19,17 @@ def _gpu():
     require_gpu()
 
 
-def to_dev(p, keep_sink=0, keep_local=0):
+def to_dev(p, keep_sink=0, keep_local=0, summary_dtype="f32"):
     if isinstance(p.q, torch.Tensor):
         q, kn, vn, k, v = p.q, p.k_new, p.v_new, p.k_pool, p.v_pool
     else:
         q, kn, vn, k, v = (dev_tensor(storage(x, p.dtype)) for x in (p.q, p.k_new, p.v_new, p.k_pool, p.v_pool))
     table = torch.from_numpy(p.block_table).cuda()
-    S = torch.full((p.num_pages, p.Hkv, p.D), float("nan"), dtype=torch.float32, device="cuda")
+    sdt = torch.bfloat16 if summary_dtype == "bf16" else torch.float32
+    S = torch.full((p.num_pages, p.Hkv, p.D), float("nan"), dtype=sdt, device="cuda")
     lens = torch.tensor([p.past_len], dtype=torch.int32, device="cuda")
     cfg = msa.make_config(p.Hq, p.Hkv, p.top_k, dtype=p.dtype, softmax_scale=p.scale, keep_sink=keep_sink,
-                          keep_local=keep_local)
+                          keep_local=keep_local, summary_dtype=summary_dtype)
     cache = msa.KVCache(k, v, S, table, lens)
     if p.past_len:
         msa.msa_build_summaries(cfg, cache, 1, p.past_len)
@@ -66,14 +67,22 @@ def check_prefill(p, d, res, k_pool_before, v_pool_before, tiles=None):
     """scores (fp32 tolerance), selection (exact on the GPU's scores + band), outputs."""
     ntiles = (p.T + 63) // 64
     lo, hi = tiles if tiles is not None else (0, ntiles)
+    sd = "bf16" if int(d["cfg"].summary_dtype) == msa.MSA_BF16 else "f32"
     kw = dict(q=host_store(d["q"]), k_new=host_store(d["kn"]), v_new=host_store(d["vn"]),
               k_pool=k_pool_before, v_pool=v_pool_before, block_table=p.block_table,
               past_len=p.past_len, Hq=p.Hq, Hkv=p.Hkv, top_k=p.top_k, scale=p.scale, P=p.P,
-              keep_sink=int(d["cfg"].keep_sink), keep_local=int(d["cfg"].keep_local))
+              keep_sink=int(d["cfg"].keep_sink), keep_local=int(d["cfg"].keep_local), summary_dtype=sd)
     ref = oracle.prefill(tiles=(lo, hi), **kw)
     G = p.Hq // p.Hkv
     q64 = host_f64(d["q"])
     S64 = block_means(p, k_pool_before, host_store(d["kn"]))   # fp64 means, for the tolerance scale
+    # bf16 pool: the GPU's stored summaries against the rounded means (at most one bf16 step
+    # apart); their difference bounds the extra score error of each block
+    diff = np.zeros_like(S64)
+    if sd == "bf16":
+        S_ref = torch.from_numpy(S64).to(torch.bfloat16).to(torch.float64).numpy()
+        diff = np.abs(host_f64(d["S"])[p.block_table[0, :S64.shape[0]]] - S_ref)
+        assert np.all(diff <= bf16_step(S_ref)), "a bf16 summary is more than one step from the rounded mean"
     same_all = True
     for tau in range(lo, hi):
         rows = slice(tau * 64, min(p.T, tau * 64 + 64))
@@ -82,9 +91,10 @@ def check_prefill(p, d, res, k_pool_before, v_pool_before, tiles=None):
         for g in range(p.Hkv):
             qt = q64[rows, g * G:(g + 1) * G].reshape(-1, p.D).mean(axis=0)
             bound = np.abs(S64[:n, g]) @ np.abs(qt)
+            extra = diff[:n, g] @ np.abs(qt)
             r_s = ref["scores"][tau, g, :n]
             g_s = res["scores"][tau, g, :n].astype(np.float64)
-            tol = SCORE_RTOL * np.maximum(np.abs(r_s), bound)
+            tol = SCORE_RTOL * np.maximum(np.abs(r_s), bound) + extra
             assert np.all(np.abs(g_s - r_s) <= tol), "prefill score mismatch tau=%d g=%d" % (tau, g)
             assert np.all(np.isneginf(res["scores"][tau, g, n:]))
             sel = res["idx"][tau, g]
@@ -93,7 +103,7 @@ def check_prefill(p, d, res, k_pool_before, v_pool_before, tiles=None):
             assert sel[keff] == n and np.all(sel[keff + 1:] == -1)
             if keff:
                 check_band(sel[:keff], r_s, keff, float(bound.max()), kw["keep_sink"], kw["keep_local"],
-                           "(tau=%d g=%d)" % (tau, g))
+                           "(tau=%d g=%d)" % (tau, g), float(extra.max()) if n else 0.0)
             same_all &= bool(np.array_equal(sel, ref["idx"][tau, g]))
     if not same_all:
         ref = oracle.prefill(tiles=(lo, hi), idx_in=res["idx"], **kw)
