@@ -413,27 +413,31 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool prefill = a.lens == nullptr;
+  const int len_raw = prefill ? 0 : a.lens[row / a.Hkv];
+  float* srow = a.scores + (long long)row * a.row_stride;
+  // the row's score loads go first, in flight with the length load: addresses are clamped to the
+  // row stride (every row holds row_stride scores, every table row at least as many ids), so they
+  // wait for nothing; entries past the row's length are masked when used
+  float v[kPer];
+  int pg[kPer];   // decode: the candidates' page ids, loaded with the scores (no later round trip)
+  const int32_t* trow = a.pages != nullptr ? a.table + (long long)(row / a.Hkv) * a.max_blocks : nullptr;
+  const int rs_last = a.row_stride - 1;
+  if (rs_last >= 0) {   // uniform
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + NT * i, rs_last)];
+    if (trow != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + NT * i, rs_last)];
+    }
+  }
   int n, N = 0;
   if (!prefill) {
-    N = clamp_len(a.lens[row / a.Hkv], a.max_len);
+    N = clamp_len(len_raw, a.max_len);
     n = (N + kP - 1) / kP;
   } else {
     n = a.base_blocks + row / a.Hkv;
   }
   const int keff = min(a.k, n);
-  float* srow = a.scores + (long long)row * a.row_stride;
-  // the row's score loads go first: clamped in-bounds addresses, masked when used
-  float v[kPer];
-  int pg[kPer];   // decode: the candidates' page ids, loaded with the scores (no later round trip)
-  const int32_t* trow = a.pages != nullptr ? a.table + (long long)(row / a.Hkv) * a.max_blocks : nullptr;
-  if (n <= kMaxFast && n > 0) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + NT * i, n - 1)];
-    if (trow != nullptr) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + NT * i, n - 1)];
-    }
-  }
   const bool do_append = NT == kThreads && !prefill && a.k_new != nullptr && N > 0;   // uniform
   const int jlast = do_append ? n - 1 : -1;
   DecodeAppend<T> ap;
@@ -491,10 +495,12 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
-  const unsigned long long span = (unsigned long long)(mx - mn) + 1ull;
+  // any binning keeps T0 a valid bound (the bins at or above bstar hold >= k_eff group maxima); a
+  // monotone one keeps it tight. A float scale avoids a 64-bit division per thread.
+  const float bscale = (float)kBins / ((float)(mx - mn) + 1.0f);
   uint32_t bin = 0u;
   if (has) {
-    bin = (uint32_t)(((unsigned long long)(cm - mn) * kBins) / span);
+    bin = min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1));
     atomicAdd(&sh.hist[bin], 1u);
   }
   if (do_append) ap.partial(a, row, sh);
