@@ -5,7 +5,8 @@
 // §1 Steps 1-2; §3 decode / prefill):
 //   msa_decode_step   score -> top-k (+ append: new K/V row, that block's summary and score)
 //                     -> attend -> split-K merge
-//   msa_prefill_chunk append + summaries -> tile query -> score -> top-k (+diagonal) -> attend
+//   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
+//                     -> attend
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
 // HIP call, so an invalid call enqueues nothing.
 #include <cmath>
@@ -331,8 +332,7 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
 
-  MSA_TRY(hip_status(launch_append_prefill(true, ca, k_new, v_new, past_blocks, T, Hkv, st)));
-  MSA_TRY(hip_status(launch_tile_query(true, q, T, Hq, Hkv, qtile, st)));
+  MSA_TRY(hip_status(launch_prefill_prologue(true, ca, k_new, v_new, q, past_blocks, T, Hq, Hkv, qtile, st)));
   MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, st)));
   TopkArgs t{};
   t.scores = scores;

@@ -20,8 +20,11 @@ struct CacheArgs {
 
 // ---- block summaries / append
 hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv, int max_len, hipStream_t st);
-hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
-                                 int past_blocks, int T, int Hkv, hipStream_t st);
+// prefill: append the chunk (K/V rows + the new blocks' summaries) and compute the tile index
+// queries qtile [ceil(T/64)][Hkv][128] in one launch
+hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
+                                   const void* q, int past_blocks, int T, int Hq, int Hkv, float* qtile,
+                                   hipStream_t st);
 
 // ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats each.
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
@@ -30,7 +33,6 @@ hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int
 // = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
 hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, const CacheArgs& c, int B,
                               int Hkv, int max_len, float* scores, int row_stride, hipStream_t st);
-hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st);
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st);
 

@@ -36,11 +36,6 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-template <typename T> __device__ __forceinline__ float ld(const T* p, long long i);
-template <> __device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
-template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
-}
 
 // HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
 // shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
@@ -188,39 +183,6 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   }
 }
 
-// tile index query: qtile[tau][g][d] = mean over the tile's rows and the group's heads.
-// 512 threads: thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (all 2G loads
-// in flight at once); the 64 rows are then summed per dim through LDS, in row order.
-template <typename TQ>
-__global__ void __launch_bounds__(512) k_tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv,
-                                                    float* __restrict__ qtile) {
-  __shared__ float s_rows[kP][kD + 1];
-  const int tau = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  const int G = Hq / Hkv;
-  const int i0 = tau * kP, n = min(T, i0 + kP) - i0;
-  const int i = tid >> 3, d0 = (tid & 7) * 16;
-  const int row = i0 + min(i, n - 1);
-  float v[kMaxGroup][16];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[h][e] = ld(q, ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0 + e);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float acc = 0.f;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) acc += v[h][e];
-    s_rows[i][d0 + e] = i < n ? acc : 0.f;
-  }
-  __syncthreads();
-  if (tid < kD) {
-    float acc = 0.f;
-    for (int r = 0; r < n; ++r) acc += s_rows[r][tid];
-    qtile[((long long)tau * Hkv + g) * kD + tid] = acc / (float)(n * G);
-  }
-}
-
 // prefill scores: a 64-tile x 64-block fp32 product per workgroup on fp32 MFMA
 // (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 accumulation); tile tau scores the blocks
 // j < past_blocks + tau (its causal candidates), -inf elsewhere in the row.
@@ -343,15 +305,6 @@ hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int
   return hipGetLastError();
 }
 
-
-hipError_t launch_tile_query(bool bf16, const void* q, int T, int Hq, int Hkv, float* qtile, hipStream_t st) {
-  const dim3 grid((T + kP - 1) / kP, Hkv);
-  if (bf16)
-    k_tile_query<uint16_t><<<grid, 512, 0, st>>>((const uint16_t*)q, T, Hq, Hkv, qtile);
-  else
-    k_tile_query<float><<<grid, 512, 0, st>>>((const float*)q, T, Hq, Hkv, qtile);
-  return hipGetLastError();
-}
 
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st) {

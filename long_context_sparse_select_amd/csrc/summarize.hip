@@ -7,6 +7,9 @@
 // always equals its definition. The pool holds fp32, or bf16 (the fp32 mean rounded to nearest
 // even on store), which halves what the decode scoring pass reads.
 //
+// The prefill chunk's append shares a launch with the tile index queries (k_prefill_prologue):
+// the two are independent, so they overlap.
+//
 // Work mapping: one wavefront per (block, KV head). A wave reads a 64 x 128 block as 16
 // loads of 4 rows; lane l owns dims 8*(l%16) .. +7 of rows l/16, l/16+4, ... so each load
 // instruction covers four whole 256 B (bf16) rows. Partial sums are combined across the four
@@ -69,14 +72,15 @@ __global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ k
   write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
-// prefill append: T new tokens after past_len (a multiple of 64) -> whole new blocks
+// prefill append, one wave per unit = (new block jn, group g): T new tokens after past_len (a
+// multiple of 64) fill whole new blocks; the wave copies the block's rows into its page and
+// writes the block's summary
 template <typename T, bool SB>
-__global__ void __launch_bounds__(256) k_append_prefill(T* __restrict__ kpool, T* __restrict__ vpool, void* __restrict__ S,
-                                                        const int32_t* __restrict__ table, int num_pages,
-                                                        const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                                        int past_blocks, int T_new, int Hkv) {
+__device__ __forceinline__ void append_unit(T* __restrict__ kpool, T* __restrict__ vpool, void* __restrict__ S,
+                                            const int32_t* __restrict__ table, int num_pages,
+                                            const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                            int past_blocks, int T_new, int Hkv, int unit) {
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ntiles = (T_new + kP - 1) / kP;
   if (unit >= ntiles * Hkv) return;
   const int g = unit % Hkv, jn = unit / Hkv;
@@ -99,6 +103,64 @@ __global__ void __launch_bounds__(256) k_append_prefill(T* __restrict__ kpool, T
   write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
+template <typename T> __device__ __forceinline__ float ld(const T* p, long long i);
+template <> __device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// tile index query (512 threads): qtile[tau][g][d] = mean over the tile's rows and the group's
+// heads. Thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (all 2G loads in
+// flight at once); the 64 rows are then summed per dim through LDS, in row order.
+template <typename TQ>
+__device__ __forceinline__ void tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv, float* __restrict__ qtile,
+                                           int tau, int g, float (*s_rows)[kD + 1]) {
+  const int tid = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int i0 = tau * kP, n = min(T, i0 + kP) - i0;
+  const int i = tid >> 3, d0 = (tid & 7) * 16;
+  const int row = i0 + min(i, n - 1);
+  float v[kMaxGroup][16];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[h][e] = ld(q, ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0 + e);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) acc += v[h][e];
+    s_rows[i][d0 + e] = i < n ? acc : 0.f;
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float acc = 0.f;
+    for (int r = 0; r < n; ++r) acc += s_rows[r][tid];
+    qtile[((long long)tau * Hkv + g) * kD + tid] = acc / (float)(n * G);
+  }
+}
+
+// The prefill chunk's two independent first steps in one launch: workgroups [0, n_app) append
+// (eight (new block, group) units each, one per wave), the others compute one tile index query
+// each, so the two overlap instead of running back to back.
+template <typename T, bool SB>
+__global__ void __launch_bounds__(512) k_prefill_prologue(T* __restrict__ kpool, T* __restrict__ vpool,
+                                                          void* __restrict__ S, const int32_t* __restrict__ table,
+                                                          int num_pages, const T* __restrict__ k_new,
+                                                          const T* __restrict__ v_new, const T* __restrict__ q,
+                                                          int past_blocks, int T_new, int Hq, int Hkv, int n_app,
+                                                          float* __restrict__ qtile) {
+  __shared__ float s_rows[kP][kD + 1];
+  if ((int)blockIdx.x < n_app) {   // uniform per workgroup
+    append_unit<T, SB>(kpool, vpool, S, table, num_pages, k_new, v_new, past_blocks, T_new, Hkv,
+                       (int)blockIdx.x * 8 + (int)(threadIdx.x >> 6));
+    return;
+  }
+  const int e = (int)blockIdx.x - n_app, ntiles = (T_new + kP - 1) / kP;
+  tile_query<T>(q, T_new, Hq, Hkv, qtile, e % ntiles, e / ntiles, s_rows);
+}
+
 }  // namespace
 
 hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv, int max_len, hipStream_t st) {
@@ -118,20 +180,23 @@ hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv,
   return hipGetLastError();
 }
 
-hipError_t launch_append_prefill(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
-                                 int past_blocks, int T, int Hkv, hipStream_t st) {
-  const int units = ((T + kP - 1) / kP) * Hkv;
-  if (units == 0) return hipSuccess;
-  const dim3 grid((units + 3) / 4);
-#define MSA_APPEND(TT, SB)                                                                                    \
-  k_append_prefill<TT, SB><<<grid, 256, 0, st>>>((TT*)c.k, (TT*)c.v, c.S, c.table, c.num_pages, (const TT*)k_new, \
-                                                 (const TT*)v_new, past_blocks, T, Hkv)
+hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_new, const void* v_new,
+                                   const void* q, int past_blocks, int T, int Hq, int Hkv, float* qtile,
+                                   hipStream_t st) {
+  const int ntiles = (T + kP - 1) / kP;
+  if (ntiles == 0) return hipSuccess;
+  const int n_app = (ntiles * Hkv + 7) / 8;
+  const dim3 grid(n_app + ntiles * Hkv);
+#define MSA_PROLOGUE(TT, SB)                                                                                  \
+  k_prefill_prologue<TT, SB><<<grid, 512, 0, st>>>((TT*)c.k, (TT*)c.v, c.S, c.table, c.num_pages, (const TT*)k_new, \
+                                                   (const TT*)v_new, (const TT*)q, past_blocks, T, Hq, Hkv, n_app,  \
+                                                   qtile)
   if (bf16) {
-    if (c.s_bf16) MSA_APPEND(uint16_t, true); else MSA_APPEND(uint16_t, false);
+    if (c.s_bf16) MSA_PROLOGUE(uint16_t, true); else MSA_PROLOGUE(uint16_t, false);
   } else {
-    if (c.s_bf16) MSA_APPEND(float, true); else MSA_APPEND(float, false);
+    if (c.s_bf16) MSA_PROLOGUE(float, true); else MSA_PROLOGUE(float, false);
   }
-#undef MSA_APPEND
+#undef MSA_PROLOGUE
   return hipGetLastError();
 }
 
