@@ -9,10 +9,12 @@
 // blocks past a sequence's length, or on a bad page id, score -inf.
 //
 // HBM-bound streaming of the index keys (64 x 128 elements per block): a workgroup owns 4 blocks
-// of one sequence; thread -> (token t = tid/4 of the block, a quarter of its dims), and every
-// thread's loads for the 4 blocks are in flight before any arithmetic. Dot products are packed bf16 dot2 (fp32 FMAs for fp32 keys)
-// against the Hkv index queries held in LDS, reduced across the 4 lanes of a token with DPP, then
-// max-reduced with DPP over each 16-lane row (4 tokens) and through LDS over the block's 16 rows.
+// of one sequence; thread -> (tokens t = tid/8 and t + 32 of the block, an eighth of their
+// dims), so each load instruction reads whole 128 B lines, and every thread's loads for the 4
+// blocks are in flight before any arithmetic. Dot products are packed bf16 dot2 (fp32 FMAs for
+// fp32 keys) against the Hkv index queries held in LDS, summed across the 8 lanes of a token
+// with DPP, max-reduced with DPP over each 16-lane row (4 tokens) and through LDS over the
+// block's 16 rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,48 +24,39 @@ namespace {
 
 constexpr int kIB = 4;   // blocks per workgroup
 
-// A lane's quarter of one 128-dim index-key row: 16 B chunks c, c+4, c+8, ... of the row (lane c of
-// the token's 4), so the 4 lanes of a token read 64 contiguous bytes per load instruction.
-template <typename T> struct RowQuarter;
-template <> struct RowQuarter<uint16_t> {
-  uint4 w[4];   // 4 chunks of 8 bf16
-  __device__ __forceinline__ void load(const uint16_t* row, int c) {
-    const uint4* p = reinterpret_cast<const uint4*>(row);
+// One thread's share of a block: two tokens (t and t + 32) of the block, and of each token the
+// 16 B chunks c, c + 8, ... (c = lane of the token's 8), so the 8 lanes of a token read one whole
+// 128 B line per load instruction. bf16 rows are 16 chunks (2 per lane), fp32 rows 32 (4).
+template <typename T>
+struct TokenPair {
+  static constexpr int kC = kD * (int)sizeof(T) / 16 / 8;   // chunks per lane per token
+  uint4 w[2][kC];
+  __device__ __forceinline__ void load(const T* block, int t, int c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = p[c + 4 * i];
+    for (int k = 0; k < 2; ++k) {
+      const uint4* row = reinterpret_cast<const uint4*>(block + (long long)(t + 32 * k) * kD);
+#pragma unroll
+      for (int i = 0; i < kC; ++i) w[k][i] = row[c + 8 * i];
+    }
   }
-  // q: an index query in storage form (64 words of bf16 pairs) in LDS; the same chunks
-  __device__ __forceinline__ float dot(const uint32_t* q, int c) const {
+  // token k's partial dot product with an index query held in LDS in storage form
+  __device__ __forceinline__ float dot(int k, const uint32_t* q, int c) const {
     const uint4* qp = reinterpret_cast<const uint4*>(q);
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 qq = qp[c + 4 * i];
-      acc = dot2_bf16(w[i].x, qq.x, acc);
-      acc = dot2_bf16(w[i].y, qq.y, acc);
-      acc = dot2_bf16(w[i].z, qq.z, acc);
-      acc = dot2_bf16(w[i].w, qq.w, acc);
-    }
-    return acc;
-  }
-};
-template <> struct RowQuarter<float> {
-  float4 f[8];  // 8 chunks of 4 fp32
-  __device__ __forceinline__ void load(const float* row, int c) {
-    const float4* p = reinterpret_cast<const float4*>(row);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = p[c + 4 * i];
-  }
-  __device__ __forceinline__ float dot(const uint32_t* q, int c) const {
-    const float4* qp = reinterpret_cast<const float4*>(q);
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 qq = qp[c + 4 * i];
-      acc = fmaf(f[i].x, qq.x, acc);
-      acc = fmaf(f[i].y, qq.y, acc);
-      acc = fmaf(f[i].z, qq.z, acc);
-      acc = fmaf(f[i].w, qq.w, acc);
+    for (int i = 0; i < kC; ++i) {
+      const uint4 qq = qp[c + 8 * i], x = w[k][i];
+      if constexpr (sizeof(T) == 2) {
+        acc = dot2_bf16(x.x, qq.x, acc);
+        acc = dot2_bf16(x.y, qq.y, acc);
+        acc = dot2_bf16(x.z, qq.z, acc);
+        acc = dot2_bf16(x.w, qq.w, acc);
+      } else {
+        acc = fmaf(__uint_as_float(x.x), __uint_as_float(qq.x), acc);
+        acc = fmaf(__uint_as_float(x.y), __uint_as_float(qq.y), acc);
+        acc = fmaf(__uint_as_float(x.z), __uint_as_float(qq.z), acc);
+        acc = fmaf(__uint_as_float(x.w), __uint_as_float(qq.w), acc);
+      }
     }
     return acc;
   }
@@ -82,7 +75,7 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
   float* s_wm = reinterpret_cast<float*>(s_dyn + Hkv * kQW);
   const int b = blockIdx.y, j0 = blockIdx.x * kIB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid & 3, t = tid >> 2;              // lane of the token's 4, token within the block
+  const int c = tid & 7, t = tid >> 3;              // lane of the token's 8; tokens t and t + 32
   const int32_t* trow = table + (long long)b * max_blocks;
   int pg[kIB];
 #pragma unroll
@@ -96,11 +89,11 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
     }
     return;
   }
-  RowQuarter<T> kr[kIB];
+  TokenPair<T> kr[kIB];
 #pragma unroll
   for (int u = 0; u < kIB; ++u) {     // every load issued before any arithmetic (page 0: valid, unused)
     const int page = page_ok(pg[u], num_pages) ? pg[u] : 0;
-    kr[u].load(ikeys + ((long long)page * kP + t) * kD, c);
+    kr[u].load(ikeys + (long long)page * kP * kD, t, c);
   }
   {   // one 16 B load per thread for Hkv <= 16 (bf16) / 8 (fp32)
     const uint4* qsrc = reinterpret_cast<const uint4*>(q_index + (long long)b * Hkv * kD);
@@ -110,13 +103,19 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
 #pragma unroll
   for (int u = 0; u < kIB; ++u) {
     const int j = j0 + u;
-    const bool live = j < nb && page_ok(pg[u], num_pages) && kP * j + t < N;
+    const bool blk = j < nb && page_ok(pg[u], num_pages);
+    const bool live0 = blk && kP * j + t < N, live1 = blk && kP * j + t + 32 < N;
     for (int g = 0; g < Hkv; ++g) {
-      float s = kr[u].dot(s_q + g * kQW, c);
-      s += dpp_mov<0xB1>(s);         // the token's 4 lanes
-      s += dpp_mov<0x4E>(s);
-      s = row16_max(live ? s : -INFINITY);   // the 4 tokens of each 16-lane row
-      if ((lane & 15) == 0) s_wm[(u * Hkv + g) * 16 + wave * 4 + (lane >> 4)] = s;
+      float s0 = kr[u].dot(0, s_q + g * kQW, c), s1 = kr[u].dot(1, s_q + g * kQW, c);
+      s0 += dpp_mov<0xB1>(s0);       // the token's 8 lanes: quad sums, then the two quads
+      s1 += dpp_mov<0xB1>(s1);
+      s0 += dpp_mov<0x4E>(s0);
+      s1 += dpp_mov<0x4E>(s1);
+      s0 += dpp_mov<0x141>(s0);
+      s1 += dpp_mov<0x141>(s1);
+      float m = fmaxf(live0 ? s0 : -INFINITY, live1 ? s1 : -INFINITY);
+      m = fmaxf(m, dpp_mov<0x140>(m));   // the row's two 8-lane token groups: 4 tokens per row
+      if ((lane & 15) == 0) s_wm[(u * Hkv + g) * 16 + wave * 4 + (lane >> 4)] = m;
     }
   }
   __syncthreads();

@@ -318,3 +318,20 @@ def test_score_entry_point_matches_select_scores():
     msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=s2)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
+
+
+EDGE = [
+    # the largest top-k the library accepts (4096 of 5000 blocks: 256 splits, the widest merge)
+    ("bf16_k4096_max", dict(B=1, Hq=8, Hkv=2, lens=[64 * 5000 - 17], top_k=4096, dtype="bf16", permute=True)),
+    # the most KV heads (64, G = 1) and the smallest k
+    ("bf16_hkv64_k1", dict(B=2, Hq=64, Hkv=64, lens=[3000, 64], top_k=1, dtype="bf16", permute=True)),
+    # the largest group (G = 8) in fp32 with k = 1
+    ("f32_g8_k1", dict(B=2, Hq=16, Hkv=2, lens=[777, 5000], top_k=1, dtype="f32")),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_decode_step_edge_sizes(name, kw):
+    c = make_decode_case(seed=27, **kw)
+    d = to_device(c)
+    full_decode_check(d, run_decode(d))
