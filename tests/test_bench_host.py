@@ -1,0 +1,54 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU refusal, the byte count behind the
+selected-KV bandwidth, and the guard that drops the recorded HBM traffic once the scoring
+kernel's sources change."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""          # no JSON line for a refused run
+
+
+def test_selected_kv_bytes_counts_valid_tokens_of_kept_blocks():
+    # two sequences of 130 and 64 tokens: blocks of 64, 64, 2 and 64 valid tokens
+    idx = torch.tensor([[[0, 2, -1], [1, 2, 5]], [[0, -1, -1], [3, 0, -1]]], dtype=torch.int32)
+    lens = np.array([130, 64])
+    per_token = 128 * 2 * 2          # K and V, 128 dims, bf16
+    want = (64 + 2) + (64 + 2) + 64 + 64   # entry 5 and block 3 of a one-block sequence are not attended
+    assert bench.selected_kv_bytes(idx, lens) == want * per_token
+    assert bench.selected_kv_bytes(idx, lens, elem=4) == 2 * want * per_token
+
+
+def test_recorded_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    rec = bench.recorded_traffic(67706880)
+    if rec is None:
+        pytest.skip("no traffic record for the current sources")
+    assert 0.9 < rec["vs_algorithmic"] < 1.5
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    # a change to the kernel's sources voids the record
+    changed = tmp_path / "score.hip"
+    changed.write_text(open(os.path.join(ROOT, bench.SCORE_SOURCES[0])).read() + "\n// edited\n")
+    monkeypatch.setattr(bench, "SCORE_SOURCES", (str(changed),) + tuple(bench.SCORE_SOURCES[1:]))
+    assert bench.recorded_traffic(67706880) is None
+
+
+def test_sources_digest_is_stable_and_content_based(tmp_path):
+    a, b = tmp_path / "a.txt", tmp_path / "b.txt"
+    a.write_text("x")
+    b.write_text("x")
+    assert bench.sources_digest([str(a)]) == bench.sources_digest([str(b)])
+    b.write_text("y")
+    assert bench.sources_digest([str(a)]) != bench.sources_digest([str(b)])
