@@ -335,3 +335,40 @@ def test_decode_step_edge_sizes(name, kw):
     c = make_decode_case(seed=27, **kw)
     d = to_device(c)
     full_decode_check(d, run_decode(d))
+
+
+def test_graph_replays_match_eager_calls():
+    """The decode step captured in a HIP graph (as the benchmark times it) gives, on every replay
+    with eager work and synchronisations in between, exactly the eager call's outputs."""
+    c = make_decode_case(B=2, Hq=32, Hkv=8, lens=[20000, 3000], top_k=32, dtype="bf16", seed=28, permute=True)
+    d = to_device(c)
+    mb = (c.max_seq_len + 63) // 64
+    out = torch.empty_like(d.q)
+    lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
+    idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(msa.msa_workspace_size(d.cfg, msa.MSA_OP_DECODE, c.B, c.max_seq_len), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        msa.msa_decode_step(d.cfg, d.q, d.cache, c.B, c.max_seq_len, out, idx_out=idx, lse_out=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = (out.clone(), lse.clone(), idx.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.zero_(); lse.zero_(); idx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]) and torch.equal(lse, want[1]) and torch.equal(idx, want[2]), r
+        step()            # eager work between replays
+        torch.cuda.synchronize()

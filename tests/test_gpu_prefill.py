@@ -167,3 +167,41 @@ def test_prefill_full_size_sampled_tiles():
     # planted blocks are found (input-recipe sanity, not parity)
     hit = sum(int(j in res["idx"][tau, g]) for (tau, g), j in p.planted.items())
     assert hit / len(p.planted) > 0.8
+
+
+def test_prefill_graph_replays_match_eager():
+    """The prefill chunk captured in a HIP graph reproduces the eager outputs on every replay (the
+    append rewrites the same rows with the same values, so the chunk is idempotent)."""
+    p = make_prefill_case(seed=47, dtype="bf16", permute=True, Hq=32, Hkv=8, past_len=1024, T=300, top_k=4)
+    d = to_dev(p)
+    ntiles = (p.T + 63) // 64
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((p.T, p.Hq), dtype=torch.float32, device="cuda")
+    idx = torch.empty((ntiles, p.Hkv, p.top_k + 1), dtype=torch.int32, device="cuda")
+    ws = torch.empty(msa.msa_workspace_size(d["cfg"], msa.MSA_OP_PREFILL, 1, p.past_len + p.T, p.T),
+                     dtype=torch.uint8, device="cuda")
+
+    def chunk():
+        msa.msa_prefill_chunk(d["cfg"], d["q"], d["kn"], d["vn"], d["cache"], p.past_len, p.T, out, idx_out=idx,
+                              lse_out=lse, workspace=ws)
+
+    chunk()
+    torch.cuda.synchronize()
+    want = (out.clone(), lse.clone(), idx.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chunk()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chunk()
+    for r in range(3):
+        out.zero_(); lse.zero_(); idx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]) and torch.equal(lse, want[1]) and torch.equal(idx, want[2]), r
+        chunk()
+        torch.cuda.synchronize()
