@@ -37,6 +37,7 @@
  *     freed by the library and no state is kept between calls (reentrant).
  *   - `stream` is a hipStream_t passed as void* (0 = the null stream). All work is enqueued
  *     asynchronously on it; no call synchronises the host or copies device data to the host.
+ *   - batch <= MSA_MAX_BATCH (a larger batch returns MSA_ERR_UNSUPPORTED).
  *   - Arguments are validated on the host before anything is enqueued. An invalid call
  *     returns MSA_ERR_INVALID_ARG / MSA_ERR_UNSUPPORTED / MSA_ERR_WORKSPACE and enqueues
  *     nothing. A failed kernel launch returns MSA_ERR_HIP. No C++ exception crosses the ABI.
@@ -91,6 +92,7 @@ typedef enum msa_op {
 #define MSA_MAX_TOP_K 4096
 #define MSA_MAX_GROUP 8        /* Hq / Hkv */
 #define MSA_MAX_KV_HEADS 64
+#define MSA_MAX_BATCH 65535    /* sequences per decode / select / attend call */
 
 typedef struct msa_config {
     int32_t num_q_heads;      /* Hq */

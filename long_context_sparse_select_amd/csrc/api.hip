@@ -106,6 +106,7 @@ msa_status check_cache(const msa_kv_cache* cache, bool need_kv, bool need_lens) 
 
 msa_status check_batch(const msa_kv_cache* cache, int B, int max_len) {
   if (B < 0 || max_len < 0) return MSA_ERR_INVALID_ARG;
+  if (B > MSA_MAX_BATCH) return MSA_ERR_UNSUPPORTED;   // the batch is a grid dimension of 65535 at most
   if ((long long)max_len > (long long)cache->max_blocks * MSA_BLOCK) return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }
@@ -202,6 +203,7 @@ msa_status msa_workspace_size(const msa_config* cfg, int32_t op, int32_t batch, 
                               int32_t chunk_len, size_t* bytes) {
   MSA_TRY(check_config(cfg));
   if (bytes == nullptr || batch < 0 || max_seq_len < 0) return MSA_ERR_INVALID_ARG;
+  if (batch > MSA_MAX_BATCH) return MSA_ERR_UNSUPPORTED;
   switch (op) {
     case MSA_OP_SELECT:
     case MSA_OP_ATTEND:

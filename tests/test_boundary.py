@@ -118,6 +118,9 @@ def test_decode_argument_errors():
     assert call_decode(c, ok_cache, k_new=FAKE) == L.MSA_ERR_INVALID_ARG          # v_new missing
     assert call_decode(c, ok_cache, B=-1) == L.MSA_ERR_INVALID_ARG
     assert call_decode(c, ok_cache, max_len=16 * 64 + 1) == L.MSA_ERR_INVALID_ARG  # beyond the table
+    assert call_decode(c, ok_cache, B=65536) == L.MSA_ERR_UNSUPPORTED               # beyond the grid limit
+    assert ws_size(c, L.MSA_OP_DECODE, B=65536)[0] == L.MSA_ERR_UNSUPPORTED
+    assert ws_size(c, L.MSA_OP_DECODE, B=65535, max_len=1024)[0] == L.MSA_OK
     assert call_decode(c, fake_cache(k_pages=None)) == L.MSA_ERR_INVALID_ARG
     assert call_decode(c, fake_cache(seq_lens=None)) == L.MSA_ERR_INVALID_ARG
     assert call_decode(c, fake_cache(max_blocks=0)) == L.MSA_ERR_INVALID_ARG
