@@ -372,3 +372,21 @@ def test_graph_replays_match_eager_calls():
         assert torch.equal(out, want[0]) and torch.equal(lse, want[1]) and torch.equal(idx, want[2]), r
         step()            # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_full_size_decode_1m_with_append():
+    """The benchmark's timed configuration: the 1M-token step with the new token's K/V appended
+    (its block's summary and score recomputed inside the top-k kernel), checked end to end against
+    the oracle run on the cache after the append."""
+    kw = workload("decode_bf16_1m_paged", seed=0)
+    c = make_decode_case_torch(**kw)
+    d = to_device(c)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    kn = torch.randn((c.B, c.Hkv, c.D), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((c.B, c.Hkv, c.D), generator=g, device="cuda").to(torch.bfloat16)
+    res = run_decode(d, k_new=kn, v_new=vn)
+    full_decode_check(d, res)
+    t = int(c.seq_lens[0]) - 1
+    page = int(c.block_table[0, t // 64])
+    assert torch.equal(d.k[page, :, t % 64], kn[0]) and torch.equal(d.v[page, :, t % 64], vn[0])
