@@ -2,10 +2,12 @@
 even; every score uses the stored bf16 summary) against the CPU oracle, through the C ABI.
 
 Tolerance: the oracle rounds the exact mean once; the GPU rounds its fp32 mean, which can land on
-the neighbouring bf16 value when the exact mean sits next to a rounding boundary. Each stored
-summary must therefore be the rounded mean or one bf16 step from it, and a block's score may move
-by the observed difference E_j = sum_d |q_idx,d| * |S_gpu,j,d - S_ref,j,d| on top of the fp32
-arithmetic term of the fp32 pool. The index-set band widens by max_j E_j for the same reason.
+the neighbouring bf16 value when the exact mean sits next to a rounding boundary, or further when
+the fp32 sum's own error exceeds the bf16 step of a near-zero mean (fp32 keys). Each stored
+summary must therefore lie within one bf16 step plus the fp32 mean's error bound of the rounded
+mean, and a block's score may move by the observed difference
+E_j = sum_d |q_idx,d| * |S_gpu,j,d - S_ref,j,d| on top of the fp32 arithmetic term of the fp32 pool.
+The index-set band widens by max_j E_j for the same reason.
 """
 import numpy as np
 import pytest
@@ -16,6 +18,7 @@ import oracle
 from synth import make_decode_case, make_decode_case_torch, make_prefill_case, round_to_bf16, storage
 from gpu_util import (Dev, SCORE_RTOL, assert_close, bf16_step, check_index_sets, dev_tensor, host_f64,
                       host_store, oracle_inputs, require_gpu, run_decode)
+from helpers import as_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -40,22 +43,39 @@ def to_device_bf16(case) -> Dev:
     return Dev(case, q, k, v, table, lens, S, cfg, cache)
 
 
+def fp32_mean_error(k_store, table, lens, Hkv, D, mb):
+    """Bound on |fp32 mean - exact mean| of each block summary: (n + 2) * 2^-24 * sum_t |k_t| / n
+    over the block's n valid keys (fp32 summation and the division). [B][mb][Hkv][D]."""
+    ak = np.abs(as_f64(k_store)).astype(np.float32)
+    out = np.zeros((len(lens), mb, Hkv, D))
+    for b, N in enumerate(lens):
+        N = int(N)
+        nb = (N + 63) // 64
+        full = N // 64
+        if full:
+            out[b, :full] = ak[table[b, :full]].sum(axis=2, dtype=np.float64) * (66.0 / 64.0)
+        if nb > full:
+            n = N - 64 * full
+            out[b, full] = ak[table[b, full], :, :n].sum(axis=1, dtype=np.float64) * ((n + 2.0) / n)
+    return out * 2.0 ** -24
+
+
 def summary_check(d, inputs):
     """Stored bf16 summaries against the oracle's rounded means: returns (S_ref, |S_gpu - S_ref|)
-    as [B][max_blocks][Hkv][D] (zero past each sequence's blocks)."""
+    as [B][max_blocks][Hkv][D] (zero past each sequence's blocks). Both sides round monotonically,
+    so they differ by at most the fp32 mean's own error plus one bf16 step at the larger value."""
     c = d.case
     S_ref = oracle.summaries(k_pool=inputs["k_pool"], block_table=c.block_table, seq_lens=c.seq_lens, Hkv=c.Hkv,
                              D=c.D, P=c.P, summary_dtype="bf16")
+    err = fp32_mean_error(inputs["k_pool"], c.block_table, c.seq_lens, c.Hkv, c.D, S_ref.shape[1])
     S_gpu = host_f64(d.S)
     diff = np.zeros_like(S_ref)
     for b in range(c.B):
         nb = (int(c.seq_lens[b]) + 63) // 64
         g = S_gpu[c.block_table[b, :nb]]
         diff[b, :nb] = np.abs(g - S_ref[b, :nb])
-        assert np.all(diff[b, :nb] <= bf16_step(S_ref[b, :nb])), "a summary is more than one bf16 step off (b=%d)" % b
-    n_off = int((diff > 0).sum())
-    total = sum((int(n) + 63) // 64 for n in c.seq_lens) * c.Hkv * c.D
-    assert n_off <= max(8, total // 1000), "%d of %d summary values off by one step" % (n_off, total)
+        allowed = bf16_step(np.maximum(np.abs(S_ref[b, :nb]), np.abs(g))) + err[b, :nb]
+        assert np.all(diff[b, :nb] <= allowed), "a summary is beyond one bf16 step + fp32 error (b=%d)" % b
     return S_ref, diff
 
 
