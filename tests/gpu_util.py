@@ -153,9 +153,12 @@ def check_band(chosen, r, keff, bound_max, keep_sink=0, keep_local=0, where="", 
     if kr <= 0:
         return
     tau = np.sort(rest)[::-1][kr - 1]
-    w = SCORE_RTOL * max(abs(tau), bound_max) + slack
-    must = j[~forced][rest > tau + w]
-    never = j[~forced][rest < tau - w]
+    if np.isneginf(tau):   # fewer finite candidates than slots: every finite one must be kept
+        must, never = j[~forced][np.isfinite(rest)], np.zeros(0, np.int64)
+    else:
+        w = SCORE_RTOL * max(abs(tau), bound_max) + slack
+        must = j[~forced][rest > tau + w]
+        never = j[~forced][rest < tau - w]
     assert set(must) <= set(chosen), "band: a clearly-in block is missing " + where
     assert not (set(never) & set(chosen)), "band: a clearly-out block was selected " + where
 
