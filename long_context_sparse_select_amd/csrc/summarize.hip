@@ -103,14 +103,8 @@ __device__ __forceinline__ void append_unit(T* __restrict__ kpool, T* __restrict
   write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
-template <typename T> __device__ __forceinline__ float ld(const T* p, long long i);
-template <> __device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
-template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
-}
-
 // tile index query (512 threads): qtile[tau][g][d] = mean over the tile's rows and the group's
-// heads. Thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (all 2G loads in
+// heads. Thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (2G 16 B loads in
 // flight at once); the 64 rows are then summed per dim through LDS, in row order.
 template <typename TQ>
 __device__ __forceinline__ void tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv, float* __restrict__ qtile,
@@ -120,19 +114,28 @@ __device__ __forceinline__ void tile_query(const TQ* __restrict__ q, int T, int 
   const int i0 = tau * kP, n = min(T, i0 + kP) - i0;
   const int i = tid >> 3, d0 = (tid & 7) * 16;
   const int row = i0 + min(i, n - 1);
-  float v[kMaxGroup][16];
+  Vec8<TQ> v[kMaxGroup][2];   // the row's 16 dims of each head: 16 B vector loads, all in flight
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[h][e] = ld(q, ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0 + e);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float acc = 0.f;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) acc += v[h][e];
-    s_rows[i][d0 + e] = i < n ? acc : 0.f;
+  for (int h = 0; h < kMaxGroup; ++h) {
+    const TQ* src = q + ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0;
+    v[h][0].load(src);
+    v[h][1].load(src + 8);
   }
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      float f[16];
+      v[h][0].to_f32(f);
+      v[h][1].to_f32(f + 8);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += f[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s_rows[i][d0 + e] = i < n ? acc[e] : 0.f;
   __syncthreads();
   if (tid < kD) {
     float acc = 0.f;
