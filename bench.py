@@ -97,8 +97,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
-                    help="counter pass: eager launches of the scoring kernel over the rotating caches and of a "
-                         "256 MiB device copy (the byte-count calibration), for rocprofv3 --pmc; no timing")
+                    help="counter pass: eager launches of the scoring kernel over the rotating caches, of the "
+                         "k = 1024 attend and of the index-branch select, then of a 256 MiB device copy (the "
+                         "byte-count calibration), for rocprofv3 --pmc; no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -269,13 +270,46 @@ def counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
         msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
     for i in range(n):
         msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
+    # the k = 1024 operating point: one selection per cache, then eager attends over those lists
+    # (k_attend_decode_mfma + k_merge dispatches; the selections add k_score_decode dispatches
+    # of the same work)
+    import numpy as np
+    bf16 = int(cfg.q_dtype) == msa.MSA_BF16
+    cfg_k = msa.make_config(int(cfg.num_q_heads), int(cfg.num_kv_heads), 1024, dtype="bf16" if bf16 else "f32",
+                            softmax_scale=float(cfg.softmax_scale))
+    Hq, Hkv = int(cfg.num_q_heads), int(cfg.num_kv_heads)
+    idx = [torch.empty((B, Hkv, 1024), dtype=torch.int32, device=dev) for _ in range(L)]
+    for l in range(L):
+        msa.msa_select(cfg_k, q_ring[l % R], caches[l], B, max_len, idx[l])
+    out = torch.empty((B, Hq, 128), dtype=q_ring[0].dtype, device=dev)
+    for i in range(n):
+        msa.msa_attend(cfg_k, q_ring[i % R], caches[i % L], B, max_len, idx[i % L], out)
+    torch.cuda.synchronize()
+    attend_bytes = float(np.mean([selected_kv_bytes(idx[l], caches[l].seq_lens.cpu().numpy(), elem=2 if bf16 else 4)
+                                  for l in range(L)]))
+    # the index branch on two 1M-token index-key caches (k_score_index dispatches)
+    from synth import make_index_case_torch
+    icases = [make_index_case_torch(B=1, Hkv=8, lens=[1 << 20], top_k=64, dtype="bf16", permute=True,
+                                    plant=("count", 16), seed=args.seed + 1000 * l, device=dev) for l in range(2)]
+    icfg = msa.make_config(8, 8, 64, dtype="bf16")
+    itabs = [(torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)) for c in icases]
+    iidx = torch.empty((1, 8, 64), dtype=torch.int32, device=dev)
+    for i in range(n):
+        c = icases[i % 2]
+        msa.msa_select_index(icfg, c.q_idx, c.index_keys, itabs[i % 2][0], itabs[i % 2][1], 1, c.max_seq_len, iidx)
+    torch.cuda.synchronize()
+    nbi = (icases[0].max_seq_len + 63) // 64
+    index_bytes = nbi * 64 * 128 * 2 + nbi * 4 + 8 * 128 * 2 + 8 * nbi * 4
+    del icases
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L, "copy_launches": 4,
+    print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L + L, "attend_launches": n,
+                      "attend_bytes_per_launch": attend_bytes, "index_launches": n,
+                      "index_score_bytes_per_launch": index_bytes, "copy_launches": 4,
                       "copy_bytes": COPY_BYTES}), flush=True)
 
 
