@@ -2,7 +2,7 @@
  * msa.h -- C ABI of libmsa: two-stage GQA block-sparse attention on MI355X (gfx950).
  *
  * The method: "MiniMax goes sparse: decoding M3's attention from a single diagram"
- * (atlascloud.ai blog), §1 "What the diagram shows".
+ * (atlascloud.ai blog; cited below as [MGS]), §1 "What the diagram shows".
  *   Step 1 (index branch): each GQA group scores the context's fixed-size blocks with one
  *     index query and keeps its top-k blocks -> one short index list per group and layer.
  *   Step 2 (sparse branch): every query head of the group runs ordinary softmax attention over
