@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
     return;
   }
   summary_loads(0);
-  {  // [MGS §1 Step 1] one index query per group: mean of the group's heads, computed while
+  {  // §1 Step 1 of the page: one index query per group (the mean of its heads), computed while
      // the summaries stream in. Thread -> (group, 8 dims): its G head rows are 16 B vector loads.
     const int G = Hq / Hkv;
     const TQ* qb = q + (long long)b * Hq * kD;
