@@ -160,7 +160,7 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
  *   q_index     [batch][Hkv][index_dim] q_dtype
  *   index_keys  [num_pages][64][index_dim] kv_dtype (page p holds the index keys of the
  *               block that block_table maps to p)
- *   index_dim   128 (anything else: MSA_ERR_UNSUPPORTED)
+ *   index_dim   64 or 128 (other positive values: MSA_ERR_UNSUPPORTED)
  *   cache       only block_table, seq_lens, num_pages and max_blocks are read; K/V and
  *               summaries may be null
  *   scores_out  nullable [batch][Hkv][ceil(max_seq_len/64)] float32

@@ -267,14 +267,15 @@ msa_status msa_select_index(const msa_config* cfg, const void* q_index, const vo
   MSA_TRY(check_batch(cache, batch, max_seq_len));
   if (q_index == nullptr || index_keys == nullptr || idx_out == nullptr) return MSA_ERR_INVALID_ARG;
   if (index_dim < 1) return MSA_ERR_INVALID_ARG;
-  if (index_dim != kD) return MSA_ERR_UNSUPPORTED;
+  if (index_dim != 64 && index_dim != 128) return MSA_ERR_UNSUPPORTED;
   const Layout L = decode_layout(cfg, MSA_OP_SELECT, batch, max_seq_len);
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
-  MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, cache_args(cfg, cache), batch,
-                                        cfg->num_kv_heads, max_seq_len, scores, L.row_stride, st)));
+  MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, index_dim,
+                                        cache_args(cfg, cache), batch, cfg->num_kv_heads, max_seq_len, scores,
+                                        L.row_stride, st)));
   return run_topk(cfg, nullptr, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
                   st);
 }

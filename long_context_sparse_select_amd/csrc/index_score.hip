@@ -10,7 +10,7 @@
 //
 // HBM-bound streaming of the index keys (64 x 128 elements per block): a workgroup owns 4 blocks
 // of one sequence; thread -> (tokens t = tid/8 and t + 32 of the block, an eighth of their
-// dims), so each load instruction reads whole 128 B lines, and every thread's loads for the 4
+// dims), so each load instruction reads whole 128 B lines (index dimension 64 or 128), and every thread's loads for the 4
 // blocks are in flight before any arithmetic. Dot products are packed bf16 dot2 (fp32 FMAs for
 // fp32 keys) against the Hkv index queries held in LDS, summed across the 8 lanes of a token
 // with DPP, max-reduced with DPP over each 16-lane row (4 tokens) and through LDS over the
@@ -27,14 +27,14 @@ constexpr int kIB = 4;   // blocks per workgroup
 // One thread's share of a block: two tokens (t and t + 32) of the block, and of each token the
 // 16 B chunks c, c + 8, ... (c = lane of the token's 8), so the 8 lanes of a token read one whole
 // 128 B line per load instruction. bf16 rows are 16 chunks (2 per lane), fp32 rows 32 (4).
-template <typename T>
+template <typename T, int DI>
 struct TokenPair {
-  static constexpr int kC = kD * (int)sizeof(T) / 16 / 8;   // chunks per lane per token
+  static constexpr int kC = DI * (int)sizeof(T) / 16 / 8;   // chunks per lane per token
   uint4 w[2][kC];
   __device__ __forceinline__ void load(const T* block, int t, int c) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint4* row = reinterpret_cast<const uint4*>(block + (long long)(t + 32 * k) * kD);
+      const uint4* row = reinterpret_cast<const uint4*>(block + (long long)(t + 32 * k) * DI);
 #pragma unroll
       for (int i = 0; i < kC; ++i) w[k][i] = row[c + 8 * i];
     }
@@ -62,7 +62,7 @@ struct TokenPair {
   }
 };
 
-template <typename T>
+template <typename T, int DI>
 __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_index, const T* __restrict__ ikeys,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ lens, int num_pages,
@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
                                                      float* __restrict__ scores, int row_stride) {
   // [Hkv][128] index queries in storage form (bf16 pairs or fp32), then [kIB][Hkv][16] row maxima
   extern __shared__ uint32_t s_dyn[];
-  constexpr int kQW = kD * sizeof(T) / 4;           // 32-bit words per index query
+  constexpr int kQW = DI * sizeof(T) / 4;           // 32-bit words per index query
   uint32_t* s_q = s_dyn;
   float* s_wm = reinterpret_cast<float*>(s_dyn + Hkv * kQW);
   const int b = blockIdx.y, j0 = blockIdx.x * kIB;
@@ -89,14 +89,14 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
     }
     return;
   }
-  TokenPair<T> kr[kIB];
+  TokenPair<T, DI> kr[kIB];
 #pragma unroll
   for (int u = 0; u < kIB; ++u) {     // every load issued before any arithmetic (page 0: valid, unused)
     const int page = page_ok(pg[u], num_pages) ? pg[u] : 0;
-    kr[u].load(ikeys + (long long)page * kP * kD, t, c);
+    kr[u].load(ikeys + (long long)page * kP * DI, t, c);
   }
   {   // one 16 B load per thread for Hkv <= 16 (bf16) / 8 (fp32)
-    const uint4* qsrc = reinterpret_cast<const uint4*>(q_index + (long long)b * Hkv * kD);
+    const uint4* qsrc = reinterpret_cast<const uint4*>(q_index + (long long)b * Hkv * DI);
     for (int e = tid; e < Hkv * kQW / 4; e += 256) reinterpret_cast<uint4*>(s_q)[e] = qsrc[e];
   }
   __syncthreads();
@@ -132,20 +132,22 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
 
 }  // namespace
 
-hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, const CacheArgs& c, int B,
-                              int Hkv, int max_len, float* scores, int row_stride, hipStream_t st) {
+hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, int index_dim,
+                              const CacheArgs& c, int B, int Hkv, int max_len, float* scores, int row_stride,
+                              hipStream_t st) {
   if (B == 0 || row_stride == 0) return hipSuccess;
   const dim3 grid((row_stride + kIB - 1) / kIB, B);
+  // LDS: the Hkv index queries in storage form, then the [kIB][Hkv][16] row maxima
+  const size_t lds = (size_t)Hkv * index_dim * (bf16 ? 2 : 4) + (size_t)kIB * Hkv * 16 * sizeof(float);
+#define MSA_INDEX(TT, DD)                                                                                 \
+  k_score_index<TT, DD><<<grid, 256, lds, st>>>((const TT*)q_index, (const TT*)index_keys, c.table, c.lens, \
+                                                c.num_pages, c.max_blocks, Hkv, max_len, scores, row_stride)
   if (bf16) {
-    const size_t lds = (size_t)Hkv * (kD / 2) * 4 + (size_t)kIB * Hkv * 16 * sizeof(float);
-    k_score_index<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)q_index, (const uint16_t*)index_keys, c.table,
-                                                    c.lens, c.num_pages, c.max_blocks, Hkv, max_len, scores,
-                                                    row_stride);
+    if (index_dim == 64) MSA_INDEX(uint16_t, 64); else MSA_INDEX(uint16_t, 128);
   } else {
-    const size_t lds = (size_t)Hkv * kD * 4 + (size_t)kIB * Hkv * 16 * sizeof(float);
-    k_score_index<float><<<grid, 256, lds, st>>>((const float*)q_index, (const float*)index_keys, c.table, c.lens,
-                                                 c.num_pages, c.max_blocks, Hkv, max_len, scores, row_stride);
+    if (index_dim == 64) MSA_INDEX(float, 64); else MSA_INDEX(float, 128);
   }
+#undef MSA_INDEX
   return hipGetLastError();
 }
 

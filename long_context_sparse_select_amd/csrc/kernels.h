@@ -29,10 +29,11 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
 // ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats each.
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
                                int max_len, float* scores, int row_stride, hipStream_t st);
-// index branch (single-head index keys [num_pages][64][128], q_index [B][Hkv][128]): block score
-// = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
-hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, const CacheArgs& c, int B,
-                              int Hkv, int max_len, float* scores, int row_stride, hipStream_t st);
+// index branch (single-head index keys [num_pages][64][index_dim], q_index [B][Hkv][index_dim],
+// index_dim 64 or 128): block score = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
+hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, int index_dim,
+                              const CacheArgs& c, int B, int Hkv, int max_len, float* scores, int row_stride,
+                              hipStream_t st);
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st);
 

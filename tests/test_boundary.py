@@ -160,7 +160,7 @@ def test_prefill_errors():
 
 def test_select_index_errors():
     """The index branch reads only the table, lengths and page count of the cache; index_dim
-    other than 128 is unsupported; score_mode is not read."""
+    other than 64 or 128 is unsupported; score_mode is not read."""
     lib = L.load_library()
     bare = fake_cache(k_pages=None, v_pages=None, summaries=None)
 
@@ -172,7 +172,8 @@ def test_select_index_errors():
     assert call(ik=None) == L.MSA_ERR_INVALID_ARG
     assert call(idx=None) == L.MSA_ERR_INVALID_ARG
     assert call(di=0) == L.MSA_ERR_INVALID_ARG
-    assert call(di=64) == L.MSA_ERR_UNSUPPORTED
+    assert call(di=96) == L.MSA_ERR_UNSUPPORTED
+    assert call(di=64, B=0) == L.MSA_OK          # 64 and 128 are both accepted
     assert call(cache=fake_cache(seq_lens=None)) == L.MSA_ERR_INVALID_ARG
     assert call(cache=fake_cache(block_table=None)) == L.MSA_ERR_INVALID_ARG
     assert call(max_len=16 * 64 + 1) == L.MSA_ERR_INVALID_ARG

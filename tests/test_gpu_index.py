@@ -36,6 +36,9 @@ SMALL = [
     # wide groups: index queries staged in several passes (bf16 32 groups, fp32 64 groups)
     ("bf16_g32", dict(B=2, Hkv=32, lens=[5000, 130], top_k=8, dtype="bf16")),
     ("f32_g64", dict(B=1, Hkv=64, lens=[3000], top_k=4, dtype="f32")),
+    # 64-dim index keys
+    ("bf16_di64_ragged", dict(B=3, Hkv=8, lens=[9000, 130, 4097], top_k=16, dtype="bf16", permute=True, Di=64)),
+    ("f32_di64_g4", dict(B=2, Hkv=4, lens=[5000, 64], top_k=8, dtype="f32", Di=64)),
 ]
 
 

@@ -82,7 +82,8 @@ def test_random_index_select(i):
     sink, local = int(r.integers(0, 3)), int(r.integers(0, 3))
     k = int(max(sink + local, 1, r.integers(1, 600)))
     c = make_index_case(seed=9900 + i, B=B, Hkv=Hkv, lens=lens, top_k=k, dtype=str(r.choice(["f32", "bf16"])),
-                        permute=bool(r.random() < 0.5), plant=("count", int(r.integers(0, 4))))
+                        permute=bool(r.random() < 0.5), plant=("count", int(r.integers(0, 4))),
+                        Di=int(r.choice([64, 128])))
     table = c.block_table.copy()
     if r.random() < 0.5 and c.num_pages > 4:       # a few bad page ids inside the sequences
         for _ in range(3):
