@@ -183,7 +183,9 @@ msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
 
 /* One decode step ([MGS §1 Steps 1-2]; [MGS §3] decode). If k_new is given, first write
  * k_new/v_new [batch][Hkv][128] into position seq_lens[b]-1 of each sequence (its page must
- * already be in block_table) and recompute that block's summary. Then Step 1 and Step 2.
+ * already be in block_table) and recompute that block's summary; a sequence of length 0 takes
+ * no token, and a page id out of range is never written. Then Step 1 and Step 2, with that
+ * block scored from its new summary.
  * idx_out / scores_out / lse_out are nullable. */
 msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_cache* cache,
                            int32_t batch, int32_t max_seq_len, const void* k_new,

@@ -3,7 +3,7 @@
 //
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
-//   msa_decode_step   score -> top-k (+ append: new K/V row, that block's summary and score)
+//   msa_decode_step   [append: new K/V row, that block's summary and score | score] (one launch) -> top-k
 //                     -> attend -> split-K merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend
@@ -124,12 +124,10 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
     if (s_ != MSA_OK) return s_;             \
   } while (0)
 
-// Step 1 on validated arguments; pages (page ids of the kept blocks) and the appended token
-// (k_new / v_new, nullable) are the decode step's extras
-msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
-                    float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
-                    const void* v_new, hipStream_t st) {
-  const bool bf16 = cfg->q_dtype == MSA_BF16;
+// top-k of decode score rows on validated arguments; pages (page ids of the kept blocks,
+// nullable) is the decode step's extra
+msa_status run_topk(const msa_config* cfg, const msa_kv_cache* cache, int B, int max_len, float* scores,
+                    int row_stride, int32_t* idx, int32_t* pages, hipStream_t st) {
   TopkArgs t{};
   t.scores = scores;
   t.row_stride = row_stride;
@@ -147,23 +145,17 @@ msa_status run_topk(const msa_config* cfg, const void* q, const msa_kv_cache* ca
   t.table = cache->block_table;
   t.max_blocks = cache->max_blocks;
   t.num_pages = cache->num_pages;
-  t.k_new = k_new;
-  t.v_new = v_new;
-  t.kpool = cache->k_pages;
-  t.vpool = cache->v_pages;
-  t.S = cache->summaries;
-  t.s_bf16 = cfg->summary_dtype == MSA_BF16;
-  t.q = q;
-  t.Hq = cfg->num_q_heads;
-  return hip_status(launch_topk(t, bf16, st));
+  return hip_status(launch_topk(t, st));
 }
 
+// Step 1 on validated arguments; the appended token (k_new / v_new, nullable) goes into the
+// scoring launch
 msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
                       float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
                       const void* v_new, hipStream_t st) {
   MSA_TRY(hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), B, cfg->num_q_heads,
-                                         cfg->num_kv_heads, max_len, scores, row_stride, st)));
-  return run_topk(cfg, q, cache, B, max_len, scores, row_stride, idx, pages, k_new, v_new, st);
+                                         cfg->num_kv_heads, max_len, scores, row_stride, k_new, v_new, st)));
+  return run_topk(cfg, cache, B, max_len, scores, row_stride, idx, pages, st);
 }
 
 // Step 2 on validated arguments
@@ -239,7 +231,7 @@ msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* c
   if (batch == 0) return MSA_OK;
   const int row_stride = (max_seq_len + MSA_BLOCK - 1) / MSA_BLOCK;
   return hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), batch, cfg->num_q_heads,
-                                        cfg->num_kv_heads, max_seq_len, scores_out, row_stride,
+                                        cfg->num_kv_heads, max_seq_len, scores_out, row_stride, nullptr, nullptr,
                                         (hipStream_t)stream));
 }
 
@@ -276,8 +268,7 @@ msa_status msa_select_index(const msa_config* cfg, const void* q_index, const vo
   MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, index_dim,
                                         cache_args(cfg, cache), batch, cfg->num_kv_heads, max_seq_len, scores,
                                         L.row_stride, st)));
-  return run_topk(cfg, nullptr, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
-                  st);
+  return run_topk(cfg, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, st);
 }
 
 msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
@@ -351,8 +342,7 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   t.base_blocks = past_blocks;
   t.keep_sink = cfg->keep_sink;
   t.keep_local = cfg->keep_local;
-  t.k_new = nullptr;   // TopkArgs{} zero-initialises the decode-only fields; no append in prefill
-  MSA_TRY(hip_status(launch_topk(t, true, st)));
+  MSA_TRY(hip_status(launch_topk(t, st)));
   PrefillArgs p{};
   p.q = q;
   p.kpool = cache->k_pages;

@@ -27,8 +27,12 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
                                    hipStream_t st);
 
 // ---- Step 1 scoring. scores rows are (b, g) [decode] or (tile, g) [prefill], row_stride floats each.
+// k_new / v_new (nullable, [B][Hkv][128]): the decode step's new token, already counted in seq_lens.
+// The same launch writes its K/V row at position seq_len-1, recomputes that block's summary from
+// its keys and scores the block from the stored summary.
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
-                               int max_len, float* scores, int row_stride, hipStream_t st);
+                               int max_len, float* scores, int row_stride, const void* k_new, const void* v_new,
+                               hipStream_t st);
 // index branch (single-head index keys [num_pages][64][index_dim], q_index [B][Hkv][index_dim],
 // index_dim 64 or 128): block score = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
 hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, int index_dim,
@@ -39,7 +43,7 @@ hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past
 
 // ---- Step 1 top-k
 struct TopkArgs {
-  float* scores;       // the decode append path rewrites the last block's score
+  float* scores;
   int row_stride;
   int32_t* idx;
   int idx_stride;      // top_k (decode) or top_k + 1 (prefill)
@@ -59,18 +63,8 @@ struct TopkArgs {
   const int32_t* table;
   int max_blocks;
   int num_pages;
-  // decode append (nullable k_new): write k_new/v_new [B][Hkv][128] at position seq_len-1,
-  // recompute that block's summary in S and its score for the row's group before selecting
-  const void* k_new;
-  const void* v_new;
-  void* kpool;
-  void* vpool;
-  void* S;              // summaries, float or bf16 (s_bf16)
-  bool s_bf16;
-  const void* q;
-  int Hq;
 };
-hipError_t launch_topk(const TopkArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 // ---- Step 2, decode
 struct AttendArgs {

@@ -15,6 +15,13 @@
 // is in flight. The chunk's scores are staged in LDS and leave as one contiguous run per row.
 // The number of KV heads is a template parameter for the power-of-two cases, so the pair-index
 // arithmetic is shifts, not divisions.
+//
+// A decode step's new token is appended by the same launch: Hkv more workgroups per sequence
+// (dispatched first) each write the token's K/V row of one group, recompute the summary of its
+// block from the block's keys, and score that block from the stored summary, while the chunk
+// workgroups stream the other summaries and leave that one score alone. Every score the top-k
+// kernel then reads describes the cache after the append (§1 Step 1: blocks are scored through
+// their summaries).
 #include "common.h"
 #include "kernels.h"
 
@@ -37,18 +44,110 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
 }
 
 
+// The decode step's new token, for sequence b and group g (one 256-thread workgroup): its K/V
+// row goes to position N-1 of its block; the block's summary becomes the mean of its older rows
+// and the new key (bf16 pools store it rounded); the block's score is <index query, stored
+// summary>. Thread -> rows r, r+16, r+32, r+48 (r = tid/16) of the block, 8 dims; its four row
+// loads are issued together, and the K/V store goes to a row nothing in this launch reads.
+// s_red: 4 x 128 + 2 floats of LDS.
+template <typename T, bool SB>
+__device__ __forceinline__ void decode_append(const T* __restrict__ q, const T* __restrict__ k_new,
+                                              const T* __restrict__ v_new, T* __restrict__ kpool,
+                                              T* __restrict__ vpool, void* __restrict__ S,
+                                              const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
+                                              int num_pages, int max_blocks, int Hq, int Hkv, int max_len,
+                                              float* __restrict__ scores, int row_stride, int b, int g,
+                                              float* s_red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = clamp_len(lens[b], max_len);
+  if (N == 0 || num_pages <= 0) return;   // uniform: no block (an empty pool scores -inf elsewhere)
+  const int t = N - 1, jl = t / kP, slot = t % kP;
+  const int page = table[(long long)b * max_blocks + jl];
+  float* dst = scores + ((long long)b * Hkv + g) * row_stride + jl;
+  if (!page_ok(page, num_pages)) {   // uniform: nothing is stored, and the block is never attended
+    if (tid == 0) *dst = -INFINITY;
+    return;
+  }
+  const int r0 = tid >> 4, d0 = (tid & 15) * 8;
+  const long long head = ((long long)page * Hkv + g) * kP * kD;
+  const long long nrow = ((long long)b * Hkv + g) * kD + d0;
+  Vec8<T> rows[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // rows past the new one re-read the new key (a valid address; unused)
+    const int r = r0 + 16 * i;
+    rows[i].load(r < slot ? kpool + head + (long long)r * kD + d0 : k_new + nrow);
+  }
+  if (r0 == (slot & 15)) {   // the 16 lanes of the new row's thread group
+    Vec8<T> kn, vn;
+    kn.load(k_new + nrow);
+    vn.load(v_new + nrow);
+    kn.store(kpool + head + (long long)slot * kD + d0);
+    vn.store(vpool + head + (long long)slot * kD + d0);
+  }
+  const int G = Hq / Hkv;
+  float qv[kMaxGroup];
+  if (tid < kD) {   // the group's query heads at dim tid
+    const T* qb = q + ((long long)b * Hq + g * G) * kD + tid;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if constexpr (sizeof(T) == 2) qv[h] = __uint_as_float((uint32_t)qb[(long long)min(h, G - 1) * kD] << 16);
+      else qv[h] = qb[(long long)min(h, G - 1) * kD];
+    }
+  }
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (r0 + 16 * i <= slot) rows[i].add_to(acc);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = across_rows_sum(acc[e]);   // the wave's four row groups
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_red[wave * kD + d0 + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float summary = (s_red[tid] + s_red[kD + tid] + s_red[2 * kD + tid] + s_red[3 * kD + tid]) / (float)(slot + 1);
+    const long long si = ((long long)page * Hkv + g) * kD + tid;
+    if constexpr (SB) {   // the score uses the value the pool holds
+      const uint32_t h = pack_bf16x2(summary, 0.f) & 0xffffu;
+      reinterpret_cast<uint16_t*>(S)[si] = (uint16_t)h;
+      summary = bf16lo(h);
+    } else {
+      reinterpret_cast<float*>(S)[si] = summary;
+    }
+    float qi = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      if (h < G) qi += qv[h];
+    const float prod = across_rows_sum(row16_sum((qi / (float)G) * summary));
+    if (lane == 0) s_red[4 * kD + wave] = prod;
+  }
+  __syncthreads();
+  if (tid == 0) *dst = s_red[4 * kD] + s_red[4 * kD + 1];
+}
+
 // HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
 // shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
+// Workgroups x < napp (napp = Hkv with a new token, else 0) append, writing the pool through
+// S_app (the same pool as S, which only the scoring workgroups read); the others score chunks.
 template <typename TQ, int HKV, bool SB>
 __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const void* __restrict__ S,
                                                       const int32_t* __restrict__ table,
                                                       const int32_t* __restrict__ lens, int num_pages,
                                                       int max_blocks, int Hq, int hkv_arg, int max_len,
-                                                      float* __restrict__ scores, int row_stride) {
+                                                      float* __restrict__ scores, int row_stride,
+                                                      const TQ* __restrict__ k_new, const TQ* __restrict__ v_new,
+                                                      TQ* __restrict__ kpool, TQ* __restrict__ vpool, void* S_app,
+                                                      int napp) {
   const int Hkv = HKV > 0 ? HKV : hkv_arg;
   extern __shared__ float s_qidx[];             // [Hkv][128] index queries, then [Hkv][kChunk] scores
   const int b = blockIdx.y;
-  const int j0 = blockIdx.x * kChunk;
+  if ((int)blockIdx.x < napp) {   // uniform per workgroup
+    decode_append<TQ, SB>(q, k_new, v_new, kpool, vpool, S_app, table, lens, num_pages, max_blocks, Hq, Hkv, max_len,
+                          scores, row_stride, b, (int)blockIdx.x, s_qidx);
+    return;
+  }
+  const int j0 = ((int)blockIdx.x - napp) * kChunk;
   const int tid = threadIdx.x;
   const int jend = min(j0 + kChunk, row_stride);
   constexpr int kLanes = SB ? 16 : 32;   // lanes per (block, group) pair, 16 B each
@@ -176,10 +275,12 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
     }
   }
   __syncthreads();
-  // each row's chunk of scores leaves as one contiguous run
+  // each row's chunk of scores leaves as one contiguous run; with a new token, its block's score
+  // is the append workgroup's
+  const int jskip = napp > 0 ? nb - 1 : -1;
   for (int e = tid; e < Hkv * kChunk; e += 256) {
     const int g = e / kChunk, jl = e % kChunk;
-    if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = s_sc[e];
+    if (j0 + jl < jend && j0 + jl != jskip) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = s_sc[e];
   }
 }
 
@@ -267,13 +368,18 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
 
 template <typename TQ, bool SB>
 void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
-                        int row_stride, hipStream_t st) {
-  const dim3 grid((row_stride + kChunk - 1) / kChunk, B);
-  const size_t lds = (size_t)Hkv * (kD + kChunk) * sizeof(float);
+                        int row_stride, const TQ* k_new, const TQ* v_new, hipStream_t st) {
+  const int napp = k_new != nullptr ? Hkv : 0;
+  const dim3 grid(napp + (row_stride + kChunk - 1) / kChunk, B);
+  const int lds_floats = Hkv * (kD + kChunk) > 4 * kD + 2 ? Hkv * (kD + kChunk) : 4 * kD + 2;
+  const size_t lds = (size_t)lds_floats * sizeof(float);
+  TQ* kp = static_cast<TQ*>(c.k);
+  TQ* vp = static_cast<TQ*>(c.v);
 #define MSA_SCORE_CASE(H)                                                                                  \
   case H:                                                                                                  \
     k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \
-                                                      Hkv, max_len, scores, row_stride);                   \
+                                                      Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, \
+                                                      c.S, napp);                                          \
     break;
   switch (Hkv) {
     MSA_SCORE_CASE(1)
@@ -285,7 +391,8 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
     MSA_SCORE_CASE(64)
     default:
       k_score_decode<TQ, 0, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq,
-                                                        Hkv, max_len, scores, row_stride);
+                                                        Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, c.S,
+                                                        napp);
   }
 #undef MSA_SCORE_CASE
 }
@@ -293,15 +400,16 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
 }  // namespace
 
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
-                               float* scores, int row_stride, hipStream_t st) {
+                               float* scores, int row_stride, const void* k_new, const void* v_new, hipStream_t st) {
   if (B == 0 || row_stride == 0) return hipSuccess;
+#define MSA_SCORE_TYPED(T, SB) \
+  launch_score_typed<T, SB>((const T*)q, c, B, Hq, Hkv, max_len, scores, row_stride, (const T*)k_new, (const T*)v_new, st)
   if (bf16) {
-    if (c.s_bf16) launch_score_typed<uint16_t, true>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
-    else launch_score_typed<uint16_t, false>((const uint16_t*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+    if (c.s_bf16) MSA_SCORE_TYPED(uint16_t, true); else MSA_SCORE_TYPED(uint16_t, false);
   } else {
-    if (c.s_bf16) launch_score_typed<float, true>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
-    else launch_score_typed<float, false>((const float*)q, c, B, Hq, Hkv, max_len, scores, row_stride, st);
+    if (c.s_bf16) MSA_SCORE_TYPED(float, true); else MSA_SCORE_TYPED(float, false);
   }
+#undef MSA_SCORE_TYPED
   return hipGetLastError();
 }
 

@@ -20,13 +20,6 @@
 // for the k_eff-th key over the row in memory, then an ordered compaction.
 // Decode rows also get each kept block's page id (for the attend kernel). The output depends
 // only on the scores.
-//
-// Decode step append (fused here, so the step needs no separate kernel): the workgroup of row
-// (b, g) writes the new token's K/V row of group g at position seq_len-1, recomputes that
-// block's summary from its older rows plus the new key, stores it, and re-scores the block with
-// the group's index query before selecting ("MiniMax goes sparse", §1 Step 1: the index branch
-// scores blocks through their summaries, which must describe the current cache). Its loads are
-// issued together with the row's score loads.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,17 +60,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(min(a, b), min(c, d));
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v += dpp_mov<0xB1>(v);
-  v += dpp_mov<0x4E>(v);
-  v += dpp_mov<0x141>(v);
-  v += dpp_mov<0x140>(v);
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-}
-
 // block-wide integer sum (all threads get it); s_tmp holds NT/64 ints
 template <int NT>
 __device__ int block_sum(int v, int* s_tmp) {
@@ -113,11 +95,7 @@ __device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
 }
 
 struct TopkShared {
-  union {
-    unsigned long long comp[kCap + 2]; // survivors: (key << 32) | ~index, larger = better
-    float rows[kWaves][kD];            // decode append: per-wave partial sums of the block's keys
-  };
-  float fsum[2];
+  unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
   int32_t sel[kMaxK + 4];
   int32_t selpg[kMaxK];
   int32_t spage[kCap];
@@ -159,10 +137,9 @@ __device__ __forceinline__ void pad(const TopkArgs& a, int row, int keff, int n,
 
 // exact selection straight from memory: T = k_eff-th largest key, then ordered compaction
 template <int NT>
-__device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, int jlast,
-                                float fresh, TopkShared& sh) {
+__device__ void select_fallback(const TopkArgs& a, const float* srow, int row, int n, int keff, TopkShared& sh) {
   const int tid = threadIdx.x;
-  auto key_of = [&](int j) { return select_key(a, j, n, j == jlast ? fresh : srow[j]); };
+  auto key_of = [&](int j) { return select_key(a, j, n, srow[j]); };
   uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
@@ -310,102 +287,8 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
   }
 }
 
-// Decode append for row (b, g): the new token's K/V row goes to position N-1 of its block, the
-// block's summary is recomputed from its older rows plus the new key, and the block is re-scored
-// with the group's index query. Split so that its loads overlap the selection: `issue` (loads,
-// and the K/V row store), `partial` (the wave's sum of the block's rows into LDS; query loads), `final`
-// (after a barrier: summary store and the per-wave product), `fresh` (after another barrier).
-// Thread -> (row r = tid/16 of the block, 8 dims).
-template <typename T>
-struct DecodeAppend {
-  Vec8<T> old_k, new_k;
-  float qv[kMaxGroup];
-  int page, slot, g;
-  bool ok;
-
-  __device__ __forceinline__ void issue(const TopkArgs& a, int row, int N) {
-    const int tid = threadIdx.x;
-    const int b = row / a.Hkv;
-    g = row % a.Hkv;
-    const int G = a.Hq / a.Hkv;
-    const int t = N - 1;
-    slot = t % kP;
-    page = a.table[(long long)b * a.max_blocks + t / kP];
-    ok = page_ok(page, a.num_pages);                              // uniform
-    const int r = tid >> 4, d0 = (tid & 15) * 8;
-    const long long head = ((long long)(ok ? page : 0) * a.Hkv + g) * kP * kD;
-    const long long nrow = ((long long)b * a.Hkv + g) * kD;
-    const T* knew = reinterpret_cast<const T*>(a.k_new) + nrow + d0;
-    new_k.load(knew);
-    // an older row of the block (a valid address either way: the new key when the page id is bad)
-    old_k.load(ok ? reinterpret_cast<const T*>(a.kpool) + head + (long long)min(r, max(slot - 1, 0)) * kD + d0 : knew);
-    if (ok && r == slot) {   // the new token's row: K and V of this group
-      Vec8<T> new_v;
-      new_v.load(reinterpret_cast<const T*>(a.v_new) + nrow + d0);
-      new_k.store(reinterpret_cast<T*>(a.kpool) + head + (long long)slot * kD + d0);
-      new_v.store(reinterpret_cast<T*>(a.vpool) + head + (long long)slot * kD + d0);
-    }
-  }
-
-  // also requests the group's query heads (used by `final`, after the next barrier)
-  __device__ __forceinline__ void partial(const TopkArgs& a, int row, TopkShared& sh) {
-    if (!ok) return;                                             // uniform
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < kD) {
-      const int G = a.Hq / a.Hkv;
-      const T* qb = reinterpret_cast<const T*>(a.q) + ((long long)(row / a.Hkv) * a.Hq + g * G) * kD;
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        const T x = qb[(long long)min(h, G - 1) * kD + tid];
-        if constexpr (sizeof(T) == 2) qv[h] = __uint_as_float((uint32_t)x << 16);
-        else qv[h] = x;
-      }
-    }
-    const int r = tid >> 4, d0 = (tid & 15) * 8;
-    float fo[8], fn[8], f[8];
-    old_k.to_f32(fo);
-    new_k.to_f32(fn);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = r < slot ? fo[e] : (r == slot ? fn[e] : 0.f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = across_rows_sum(f[e]);    // the wave's 4 rows
-    if (lane < 16) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sh.rows[wave][d0 + e] = f[e];
-    }
-  }
-
-  __device__ __forceinline__ void final(const TopkArgs& a, TopkShared& sh) const {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (!ok || tid >= kD) return;
-    const int G = a.Hq / a.Hkv;
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += sh.rows[w][tid];
-    float summary = acc / (float)(slot + 1);
-    const long long si = ((long long)page * a.Hkv + g) * kD + tid;
-    if (a.s_bf16) {   // uniform: the pool stores the rounded mean, and the score uses what is stored
-      const uint32_t h = pack_bf16x2(summary, 0.f) & 0xffffu;
-      reinterpret_cast<uint16_t*>(a.S)[si] = (uint16_t)h;
-      summary = bf16lo(h);
-    } else {
-      reinterpret_cast<float*>(a.S)[si] = summary;
-    }
-    float qi = 0.f;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h < G) qi += qv[h];
-    const float prod = wave_sum_f32((qi / (float)G) * summary);
-    if (lane == 0) sh.fsum[wave] = prod;
-  }
-
-  __device__ __forceinline__ float fresh(const TopkShared& sh) const {
-    return ok ? sh.fsum[0] + sh.fsum[1] : -INFINITY;             // never read, never written
-  }
-};
-
-// NT threads (512 or 1024); the fused decode append needs 1024 (one 16-lane row group per key row)
-template <typename T, int NT>
+// NT threads: 512 or 1024
+template <int NT>
 __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   constexpr int kW = NT / 64;
   constexpr int kMaxFast = NT * kPer;
@@ -430,32 +313,11 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
       for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + NT * i, rs_last)];
     }
   }
-  int n, N = 0;
-  if (!prefill) {
-    N = clamp_len(len_raw, a.max_len);
-    n = (N + kP - 1) / kP;
-  } else {
-    n = a.base_blocks + row / a.Hkv;
-  }
+  const int n = prefill ? a.base_blocks + row / a.Hkv : (clamp_len(len_raw, a.max_len) + kP - 1) / kP;
   const int keff = min(a.k, n);
-  const bool do_append = NT == kThreads && !prefill && a.k_new != nullptr && N > 0;   // uniform
-  const int jlast = do_append ? n - 1 : -1;
-  DecodeAppend<T> ap;
-  if (do_append) ap.issue(a, row, N);
-
   const int ngroups = min(n, NT);     // threads holding at least one candidate
   const bool fast = n <= kMaxFast && keff < n && keff <= ngroups && keff <= kSmallK;   // uniform
-  if (!fast) {
-    // every candidate kept, or the exact path: finish the append first
-    float fresh = 0.f;
-    if (do_append) {
-      ap.partial(a, row, sh);
-      __syncthreads();
-      ap.final(a, sh);
-      __syncthreads();
-      fresh = ap.fresh(sh);
-      if (tid == 0) srow[jlast] = fresh;
-    }
+  if (!fast) {   // every candidate kept, or the exact path
     if (keff == n) {
       for (int i = tid; i < n; i += NT) emit(a, row, i, i);
     } else if (n <= kMaxFast) {   // large k: exact select on the keys in registers
@@ -463,25 +325,23 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int j = tid + NT * i;
-        key[i] = j < n ? select_key(a, j, n, j == jlast ? fresh : v[i]) : 0u;
+        key[i] = j < n ? select_key(a, j, n, v[i]) : 0u;
       }
       select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);
     } else {
-      select_fallback<NT>(a, srow, row, n, keff, jlast, fresh, sh);
+      select_fallback<NT>(a, srow, row, n, keff, sh);
     }
     pad<NT>(a, row, keff, n, prefill);
     return;
   }
 
-  // ---- fast path. The appended block's stale score is left out of the bound (key 0 sorts below
-  // every real key) and re-enters as a survivor once its fresh score is known: T0 stays a valid
-  // lower bound of the k_eff-th largest key.
+  // ---- fast path
   uint32_t key[kPer];
   uint32_t cm = 0u;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = tid + NT * i;
-    key[i] = (j < n && j != jlast) ? select_key(a, j, n, v[i]) : 0u;
+    key[i] = j < n ? select_key(a, j, n, v[i]) : 0u;
     cm = max(cm, key[i]);
   }
   const bool has = tid < ngroups;
@@ -503,7 +363,6 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     bin = min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1));
     atomicAdd(&sh.hist[bin], 1u);
   }
-  if (do_append) ap.partial(a, row, sh);
   __syncthreads();
   // ---- bin holding the k_eff-th largest group maximum (wave 0: lane owns bins 4l..4l+3)
   if (wave == 0) {
@@ -521,18 +380,11 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
       run += cc[i];
     }
   }
-  if (do_append) ap.final(a, sh);
   __syncthreads();
   // ---- T0 = smallest group maximum in bins >= bstar
   const uint32_t t0 = wave_min_u32((has && bin >= (uint32_t)sh.bstar) ? cm : 0xffffffffu);
   if (lane == 0) sh.red[wave] = t0;
-  float fresh = 0.f;
-  if (do_append) {
-    fresh = ap.fresh(sh);
-    if (jlast % NT == tid) key[jlast / NT] = select_key(a, jlast, n, fresh);
-  }
   __syncthreads();
-  if (do_append && tid == 0) srow[jlast] = fresh;
   uint32_t T0 = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < kW; ++w) T0 = min(T0, sh.red[w]);
@@ -590,20 +442,14 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, bool bf16, hipStream_t st) {
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  // rows of at most 512 * kPer candidates and k <= 512, with no fused append, run on 512 threads
-  // (two workgroups fit a CU); everything else on 1024
+  // rows of at most 512 * kPer candidates and k <= 512 run on 512 threads (two workgroups fit a
+  // CU); longer rows or larger k on 1024
   const bool prefill = a.lens == nullptr;
   const long long n_max = prefill ? (long long)a.base_blocks + (a.rows - 1) / a.Hkv : ((long long)a.max_len + kP - 1) / kP;
-  const bool small = n_max <= 512 * kPer && a.k <= 512 && (prefill || a.k_new == nullptr);
-  if (bf16) {
-    if (small) k_topk<uint16_t, 512><<<a.rows, 512, 0, st>>>(a);
-    else k_topk<uint16_t, kThreads><<<a.rows, kThreads, 0, st>>>(a);
-  } else {
-    if (small) k_topk<float, 512><<<a.rows, 512, 0, st>>>(a);
-    else k_topk<float, kThreads><<<a.rows, kThreads, 0, st>>>(a);
-  }
+  if (n_max <= 512 * kPer && a.k <= 512) k_topk<512><<<a.rows, 512, 0, st>>>(a);
+  else k_topk<kThreads><<<a.rows, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -142,7 +142,7 @@ def test_select_and_score_entry_points_bf16_summaries():
 
 
 def test_decode_step_appends_into_a_bf16_pool():
-    """The fused append rewrites the last block's bf16 summary and scores it from the stored value."""
+    """The step's append rewrites the last block's bf16 summary and scores it from the stored value."""
     c = make_decode_case(seed=63, B=3, Hq=32, Hkv=8, lens=[777, 64, 4097], top_k=8, dtype="bf16", permute=True)
     d = to_device_bf16(c)
     r = np.random.default_rng(9)

@@ -376,7 +376,7 @@ def test_graph_replays_match_eager_calls():
 
 def test_full_size_decode_1m_with_append():
     """The benchmark's timed configuration: the 1M-token step with the new token's K/V appended
-    (its block's summary and score recomputed inside the top-k kernel), checked end to end against
+    (its block's summary and score recomputed in the scoring launch), checked end to end against
     the oracle run on the cache after the append."""
     kw = workload("decode_bf16_1m_paged", seed=0)
     c = make_decode_case_torch(**kw)

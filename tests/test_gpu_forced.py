@@ -1,7 +1,7 @@
 """GPU parity of forced sink / local blocks (the first keep_sink and last keep_local candidates of
 every row are always kept and count toward k_eff) against the CPU oracle, through the C ABI, on
 every selection path of the top-k kernel: the group-maximum bound (k <= 256), the exact large-k
-select, the memory-based path for rows longer than 16,384 blocks, the fused token append, the
+select, the memory-based path for rows longer than 16,384 blocks, a step with a token append, the
 prefill tiles and the index branch."""
 import numpy as np
 import pytest
@@ -53,7 +53,7 @@ def test_decode_step_forced(name, kw, sink, local):
 
 
 def test_decode_step_forced_with_append():
-    """The fused append path: the appended token's block is the forced local block."""
+    """A step with a token append: the appended token's block is the forced local block."""
     c = make_decode_case(seed=52, B=3, Hq=32, Hkv=8, lens=[777, 64, 40000], top_k=8, dtype="bf16", permute=True)
     d = forced(to_device(c), 1, 1)
     r = np.random.default_rng(7)

@@ -1,13 +1,13 @@
 """Seeded random sweep of small configurations against the oracle, through the C ABI: storage type,
 KV heads (powers of two and not), group size 1..8, batch, ragged lengths (0 included), k from 1 to
-past the number of blocks, forced sink / local blocks, the summary pool type and page
-permutation, for decode steps and prefill chunks. Each case is small; together they reach
+past the number of blocks, forced sink / local blocks, the summary pool type, page permutation
+and (decode) a new token appended by the step, for decode steps and prefill chunks. Each case is small; together they reach
 combinations the hand-written cases do not."""
 import numpy as np
 import pytest
 
 from synth import make_decode_case, make_prefill_case
-from gpu_util import full_decode_check, require_gpu, run_decode, to_device
+from gpu_util import require_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -34,17 +34,11 @@ def decode_params(i):
 
 @pytest.mark.parametrize("i", range(48))
 def test_random_decode(i):
+    import test_gpu_append as ta
     kw, sink, local, sdt = decode_params(i)
+    append = bool(np.random.default_rng(9050 + i).random() < 0.5)   # its own stream: the cases stay as they were
     c = make_decode_case(seed=9100 + i, **kw)
-    if sdt == "bf16":
-        import test_gpu_bf16_summaries as tb
-        d = tb.to_device_bf16(c)
-        d.cfg.keep_sink, d.cfg.keep_local = sink, local
-        tb.check_decode_bf16(d, run_decode(d))
-    else:
-        d = to_device(c)
-        d.cfg.keep_sink, d.cfg.keep_local = sink, local
-        full_decode_check(d, run_decode(d))
+    ta.step_and_check(ta.device_case(c, sdt), sdt, seed=9060 + i, sink=sink, local=local, append=append)
 
 
 def prefill_params(i):
