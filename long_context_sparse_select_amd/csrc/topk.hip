@@ -6,13 +6,15 @@
 // min(k, n); the list is written in ascending block order and padded with -1; in prefill the
 // tile's diagonal block is appended after the k_eff entries.
 //
-// One 1024-thread workgroup per row; scores are compared as order-preserving 32-bit keys.
-// Rows of up to 16384 candidates are held in registers (16 per thread, j = tid + 1024 i):
-//  1. each thread's maximum is a group maximum; the k_eff-th largest group maximum is a lower
-//     bound T0 of the k_eff-th largest key (the k_eff groups with the largest maxima each hold
-//     a key >= T0). A 256-bin histogram of the group maxima, normalised to their range, finds
-//     a bin whose lower edge still leaves >= k_eff maxima above it; T0 = the smallest group
-//     maximum in or above that bin, so >= k_eff keys are >= T0 -- whatever the data;
+// One workgroup per row (1024 threads, or 512 for short rows); scores are compared as
+// order-preserving 32-bit keys. Rows of up to 16 candidates per thread are held in registers
+// (j = tid + NT i):
+//  1. each thread's maximum is a group maximum; any value with k_eff group maxima at or above
+//     it is a lower bound T0 of the k_eff-th largest key (each of those groups holds a key
+//     >= T0). A 256-bin histogram of the group maxima, normalised to their range, finds the bin
+//     where the count from the top reaches k_eff; T0 = that bin's lower edge (less a margin for
+//     the float binning), so >= k_eff keys are >= T0 -- whatever the data. Every wave reads the
+//     bin off the histogram itself, so the bound costs two barriers;
 //  2. the survivors (keys >= T0; typically a little over k) are gathered in LDS and ranked
 //     exactly by (key desc, index asc); ranks < k_eff are kept;
 //  3. the kept indices are sorted ascending by counting.
@@ -98,7 +100,6 @@ struct TopkShared {
   unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
   int32_t sel[kMaxK + 4];
   int32_t selpg[kMaxK];
-  int32_t spage[kCap];
   uint32_t hist[kBins];
   uint32_t hbig[kLBins];             // exact select: histogram of the current key range
   int pre[kPer * kWaves];            // exact select: per (slot, wave) counts, then their prefixes
@@ -106,7 +107,6 @@ struct TopkShared {
   uint32_t red[2 * kWaves];
   int tmp[kWaves];
   int cnt;
-  int bstar;
 };
 
 // A forced block's key sits above every order key (even a NaN's), so every selection path keeps
@@ -213,7 +213,7 @@ __device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&po
 //     at their rank in ascending block order (no sort needed).
 template <int NT>
 __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const uint32_t (&key)[kPer],
-                             const int (&pg)[kPer], bool with_pages, TopkShared& sh) {
+                             const int32_t* trow, TopkShared& sh) {
   constexpr int kW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   bool valid[kPer];
@@ -277,12 +277,17 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
   bool sel[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) sel[i] = valid[i] && (key[i] > T || (eq[i] && rk[i] < need_eq));
+  int pg[kPer];   // decode: the kept blocks' page ids, loaded while the prefix is formed
+  if (trow != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) pg[i] = sel[i] ? trow[tid + NT * i] : -1;
+  }
   ordered_prefix<NT>(sel, rk, sh);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (sel[i]) {
       a.idx[(long long)row * a.idx_stride + rk[i]] = tid + NT * i;
-      if (with_pages) a.pages[(long long)row * a.k + rk[i]] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
+      if (trow != nullptr) a.pages[(long long)row * a.k + rk[i]] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
     }
   }
 }
@@ -299,19 +304,15 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const int len_raw = prefill ? 0 : a.lens[row / a.Hkv];
   float* srow = a.scores + (long long)row * a.row_stride;
   // the row's score loads go first, in flight with the length load: addresses are clamped to the
-  // row stride (every row holds row_stride scores, every table row at least as many ids), so they
-  // wait for nothing; entries past the row's length are masked when used
+  // row stride (every row holds row_stride scores), so they wait for nothing; entries past the
+  // row's length are masked when used. Page ids (decode) are read later, for kept blocks only:
+  // the row's loads are what one CU must pull in before anything else can start.
   float v[kPer];
-  int pg[kPer];   // decode: the candidates' page ids, loaded with the scores (no later round trip)
   const int32_t* trow = a.pages != nullptr ? a.table + (long long)(row / a.Hkv) * a.max_blocks : nullptr;
   const int rs_last = a.row_stride - 1;
   if (rs_last >= 0) {   // uniform
 #pragma unroll
     for (int i = 0; i < kPer; ++i) v[i] = srow[min(tid + NT * i, rs_last)];
-    if (trow != nullptr) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) pg[i] = trow[min(tid + NT * i, rs_last)];
-    }
   }
   const int n = prefill ? a.base_blocks + row / a.Hkv : (clamp_len(len_raw, a.max_len) + kP - 1) / kP;
   const int keff = min(a.k, n);
@@ -327,7 +328,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
         const int j = tid + NT * i;
         key[i] = j < n ? select_key(a, j, n, v[i]) : 0u;
       }
-      select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);
+      select_large<NT>(a, row, n, keff, key, trow, sh);
     } else {
       select_fallback<NT>(a, srow, row, n, keff, sh);
     }
@@ -350,22 +351,19 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
   if (lane == 0) { sh.red[wave] = wmx; sh.red[kW + wave] = wmn; }
   if (tid < kBins) sh.hist[tid] = 0u;
-  if (tid == 0) sh.bstar = 0;   // bin 0 keeps every group maximum: always a valid bound
   __syncthreads();
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
-  // any binning keeps T0 a valid bound (the bins at or above bstar hold >= k_eff group maxima); a
-  // monotone one keeps it tight. A float scale avoids a 64-bit division per thread.
+  // bin(d) = min(floor(fl(fl(d) * bscale)), kBins - 1) for d = key - mn: monotone in the key. A
+  // float scale avoids a 64-bit division per thread.
   const float bscale = (float)kBins / ((float)(mx - mn) + 1.0f);
-  uint32_t bin = 0u;
-  if (has) {
-    bin = min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1));
-    atomicAdd(&sh.hist[bin], 1u);
-  }
+  if (has) atomicAdd(&sh.hist[min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1))], 1u);
   __syncthreads();
-  // ---- bin holding the k_eff-th largest group maximum (wave 0: lane owns bins 4l..4l+3)
-  if (wave == 0) {
+  // ---- bin bstar holding the k_eff-th largest group maximum, found by every wave (no barrier):
+  // lane l owns bins 4l..4l+3; bin 0 would keep every group maximum, the fallback
+  uint32_t bstar;
+  {
     const uint4 c4 = reinterpret_cast<const uint4*>(sh.hist)[lane];
     const uint32_t local = c4.x + c4.y + c4.z + c4.w;
     uint32_t incl = local;  // suffix sum over lanes >= lane
@@ -373,31 +371,30 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
       const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
       if (lane + off < 64) incl += y;
     }
-    uint32_t run = incl - local;
+    uint32_t run = incl - local, mine = 0u;
     const uint32_t cc[4] = {c4.x, c4.y, c4.z, c4.w};
     for (int i = 3; i >= 0; --i) {
-      if (run < (uint32_t)keff && run + cc[i] >= (uint32_t)keff) sh.bstar = 4 * lane + i;
+      if (run < (uint32_t)keff && run + cc[i] >= (uint32_t)keff) mine = 4 * lane + i;
       run += cc[i];
     }
+    bstar = wave_max_u32(mine);
   }
-  __syncthreads();
-  // ---- T0 = smallest group maximum in bins >= bstar
-  const uint32_t t0 = wave_min_u32((has && bin >= (uint32_t)sh.bstar) ? cm : 0xffffffffu);
-  if (lane == 0) sh.red[wave] = t0;
-  __syncthreads();
-  uint32_t T0 = 0xffffffffu;
-#pragma unroll
-  for (int w = 0; w < kW; ++w) T0 = min(T0, sh.red[w]);
-  // ---- 2. survivors (keys >= T0) as (key, ~index) composites (+ page id)
+  // ---- T0 = a key at or below the lower edge of bin bstar. The bins >= bstar hold >= k_eff group
+  // maxima, all >= that edge, so at least k_eff keys are >= T0. The edge: bin(d) >= bstar needs
+  // d * bscale * (1 + 2^-24)^2 >= bstar, i.e. d >= bstar / bscale - 512 (d < 2^32); T0 sits 513
+  // below that, which no rounding of the quotient can cross.
+  uint32_t T0 = mn;
+  if (bstar > 0u) {   // uniform
+    const double q = floor((double)bstar / (double)bscale) - 513.0;
+    if (q > 0.0) T0 = mn + (uint32_t)q;
+  }
+  // ---- 2. survivors (keys >= T0) as (key, ~index) composites
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = tid + NT * i;
     if (j < n && key[i] >= T0) {
       const int p = atomicAdd(&sh.cnt, 1);
-      if (p < kCap) {
-        sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
-        if (trow != nullptr) sh.spage[p] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
-      }
+      if (p < kCap) sh.comp[p] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)j);
     }
   }
   __syncthreads();
@@ -409,14 +406,14 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     for (int e = tid; e < m; e += NT) {
       const unsigned long long ce = sh.comp[e];
       const int je = (int)~(uint32_t)ce;
-      const int pge = trow != nullptr ? sh.spage[e] : -1;
+      const int pge = trow != nullptr ? trow[je] : -1;   // in flight during the ranking
       int rank = 0;
 #pragma unroll 4
       for (int f = 0; f < npair; ++f) {
         const ulonglong2 c2 = cp[f];
         rank += (c2.x > ce) + (2 * f + 1 < m && c2.y > ce);   // comp[m] is not a survivor
       }
-      if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = pge; }
+      if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = page_ok(pge, a.num_pages) ? pge : -1; }
     }
     if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
     __syncthreads();
@@ -436,7 +433,7 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     }
     done = true;
   }
-  if (!done) select_large<NT>(a, row, n, keff, key, pg, trow != nullptr, sh);   // mass ties at T0
+  if (!done) select_large<NT>(a, row, n, keff, key, trow, sh);   // mass ties at T0
   pad<NT>(a, row, keff, n, prefill);
 }
 
