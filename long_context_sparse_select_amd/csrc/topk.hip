@@ -36,6 +36,7 @@ constexpr int kCap = 2048;
 constexpr int kBins = 256;
 constexpr int kMaxK = 4096;
 constexpr int kSmallK = 256;    // k_eff up to this uses the survivor path; larger k the exact select
+constexpr int kRowRank = 512;   // survivors ranked 16 lanes each up to this count
 constexpr int kLBins = 1024;    // bins per pass of the exact select
 
 template <int CTRL>
@@ -104,7 +105,7 @@ struct TopkShared {
   uint32_t hbig[kLBins];             // exact select: histogram of the current key range
   int pre[kPer * kWaves];            // exact select: per (slot, wave) counts, then their prefixes
   uint32_t range[3];                 // exact select: lo, hi, keys above hi
-  uint32_t red[2 * kWaves];
+  uint32_t red[3 * kWaves];
   int tmp[kWaves];
   int cnt;
 };
@@ -205,10 +206,27 @@ __device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&po
   return sh.cnt;
 }
 
+// The score an order key came from (keys of NaN payloads give NaN; the forced key is not a score).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+constexpr uint32_t kPosInfKey = 0xff800000u;   // order_key(+inf)
+
+// Bin of a key on a linear score scale from vlo (bins of 1/vscale): monotone in the key, with
+// every key above +inf's (NaN payloads, the forced key) in the top bin and NaN below -inf in bin 0.
+__device__ __forceinline__ uint32_t value_bin(uint32_t k, float vlo, float vscale) {
+  const float t = (key_value(k) - vlo) * vscale;
+  return k > kPosInfKey ? (uint32_t)(kLBins - 1) : (uint32_t)fminf(fmaxf(t, 0.f), (float)(kLBins - 1));
+}
+
 // Exact selection for large k on keys held in registers (slot i of thread t = block t + NT*i):
 //  1. the k_eff-th largest key T by range refinement: a 1024-bin histogram of the keys in
-//     [lo, hi], the bin where the count from the top reaches k_eff becomes the next range; a
-//     32-bit key range takes at most 4 passes;
+//     [lo, hi], the bin where the count from the top reaches k_eff becomes the next range (a
+//     32-bit key range takes at most 4 passes). The first pass bins score values linearly
+//     instead of keys: order keys of typical scores bunch into a sliver of the key range, so a
+//     key-linear first pass piles thousands of LDS atomics onto a few bins and leaves most keys
+//     in the chosen one; the chosen value bin is mapped back to its exact key range by a
+//     min / max over the keys that fall in it;
 //  2. ordered compaction: keys > T, then the ties == T with the smallest block indices, written
 //     at their rank in ascending block order (no sort needed).
 template <int NT>
@@ -217,23 +235,74 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
   constexpr int kW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   bool valid[kPer];
-  uint32_t kmx = 0u, kmn = 0xffffffffu;
+  uint32_t kmx = 0u, kmn = 0xffffffffu, kfin = 0u;   // kfin: the largest key at or below +inf's
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     valid[i] = tid + NT * i < n;
-    if (valid[i]) { kmx = max(kmx, key[i]); kmn = min(kmn, key[i]); }
+    if (valid[i]) {
+      kmx = max(kmx, key[i]);
+      kmn = min(kmn, key[i]);
+      if (key[i] <= kPosInfKey) kfin = max(kfin, key[i]);
+    }
   }
   kmx = wave_max_u32(kmx);
   kmn = wave_min_u32(kmn);
-  if (lane == 0) { sh.red[wave] = kmx; sh.red[kW + wave] = kmn; }
+  kfin = wave_max_u32(kfin);
+  if (lane == 0) { sh.red[wave] = kmx; sh.red[kW + wave] = kmn; sh.red[2 * kW + wave] = kfin; }
   __syncthreads();
   if (tid == 0) {
-    uint32_t mx = 0u, mn = 0xffffffffu;
-    for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
-    sh.range[0] = mn; sh.range[1] = mx; sh.range[2] = 0u;
+    uint32_t mx = 0u, mn = 0xffffffffu, fin = 0u;
+    for (int w = 0; w < kW; ++w) {
+      mx = max(mx, sh.red[w]);
+      mn = min(mn, sh.red[kW + w]);
+      fin = max(fin, sh.red[2 * kW + w]);
+    }
+    sh.range[0] = mn; sh.range[1] = mx; sh.range[2] = fin;
   }
   __syncthreads();
   uint32_t lo = sh.range[0], hi = sh.range[1], above = 0u;
+  const float vlo = key_value(lo), vfin = key_value(sh.range[2]);
+  if (lo != hi && sh.range[2] > lo && isfinite(vlo) && isfinite(vfin) && vfin > vlo) {   // uniform
+    // ---- first pass on a score scale from the smallest key to the largest finite one
+    const float vscale = (float)kLBins / (vfin - vlo);
+    for (int b = tid; b < kLBins; b += NT) sh.hbig[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (valid[i]) atomicAdd(&sh.hbig[value_bin(key[i], vlo, vscale)], 1u);
+    __syncthreads();
+    if (wave == 0) {   // lane l owns bins 16l .. 16l+15; counts from the top
+      uint32_t c[16], local = 0u;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { c[e] = sh.hbig[16 * lane + e]; local += c[e]; }
+      uint32_t incl = local;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)incl, off);
+        if (lane + off < 64) incl += y;
+      }
+      uint32_t run = incl - local;
+      for (int e = 15; e >= 0; --e) {
+        if (run < (uint32_t)keff && run + c[e] >= (uint32_t)keff) { sh.range[0] = 16 * lane + e; sh.range[2] = run; }
+        run += c[e];
+      }
+    }
+    __syncthreads();
+    // ---- exact key range of the chosen bin: every key in it lies in [min, max] of its keys, and
+    // (the binning being monotone) every key in that interval is in it; keys above are `above`
+    const uint32_t bsel = sh.range[0];
+    above = sh.range[2];
+    uint32_t bmx = 0u, bmn = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (valid[i] && value_bin(key[i], vlo, vscale) == bsel) { bmx = max(bmx, key[i]); bmn = min(bmn, key[i]); }
+    bmx = wave_max_u32(bmx);
+    bmn = wave_min_u32(bmn);
+    if (lane == 0) { sh.red[wave] = bmx; sh.red[kW + wave] = bmn; }
+    __syncthreads();
+    lo = 0xffffffffu; hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) { hi = max(hi, sh.red[w]); lo = min(lo, sh.red[kW + w]); }
+  }
   while (lo != hi) {   // uniform
     for (int b = tid; b < kLBins; b += NT) sh.hbig[b] = 0u;
     __syncthreads();
@@ -401,35 +470,48 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const int m = sh.cnt;
   bool done = false;
   if (m >= keff && m <= kCap) {   // uniform; m >= k_eff holds by construction of T0
-    const int npair = (m + 1) >> 1;
-    const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
-    for (int e = tid; e < m; e += NT) {
-      const unsigned long long ce = sh.comp[e];
-      const int je = (int)~(uint32_t)ce;
-      const int pge = trow != nullptr ? trow[je] : -1;   // in flight during the ranking
-      int rank = 0;
-#pragma unroll 4
-      for (int f = 0; f < npair; ++f) {
-        const ulonglong2 c2 = cp[f];
-        rank += (c2.x > ce) + (2 * f + 1 < m && c2.y > ce);   // comp[m] is not a survivor
+    // ---- rank of each survivor by (key desc, index asc) = the number of larger composites.
+    // Up to kRowRank survivors: 16 lanes (one DPP row) per survivor, each lane counting over
+    // every 16th composite, so a row's reads are one contiguous 128 B run; beyond that, one
+    // thread per survivor. A kept survivor's page id is read while it is ranked.
+    const int part = tid & 15;
+    if (m <= kRowRank) {   // uniform
+      for (int e = tid >> 4; e < m; e += NT / 16) {   // uniform per 16-lane row
+        const unsigned long long ce = sh.comp[e];
+        const int je = (int)~(uint32_t)ce;
+        const int pge = (trow != nullptr && part == 0) ? trow[je] : -1;
+        int c = 0;
+        for (int f = part; f < m; f += 16) c += sh.comp[f] > ce;
+        const int rank = (int)row16_sum((float)c);   // counts < 2^24: exact
+        if (part == 0 && rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = page_ok(pge, a.num_pages) ? pge : -1; }
       }
-      if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = page_ok(pge, a.num_pages) ? pge : -1; }
+    } else {
+      const int npair = (m + 1) >> 1;
+      const ulonglong2* cp = reinterpret_cast<const ulonglong2*>(sh.comp);
+      for (int e = tid; e < m; e += NT) {
+        const unsigned long long ce = sh.comp[e];
+        const int je = (int)~(uint32_t)ce;
+        const int pge = trow != nullptr ? trow[je] : -1;
+        int rank = 0;
+#pragma unroll 4
+        for (int f = 0; f < npair; ++f) {
+          const ulonglong2 c2 = cp[f];
+          rank += (c2.x > ce) + (2 * f + 1 < m && c2.y > ce);   // comp[m] is not a survivor
+        }
+        if (rank < keff) { sh.sel[rank] = je; sh.selpg[rank] = page_ok(pge, a.num_pages) ? pge : -1; }
+      }
     }
-    if (tid < 4) sh.sel[keff + tid] = 0x7fffffff;   // pad for 4-wide reads
     __syncthreads();
-    // ---- 3. ascending block order
-    const int nq = (keff + 3) >> 2;
-    const int4* sp = reinterpret_cast<const int4*>(sh.sel);
-    for (int e = tid; e < keff; e += NT) {
+    // ---- 3. ascending block order: position = kept blocks with a smaller index (16 lanes each)
+    for (int e = tid >> 4; e < keff; e += NT / 16) {   // uniform per 16-lane row
       const int vj = sh.sel[e];
-      int pos = 0;
-#pragma unroll 4
-      for (int f = 0; f < nq; ++f) {
-        const int4 q4 = sp[f];
-        pos += (q4.x < vj) + (q4.y < vj) + (q4.z < vj) + (q4.w < vj);
+      int c = 0;
+      for (int f = part; f < keff; f += 16) c += sh.sel[f] < vj;
+      const int pos = (int)row16_sum((float)c);
+      if (part == 0) {
+        a.idx[(long long)row * a.idx_stride + pos] = vj;
+        if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = sh.selpg[e];
       }
-      a.idx[(long long)row * a.idx_stride + pos] = vj;
-      if (a.pages != nullptr) a.pages[(long long)row * a.k + pos] = sh.selpg[e];
     }
     done = true;
   }
