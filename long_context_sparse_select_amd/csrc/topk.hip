@@ -416,18 +416,40 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   }
   const bool has = tid < ngroups;
   if (tid == 0) sh.cnt = 0;
-  // ---- 1. range of the group maxima
+  // ---- 1. range of the group maxima: smallest, largest, and largest at or below +inf's key
   const uint32_t wmx = wave_max_u32(has ? cm : 0u), wmn = wave_min_u32(has ? cm : 0xffffffffu);
-  if (lane == 0) { sh.red[wave] = wmx; sh.red[kW + wave] = wmn; }
+  const uint32_t wfin = wave_max_u32(has && cm <= kPosInfKey ? cm : 0u);
+  if (lane == 0) { sh.red[wave] = wmx; sh.red[kW + wave] = wmn; sh.red[2 * kW + wave] = wfin; }
   if (tid < kBins) sh.hist[tid] = 0u;
   __syncthreads();
-  uint32_t mx = 0u, mn = 0xffffffffu;
+  uint32_t mx = 0u, mn = 0xffffffffu, fin = 0u;
 #pragma unroll
-  for (int w = 0; w < kW; ++w) { mx = max(mx, sh.red[w]); mn = min(mn, sh.red[kW + w]); }
-  // bin(d) = min(floor(fl(fl(d) * bscale)), kBins - 1) for d = key - mn: monotone in the key. A
-  // float scale avoids a 64-bit division per thread.
+  for (int w = 0; w < kW; ++w) {
+    mx = max(mx, sh.red[w]);
+    mn = min(mn, sh.red[kW + w]);
+    fin = max(fin, sh.red[2 * kW + w]);
+  }
+  // Binning of the group maxima. Preferred: linear in the score value over [vlo, vfin] (order keys
+  // of ordinary scores bunch into a sliver of the key range, so key-linear bins are coarse where
+  // the k_eff-th maximum sits). Keys above +inf's (forced blocks, NaN payloads) go to the top bin.
+  // Used only when the value range is finite and wide against the values' own magnitude (2^-12),
+  // which keeps the float edge below safely under every key of the chosen bin. Otherwise
+  // key-linear: bin(d) = min(floor(fl(fl(d) * bscale)), kBins - 1) for d = key - mn.
+  const float vlo = key_value(mn), vfin = key_value(fin);
+  const bool by_value = fin > mn && isfinite(vlo) && isfinite(vfin) &&
+                        (vfin - vlo) > 0x1p-12f * fmaxf(fabsf(vlo), fabsf(vfin));   // uniform
+  const float vscale = by_value ? (float)kBins / (vfin - vlo) : 0.f;
   const float bscale = (float)kBins / ((float)(mx - mn) + 1.0f);
-  if (has) atomicAdd(&sh.hist[min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1))], 1u);
+  if (has) {
+    uint32_t bin;
+    if (by_value) {
+      const float t = (key_value(cm) - vlo) * vscale;
+      bin = cm > kPosInfKey ? (uint32_t)(kBins - 1) : (uint32_t)fminf(fmaxf(t, 0.f), (float)(kBins - 1));
+    } else {
+      bin = min((uint32_t)((float)(cm - mn) * bscale), (uint32_t)(kBins - 1));
+    }
+    atomicAdd(&sh.hist[bin], 1u);
+  }
   __syncthreads();
   // ---- bin bstar holding the k_eff-th largest group maximum, found by every wave (no barrier):
   // lane l owns bins 4l..4l+3; bin 0 would keep every group maximum, the fallback
@@ -448,14 +470,21 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
     }
     bstar = wave_max_u32(mine);
   }
-  // ---- T0 = a key at or below the lower edge of bin bstar. The bins >= bstar hold >= k_eff group
-  // maxima, all >= that edge, so at least k_eff keys are >= T0. The edge: bin(d) >= bstar needs
-  // d * bscale * (1 + 2^-24)^2 >= bstar, i.e. d >= bstar / bscale - 512 (d < 2^32); T0 sits 513
-  // below that, which no rounding of the quotient can cross.
+  // ---- T0 = a key at or below every key of bins >= bstar. Those bins hold >= k_eff group maxima,
+  // so at least k_eff keys are >= T0.
+  //  * value bins: bin(v) >= bstar needs (v - vlo) * vscale >= bstar up to a few float roundings
+  //    (relative 2^-22), so v >= vlo + (bstar - 1/2) / vscale with ~half a bin to spare, which
+  //    covers the rounding of that edge itself (the range is >= 2^11 ulps of the values);
+  //  * key bins: bin(d) >= bstar needs d * bscale * (1 + 2^-24)^2 >= bstar, i.e.
+  //    d >= bstar / bscale - 512 (d < 2^32); T0 sits 513 below that.
   uint32_t T0 = mn;
   if (bstar > 0u) {   // uniform
-    const double q = floor((double)bstar / (double)bscale) - 513.0;
-    if (q > 0.0) T0 = mn + (uint32_t)q;
+    if (by_value) {
+      T0 = max(mn, order_key(vlo + ((float)bstar - 0.5f) / vscale));
+    } else {
+      const double q = floor((double)bstar / (double)bscale) - 513.0;
+      if (q > 0.0) T0 = mn + (uint32_t)q;
+    }
   }
   // ---- 2. survivors (keys >= T0) as (key, ~index) composites
 #pragma unroll

@@ -46,6 +46,17 @@ def crafted(kind, rng, shape):
         s = -1.0 - np.abs(rng.standard_normal(shape))
     elif kind == "subnormal":
         s = rng.standard_normal(shape) * 1e-40
+    elif kind == "with_inf":                        # a few +inf and -inf among normal scores
+        s = rng.standard_normal(shape)
+        for r in np.ndindex(shape[:-1]):
+            s[r][rng.choice(shape[-1], 3, replace=False)] = np.inf
+            s[r][rng.choice(shape[-1], 40, replace=False)] = -np.inf
+    elif kind == "offset":                          # spread 1e-2 on 1000: just under the value-bin guard
+        s = 1000.0 + 1e-2 * rng.standard_normal(shape)
+    elif kind == "outlier":                         # one huge score stretches the value range
+        s = rng.standard_normal(shape)
+        for r in np.ndindex(shape[:-1]):
+            s[r][rng.integers(shape[-1])] = 1e6
     else:
         raise ValueError(kind)
     return s.astype(np.float32)
@@ -116,6 +127,17 @@ CASES = [
     ("normal", [16384], 4096, 0, 0, 0),
     ("normal", [20000, 30000], 64, 0, 0, 0),          # memory-based select (rows > 16,384)
     ("quantized", [20000], 1024, 1, 1, 3),
+    # small k on every distribution: the group-maximum bound on score-value bins, or key bins
+    # where the value range is unusable (narrow against the magnitude, infinite, subnormal)
+    ("narrow", [16384, 700], 64, 0, 0, 0),
+    ("offset", [16384, 4100], 32, 0, 0, 0),
+    ("wide", [16384, 4100], 64, 0, 0, 0),
+    ("negative", [16384, 4100], 32, 0, 0, 0),
+    ("subnormal", [16384, 4100], 64, 0, 0, 0),
+    ("with_inf", [16384, 4100], 64, 0, 0, 0),
+    ("outlier", [16384, 4100], 64, 0, 0, 0),
+    ("quantized", [16384, 4100], 32, 1, 1, 4),
+    ("normal", [4100, 16384], 200, 2, 0, 9),
 ]
 
 
