@@ -177,12 +177,40 @@ def main():
     t_step = timed(decode)
     log("decode step: %.2f us" % (t_step * 1e6))
     # stage timings: Step 1 scoring alone (one kernel), Step 1 (score + top-k), Step 2 (attend + merge)
-    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf))
+    # the scoring kernel alone streams summaries only: it rotates over SCORE_POOLS summary pools (the
+    # caches' own plus copies), ~1 GB at 1M tokens, so no pool can stay in the 256 MB infinity cache
+    # from one launch to its next use and the rate is HBM's
+    score_caches = list(caches)
+    while len(score_caches) < SCORE_POOLS:
+        base = caches[len(score_caches) % L]
+        score_caches.append(msa.KVCache(base.k_pages, base.v_pages, base.summaries.clone(), base.block_table,
+                                        base.seq_lens))
+    P = len(score_caches)
+    g_score = timed_graph(lambda i: msa.msa_score(cfg, q_ring[i % R], score_caches[i % P], B, max_len, sc_buf),
+                          P, torch)
+    run_graph(g_score, 2, torch)
+    n_score = max(2, steps // P)
+    t_score = run_graph(g_score, n_score, torch) / (n_score * P)
+    del g_score, score_caches
     t_sel = timed(select)
-    t_att = timed(attend)
+    # Step 2 alone: one selected list per (cache, query) pair, L * R lists (512 MiB of selected K/V
+    # at 1M tokens, beyond the infinity cache), attended in rotation
+    att_idx = [[torch.empty_like(idx_bufs[0]) for _ in range(R)] for _ in range(L)]
+    for l in range(L):
+        for r in range(R):
+            msa.msa_select(cfg, q_ring[r], caches[l], B, max_len, att_idx[l][r], workspace=ws)
+    PA = L * R
+    g_att = timed_graph(lambda i: msa.msa_attend(cfg, q_ring[(i // L) % R], caches[i % L], B, max_len,
+                                                 att_idx[i % L][(i // L) % R], out, lse_out=lse, workspace=ws),
+                        PA, torch)
+    run_graph(g_att, 2, torch)
+    n_att = max(2, steps // PA)
+    t_att = run_graph(g_att, n_att, torch) / (n_att * PA)
+    del g_att
     torch.cuda.synchronize()
     elem = 2 if c0.dtype == "bf16" else 4
-    kv_bytes = float(np.mean([selected_kv_bytes(idx_bufs[l], cases[l].seq_lens, elem=elem) for l in range(L)]))
+    kv_bytes = float(np.mean([selected_kv_bytes(att_idx[l][r], cases[l].seq_lens, elem=elem)
+                              for l in range(L) for r in range(R)]))
     nb_tot = sum((int(n) + 63) // 64 for n in c0.seq_lens)
     # algorithmic bytes of one scoring launch: summaries + block-table entries read, scores written
     score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
@@ -256,6 +284,7 @@ def main():
 
 
 COPY_BYTES = 256 << 20
+SCORE_POOLS = 16
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_score_decode_1m_hbm_traffic.md")
 SCORE_SOURCES = ("long_context_sparse_select_amd/csrc/score.hip", "long_context_sparse_select_amd/csrc/common.h")
 
@@ -378,9 +407,10 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
 
 def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev):
     """Gather-attend bandwidth on the batch-8, 131072-token workload (64 MiB of selected K/V per
-    launch, so the stage is less latency-bound than at batch 1). Two caches rotated."""
+    launch, so the stage is less latency-bound than at batch 1). Two caches, eight queries each:
+    16 selected lists (1 GiB of selected K/V, beyond the infinity cache) attended in rotation."""
     kw = workload("decode_bf16_b8_128k", seed=args.seed)
-    L = 2
+    L, NQ = 2, 8
     items = []
     for layer in range(L):
         c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed + 1000 * layer))
@@ -390,19 +420,25 @@ def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload,
         cache = msa.KVCache(c.k_pool, c.v_pool, S, table, lens)
         cfg = msa.make_config(c.Hq, c.Hkv, c.top_k, dtype="bf16", softmax_scale=c.scale)
         msa.msa_build_summaries(cfg, cache, c.B, c.max_seq_len)
-        idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device=dev)
-        msa.msa_select(cfg, c.q, cache, c.B, c.max_seq_len, idx)
-        items.append((c, cache, idx))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 77 + layer)
+        qs = [c.q] + [torch.randn(c.q.shape, generator=gen, device=dev, dtype=torch.float32).to(c.q.dtype)
+                      for _ in range(NQ - 1)]
+        for q in qs:
+            idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device=dev)
+            msa.msa_select(cfg, q, cache, c.B, c.max_seq_len, idx)
+            items.append((c, cache, idx, q))
     c0 = items[0][0]
     out = torch.empty_like(c0.q)
     ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, c0.B, c0.max_seq_len), dtype=torch.uint8,
                      device=dev)
     torch.cuda.synchronize()
-    g = timed_graph(lambda i: msa.msa_attend(cfg, items[i % L][0].q, items[i % L][1], c0.B, c0.max_seq_len,
-                                             items[i % L][2], out, workspace=ws), 8, torch)
-    run_graph(g, 3, torch)
-    n = 25
-    t = run_graph(g, n, torch) / (8 * n)
+    P = len(items)
+    g = timed_graph(lambda i: msa.msa_attend(cfg, items[i % P][3], items[i % P][1], c0.B, c0.max_seq_len,
+                                             items[i % P][2], out, workspace=ws), P, torch)
+    run_graph(g, 2, torch)
+    n = 12
+    t = run_graph(g, n, torch) / (P * n)
     kv = float(np.mean([selected_kv_bytes(it[2], it[0].seq_lens) for it in items]))
     log("batch-8 attend: %.2f us, %.0f GB/s of selected KV" % (t * 1e6, kv / t / 1e9))
     return {"workload": "decode_bf16_b8_128k", "attend_us": t * 1e6, "kv_GBps": kv / t / 1e9,
@@ -472,7 +508,18 @@ def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, v
     t_step = timed(lambda i: msa.msa_decode_step(cfg, q_ring[i % R], bcaches[i % L], B, max_len, out,
                                                  k_new=kn_ring[i % R], v_new=vn_ring[i % R], idx_out=idx[i % L],
                                                  workspace=ws))
-    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], bcaches[i % L], B, max_len, sc))
+    # scoring alone over 2 * SCORE_POOLS bf16 pools (~1 GB), beyond the infinity cache as above
+    spools = list(bcaches)
+    while len(spools) < 2 * SCORE_POOLS:
+        base = bcaches[len(spools) % L]
+        spools.append(msa.KVCache(base.k_pages, base.v_pages, base.summaries.clone(), base.block_table,
+                                  base.seq_lens))
+    P = len(spools)
+    g_score = timed_graph(lambda i: msa.msa_score(cfg, q_ring[i % R], spools[i % P], B, max_len, sc), P, torch)
+    run_graph(g_score, 2, torch)
+    n_score = max(2, args.steps // P)
+    t_score = run_graph(g_score, n_score, torch) / (n_score * P)
+    del g_score, spools
     torch.cuda.synchronize()
     nb = sum((int(n) + 63) // 64 for n in c0.seq_lens)
     score_bytes = nb * c0.Hkv * c0.D * 2 + nb * 4 + nb * c0.Hkv * 4 + B * c0.Hq * c0.D * 2

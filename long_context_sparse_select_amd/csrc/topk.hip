@@ -11,10 +11,11 @@
 // (j = tid + NT i):
 //  1. each thread's maximum is a group maximum; any value with k_eff group maxima at or above
 //     it is a lower bound T0 of the k_eff-th largest key (each of those groups holds a key
-//     >= T0). A 256-bin histogram of the group maxima, normalised to their range, finds the bin
-//     where the count from the top reaches k_eff; T0 = that bin's lower edge (less a margin for
-//     the float binning), so >= k_eff keys are >= T0 -- whatever the data. Every wave reads the
-//     bin off the histogram itself, so the bound costs two barriers;
+//     >= T0). A 256-bin histogram of the group maxima -- linear in the score value between the
+//     smallest and largest finite maximum, or linear in the key where that range is unusable --
+//     finds the bin where the count from the top reaches k_eff; T0 = that bin's lower edge (less
+//     a margin for the float binning), so >= k_eff keys are >= T0 -- whatever the data. Every
+//     wave reads the bin off the histogram itself, so the bound costs two barriers;
 //  2. the survivors (keys >= T0; typically a little over k) are gathered in LDS and ranked
 //     exactly by (key desc, index asc); ranks < k_eff are kept;
 //  3. the kept indices are sorted ascending by counting.
