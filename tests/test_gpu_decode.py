@@ -41,6 +41,11 @@ SMALL = [
     ("bf16_g4_b20_many_rows", dict(B=20, Hq=32, Hkv=8, lens=[20000, 1, 4100, 64, 65, 127, 8191, 5000, 12345, 300,
                                                              16384, 2, 999, 4096, 7777, 640, 641, 19999, 3000, 10],
                                    top_k=64, dtype="bf16", permute=True)),
+    # 256 (sequence, group) rows: one workgroup per row attends the whole list and writes the final
+    # output (no split, no merge launch); ragged and tiny rows
+    ("bf16_g4_b32_single_split", dict(B=32, Hq=32, Hkv=8, lens=[1, 63, 64, 65] + [97 * i + 5 for i in range(1, 29)],
+                                      top_k=16, dtype="bf16", permute=True)),
+    ("f32_g2_b64_single_split", dict(B=64, Hq=8, Hkv=4, lens=[17 * i + 3 for i in range(64)], top_k=6, dtype="f32")),
 ]
 
 
