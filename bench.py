@@ -69,6 +69,31 @@ def timed_graph(fn_steps, nsteps_graph, torch):
     return g
 
 
+def single_steps(fn_steps, nsteps, torch, scrub_bytes=1 << 30):
+    """Median times of single steps, each a one-step HIP graph timed alone (so the graph's own
+    launch is inside the interval): (warm, cold). Warm steps follow each other; each cold step
+    follows a write of scrub_bytes to an unrelated buffer, outside the timed interval, so no
+    input of the step is left in the infinity cache or an L2 by the step before."""
+    graphs = [timed_graph(lambda i, j=j: fn_steps(j), 1, torch) for j in range(nsteps)]
+    scrub = torch.empty(scrub_bytes, dtype=torch.uint8, device="cuda")
+    res = []
+    for cold in (False, True):
+        times = []
+        for rep in range(3):
+            for j, g in enumerate(graphs):
+                if cold:
+                    scrub.fill_((rep + j) & 0xff)
+                start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                start.record()
+                g.replay()
+                end.record()
+                torch.cuda.synchronize()
+                times.append(start.elapsed_time(end) / 1e3)
+        res.append(float(sorted(times)[len(times) // 2]))
+    del graphs, scrub
+    return res[0], res[1]
+
+
 def run_graph(g, replays, torch):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -176,6 +201,9 @@ def main():
 
     t_step = timed(decode)
     log("decode step: %.2f us" % (t_step * 1e6))
+    t_warm1, t_cold = single_steps(decode, per_graph, torch)
+    log("single decode steps timed alone (graph launch included): %.2f us warm, %.2f us after a 1 GiB "
+        "scrub write" % (t_warm1 * 1e6, t_cold * 1e6))
     # stage timings: Step 1 scoring alone (one kernel), Step 1 (score + top-k), Step 2 (attend + merge)
     # the scoring kernel alone streams summaries only: it rotates over SCORE_POOLS summary pools (the
     # caches' own plus copies), ~1 GB at 1M tokens, so no pool can stay in the 256 MB infinity cache
@@ -242,7 +270,8 @@ def main():
                      "frac": score_gbps / HBM_PEAK_GBPS, "traffic": None, "traffic_detail": None,
                      "bytes_per_launch": score_bytes, "us_per_launch": t_score * 1e6},
         "stages_us": {"score": t_score * 1e6, "select": t_sel * 1e6, "attend_merge": t_att * 1e6,
-                      "step": t_step * 1e6},
+                      "step": t_step * 1e6, "single_step_warm": t_warm1 * 1e6,
+                      "single_step_cold": t_cold * 1e6},
         "attend_roofline": {"bound": "hbm", "kernel": "k_attend_decode + k_merge (msa_attend)",
                             "achieved": kv_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": kv_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kv_bytes},
@@ -647,10 +676,22 @@ def cpu_baseline(args, case, torch, np):
         oracle.decode(**kw)
     dt = time.perf_counter() - t0
     log("cpu oracle: %d steps in %.1f s on %d threads" % (n, dt, threads))
+    # the same oracle on one thread, over a sample of about a fifth of the time
+    kw1 = dict(kw, nthreads=1)
+    t0 = time.perf_counter()
+    oracle.decode(**kw1)
+    one1 = time.perf_counter() - t0
+    n1 = int(max(1, min(1000, 0.2 * args.cpu_seconds / max(one1, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(n1):
+        oracle.decode(**kw1)
+    dt1 = time.perf_counter() - t0
+    log("cpu oracle, one thread: %d steps in %.1f s" % (n1, dt1))
     return {"value": n * case.B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "host_cores": os.cpu_count(),
+            "host_cores": os.cpu_count(), "single_thread_value": n1 * case.B / dt1,
             "sample": "%d decode steps (select from cached fp64 summaries + attend) of the same 1M-token "
-                      "workload, fp64 C oracle, threads over (sequence, KV group) units" % n}
+                      "workload, fp64 C oracle, threads over (sequence, KV group) units; %d more steps on one "
+                      "thread for single_thread_value" % (n, n1)}
 
 
 if __name__ == "__main__":
