@@ -94,6 +94,43 @@ def single_steps(fn_steps, nsteps, torch, scrub_bytes=1 << 30):
     return res[0], res[1]
 
 
+def measured_peaks(torch, msa, read_bytes=4 << 30, mfma_workgroups=1024, mfma_iters=4000):
+    """The GPU's achievable HBM read rate (msa_probe_hbm_read over a read_bytes buffer, far beyond
+    the infinity cache) and bf16 MFMA rate (msa_probe_mfma_bf16: register operands, no memory
+    traffic), each the best of five launches timed with HIP events on the launch stream."""
+    dev = torch.device("cuda")
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            fn()
+            end.record()
+            torch.cuda.synchronize()
+            ts.append(start.elapsed_time(end) / 1e3)
+        return min(ts)
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(msa.PROBE_READ_SINK_FLOATS, dtype=torch.float32, device=dev)
+    t_read = best(lambda: msa.msa_probe_hbm_read(buf, sink))
+    del buf, sink
+    msink = torch.empty(4 * mfma_workgroups, dtype=torch.float32, device=dev)
+    t_mfma = best(lambda: msa.msa_probe_mfma_bf16(msink, mfma_workgroups, mfma_iters))
+    flops = float(mfma_workgroups) * 4 * mfma_iters * 4 * 32768
+    hbm, mf = read_bytes / t_read / 1e9, flops / t_mfma / 1e12
+    log("measured peaks: HBM read %.0f GB/s (%.0f %% of %.0f), bf16 MFMA %.0f TFLOP/s (%.0f %% of %.0f)"
+        % (hbm, 100 * hbm / HBM_PEAK_GBPS, HBM_PEAK_GBPS, mf, 100 * mf / BF16_PEAK_TFLOPS, BF16_PEAK_TFLOPS))
+    return {"hbm_read_GBps": hbm, "hbm_read_frac_of_published": hbm / HBM_PEAK_GBPS,
+            "bf16_mfma_TFLOPs": mf, "bf16_mfma_frac_of_published": mf / BF16_PEAK_TFLOPS,
+            "method": "msa_probe_hbm_read: %d MiB streamed once per launch, 16 B loads, 8 in flight per thread; "
+                      "msa_probe_mfma_bf16: %d workgroups x 4 waves x %d rounds of 4 independent "
+                      "32x32x16 bf16 MFMAs; best of 5 launches each" % (read_bytes >> 20, mfma_workgroups,
+                                                                         mfma_iters)}
+
+
 def run_graph(g, replays, torch):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -304,6 +341,13 @@ def main():
         except msa.MsaError as e:
             log("prefill skipped: %s" % e)
             rec["prefill"] = None
+    # ---- the GPU's own denominators, measured beside the published ones
+    peaks = measured_peaks(torch, msa)
+    rec["measured_peaks"] = peaks
+    rec["roofline"]["frac_of_measured"] = rec["roofline"]["achieved"] / peaks["hbm_read_GBps"]
+    rec["attend_roofline"]["frac_of_measured"] = rec["attend_roofline"]["achieved"] / peaks["hbm_read_GBps"]
+    if rec.get("prefill"):
+        rec["prefill"]["bf16_mfma_frac_of_measured"] = rec["prefill"]["TFLOPs"] / peaks["bf16_mfma_TFLOPs"]
     # ---- CPU oracle baseline (regenerates the first cache of the workload: same seed, same data)
     if not args.no_cpu_baseline:
         c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed))

@@ -17,6 +17,8 @@ MSA_OP_SELECT, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL = range(4)
 
 EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_score", "msa_select", "msa_select_index",
             "msa_attend", "msa_decode_step", "msa_prefill_chunk", "msa_status_string")
+# measurement probes of the GPU itself (include/msa_probe.h)
+EXPORTED_PROBES = ("msa_probe_hbm_read", "msa_probe_mfma_bf16")
 
 
 class MsaConfig(ctypes.Structure):
@@ -71,6 +73,10 @@ def load_library():
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
         lib.msa_status_string.restype = ctypes.c_char_p
+        lib.msa_probe_hbm_read.argtypes = [V, Z, V, V]
+        lib.msa_probe_mfma_bf16.argtypes = [V, I, I, V]
+        for name in EXPORTED_PROBES:
+            getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -198,3 +204,23 @@ def msa_prefill_chunk(cfg: MsaConfig, q, k_new, v_new, cache: KVCache, past_len:
                                             past_len, T, _p(idx_out), _p(scores_out), _p(out), _p(lse_out),
                                             _p(ws), nbytes, _stream(stream, q)),
            "msa_prefill_chunk")
+
+
+PROBE_READ_SINK_FLOATS = 2048 * 256
+
+
+def msa_probe_hbm_read(buf, sink, stream=None) -> None:
+    """Streaming read of the whole device tensor buf (bytes a multiple of 16); sink: a float32
+    device tensor of PROBE_READ_SINK_FLOATS elements."""
+    nbytes = int(buf.numel()) * int(buf.element_size())
+    if int(sink.numel()) < PROBE_READ_SINK_FLOATS:
+        raise ValueError("sink needs %d floats" % PROBE_READ_SINK_FLOATS)
+    _check(load_library().msa_probe_hbm_read(_p(buf), nbytes, _p(sink), _stream(stream, buf)), "msa_probe_hbm_read")
+
+
+def msa_probe_mfma_bf16(sink, workgroups: int, iters: int, stream=None) -> None:
+    """bf16 MFMA chains: workgroups * 4 * iters * 4 * 32768 FLOP; sink: >= 4 * workgroups floats."""
+    if int(sink.numel()) < 4 * workgroups:
+        raise ValueError("sink needs %d floats" % (4 * workgroups))
+    _check(load_library().msa_probe_mfma_bf16(_p(sink), int(workgroups), int(iters), _stream(stream, sink)),
+           "msa_probe_mfma_bf16")

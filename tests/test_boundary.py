@@ -18,8 +18,8 @@ if not os.path.exists(L.library_path()):
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:msa_status|const char\*)\s+(msa_\w+)\s*\(", text, re.M)))
 
 
@@ -27,8 +27,23 @@ def test_exports_every_declared_symbol():
     lib = L.load_library()
     names = declared_functions()
     assert set(names) == set(L.EXPORTED)
-    for n in names:
+    probes = declared_functions(os.path.join(ROOT, "include", "msa_probe.h"))
+    assert set(probes) == set(L.EXPORTED_PROBES)
+    for n in names + probes:
         assert hasattr(lib, n), n
+
+
+def test_probe_argument_validation():
+    lib = L.load_library()
+    sink = ctypes.c_void_p(16)   # never dereferenced: every call below is rejected on the host
+    assert lib.msa_probe_hbm_read(None, 1 << 20, sink, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_hbm_read(ctypes.c_void_p(256), 100, sink, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_hbm_read(ctypes.c_void_p(8), 1 << 20, sink, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_hbm_read(ctypes.c_void_p(256), 1 << 20, None, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_bf16(None, 8, 10, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_bf16(sink, 0, 10, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_bf16(sink, 8, 0, None) == L.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_bf16(sink, 70000, 10, None) == L.MSA_ERR_INVALID_ARG
 
 
 def test_status_strings():
