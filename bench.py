@@ -162,6 +162,9 @@ def main():
                     help="counter pass: eager launches of the scoring kernel over the rotating caches, of the "
                          "k = 1024 attend and of the index-branch select, then of a 256 MiB device copy (the "
                          "byte-count calibration), for rocprofv3 --pmc; no timing")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill chunk line (its own JSON object), e.g. for rocprofv3 --pmc passes "
+                         "over the MFMA attend")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -174,6 +177,10 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev)}),
+              flush=True)
+        return
     kw = workload(args.workload, seed=args.seed)
     L = max(1, args.layers)
     log("generating %d caches of %s" % (L, args.workload))
