@@ -8,10 +8,11 @@
 // <q_index[b][g], K_idx[t]>, unscaled; a block's score is the maximum over its valid tokens;
 // blocks past a sequence's length, or on a bad page id, score -inf.
 //
-// HBM-bound streaming of the index keys (64 x 128 elements per block): a workgroup owns 4 blocks
-// of one sequence; thread -> (tokens t = tid/8 and t + 32 of the block, an eighth of their
-// dims), so each load instruction reads whole 128 B lines (index dimension 64 or 128), and every thread's loads for the 4
-// blocks are in flight before any arithmetic. Dot products are packed bf16 dot2 (fp32 FMAs for
+// HBM-bound streaming of the index keys (64 x 128 elements per block): a workgroup owns kIB
+// blocks of one sequence (one: 16,384 workgroups at 1M tokens; 1, 2, 4 and 8 swept, one was
+// fastest); thread -> (tokens t = tid/8 and t + 32 of the block, an eighth of their dims), so
+// each load instruction reads whole 128 B lines (index dimension 64 or 128), and every thread's
+// loads for its blocks are in flight before any arithmetic. Dot products are packed bf16 dot2 (fp32 FMAs for
 // fp32 keys) against the Hkv index queries held in LDS, summed across the 8 lanes of a token
 // with DPP, max-reduced with DPP over each 16-lane row (4 tokens) and through LDS over the
 // block's 16 rows.
@@ -22,7 +23,7 @@ namespace msa {
 
 namespace {
 
-constexpr int kIB = 4;   // blocks per workgroup
+constexpr int kIB = 1;   // blocks per workgroup
 
 // One thread's share of a block: two tokens (t and t + 32) of the block, and of each token the
 // 16 B chunks c, c + 8, ... (c = lane of the token's 8), so the 8 lanes of a token read one whole
@@ -119,7 +120,7 @@ __global__ void __launch_bounds__(256) k_score_index(const T* __restrict__ q_ind
     }
   }
   __syncthreads();
-  for (int e = tid; e < Hkv * kIB; e += 256) {       // g-major: each row's 4 scores are contiguous
+  for (int e = tid; e < Hkv * kIB; e += 256) {       // g-major: each row's kIB scores are contiguous
     const int g = e / kIB, u = e % kIB, j = j0 + u;
     if (j >= row_stride) continue;
     const float4* w16 = reinterpret_cast<const float4*>(s_wm + (u * Hkv + g) * 16);
