@@ -287,6 +287,7 @@ def main():
     # algorithmic bytes of one scoring launch: summaries + block-table entries read, scores written
     score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
     kv_gbps = kv_bytes / t_att / 1e9
+    step_bytes = score_bytes + kv_bytes + 2 * B * Hq * D * elem + B * Hkv * k * 4
     score_gbps = score_bytes / t_score / 1e9
     log("score %.2f us (%.0f GB/s); select %.2f us; attend %.2f us (%.0f GB/s of selected KV)"
         % (t_score * 1e6, score_gbps, t_sel * 1e6, t_att * 1e6, kv_gbps))
@@ -309,6 +310,11 @@ def main():
                    "caches_rotated": L, "graph_steps": per_graph},
         "kv_GBps": kv_gbps,
         "kv_hbm_frac": kv_gbps / HBM_PEAK_GBPS,
+        # the whole step's algorithmic bytes (summaries, table, scores, selected K/V, q twice, o, the
+        # index lists) over the step time, beside the selected-KV rate so Step 1's cost is not hidden
+        "step_GBps": step_bytes / t_step / 1e9,
+        "step_hbm_frac": step_bytes / t_step / 1e9 / HBM_PEAK_GBPS,
+        "step_bytes": step_bytes,
         "roofline": {"bound": "hbm", "kernel": "k_score_decode (msa_score): Step 1 block scoring",
                      "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": score_gbps / HBM_PEAK_GBPS, "traffic": None, "traffic_detail": None,
