@@ -200,7 +200,11 @@ msa_status msa_workspace_size(const msa_config* cfg, int32_t op, int32_t batch, 
     case MSA_OP_SELECT:
     case MSA_OP_ATTEND:
     case MSA_OP_DECODE:
-      *bytes = decode_layout(cfg, op, batch, max_seq_len).total;
+      {
+        const Layout L = decode_layout(cfg, op, batch, max_seq_len);
+        if (L.nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;   // never: the split rule bounds it
+        *bytes = L.total;
+      }
       return MSA_OK;
     case MSA_OP_PREFILL:
       if (chunk_len < 1 || batch != 1 || max_seq_len < chunk_len) return MSA_ERR_INVALID_ARG;
@@ -279,6 +283,7 @@ msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   MSA_TRY(check_batch(cache, batch, max_seq_len));
   if (q == nullptr || idx == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
   const Layout L = decode_layout(cfg, MSA_OP_ATTEND, batch, max_seq_len);
+  if (L.nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
@@ -294,6 +299,7 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
   MSA_TRY(check_batch(cache, batch, max_seq_len));
   if (q == nullptr || out == nullptr || ((k_new == nullptr) != (v_new == nullptr))) return MSA_ERR_INVALID_ARG;
   const Layout L = decode_layout(cfg, MSA_OP_DECODE, batch, max_seq_len);
+  if (L.nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;

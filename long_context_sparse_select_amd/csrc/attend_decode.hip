@@ -80,7 +80,7 @@ template <> struct Q8<float> {
   }
 };
 
-constexpr int kMaxSplit = 256;
+constexpr int kMaxSplit = kMaxDecodeSplit;
 
 template <typename T> __device__ __forceinline__ void store_out2(T* out, long long i, float a, float b);
 template <> __device__ __forceinline__ void store_out2<uint16_t>(uint16_t* out, long long i, float a, float b) {
@@ -550,7 +550,7 @@ hipError_t launch_attend_typed(const AttendArgs& a, int G, hipStream_t st) {
 // output, and the merge launch goes away (batch 32 x 8 groups, k = 64: attend 104.6 -> 99.5 us).
 int decode_blocks_per_split(int B, int Hkv, int k) {
   const long long rows = (long long)B * Hkv;
-  if (k <= 2 || rows * ((k + 1) / 2) <= 512) return 2;
+  if (k <= 2 || (rows * ((k + 1) / 2) <= 512 && (k + 1) / 2 <= kMaxSplit)) return 2;
   if (rows >= 256) return k;
   int bps = 4;
   while (bps < k && (rows * ((k + bps - 1) / bps) > 512 || (k + bps - 1) / bps > kMaxSplit)) bps *= 2;

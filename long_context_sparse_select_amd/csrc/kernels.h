@@ -1,5 +1,5 @@
 // Internal launchers of libmsa (host side). Every launcher enqueues on `st` and returns the
-// launch status; all argument validation happens before, in api.cpp.
+// launch status; all argument validation happens before, in api.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,6 +84,9 @@ struct AttendArgs {
   void* out;            // [B][Hq][128]
   float* lse;           // nullable [B][Hq]
 };
+// Split-K partials one merge workgroup combines; decode_blocks_per_split keeps the split count
+// ceil(k / blocks_per_split) at or below it for every (B, Hkv, k).
+constexpr int kMaxDecodeSplit = 256;
 int decode_blocks_per_split(int B, int Hkv, int k);
 hipError_t launch_attend_decode(bool bf16, const AttendArgs& a, hipStream_t st);
 

@@ -80,6 +80,20 @@ def test_workspace_sizes():
     assert ws_size(c, 17)[0] == L.MSA_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 8, 1), (1, 4, 2), (1, 32, 8), (2, 8, 1), (3, 16, 8), (8, 32, 8),
+                                      (31, 32, 8), (32, 32, 8), (300, 8, 1)])
+def test_attend_splits_fit_one_merge_workgroup(B, Hq, Hkv):
+    """The attend workspace holds B * Hq * nsplit partials of 128 + 2 floats (two 256-aligned
+    arrays); one merge workgroup combines at most 256 splits, so for every k the workspace must
+    stay within 256 splits' worth (a 257th split would add B * Hq * 520 bytes, more than the
+    alignment slack)."""
+    for k in list(range(1, 1100)) + list(range(1100, 4097, 37)) + [4096]:
+        c = cfg(num_q_heads=Hq, num_kv_heads=Hkv, top_k=k)
+        st, att = ws_size(c, L.MSA_OP_ATTEND, B, 1 << 20)
+        assert st == 0
+        assert att <= B * Hq * 256 * (128 + 2) * 4 + 510, (B, Hq, Hkv, k)
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("num_q_heads", 0, L.MSA_ERR_INVALID_ARG),
     ("num_q_heads", 30, L.MSA_ERR_INVALID_ARG),        # Hq % Hkv != 0

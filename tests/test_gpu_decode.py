@@ -37,6 +37,10 @@ SMALL = [
     # large k: the exact selection path (range-refined threshold + ordered compaction)
     ("bf16_g4_k1024", dict(B=1, Hq=8, Hkv=2, lens=[262144], top_k=1024, dtype="bf16", permute=True)),
     ("f32_g2_k700_ragged", dict(B=2, Hq=4, Hkv=2, lens=[100000, 45000], top_k=700, dtype="f32")),
+    # one (sequence, group) row with k above 512 (the fp32 workload's head layout): the attend must
+    # still fit its splits in one merge workgroup (at most 256), so every list entry is attended
+    ("bf16_g8_hkv1_k1024", dict(B=1, Hq=8, Hkv=1, lens=[70001], top_k=1024, dtype="bf16", permute=True)),
+    ("f32_g8_hkv1_k600", dict(B=1, Hq=8, Hkv=1, lens=[40000], top_k=600, dtype="f32")),
     # 160 (sequence, group) rows: sixteen blocks per workgroup (four chunks of four), ragged rows
     ("bf16_g4_b20_many_rows", dict(B=20, Hq=32, Hkv=8, lens=[20000, 1, 4100, 64, 65, 127, 8191, 5000, 12345, 300,
                                                              16384, 2, 999, 4096, 7777, 640, 641, 19999, 3000, 10],
