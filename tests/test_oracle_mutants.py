@@ -63,6 +63,14 @@ MUTANTS = [
      "        if (0)\n            for", False),
     ("prefill_forced_dropped", "orc_topk_forced(s, diag, K, a->keep_sink, a->keep_local, sel)",
      "orc_topk_forced(s, diag, K, 0, 0, sel)", False),
+    # the prefill route over given lists (idx_in)
+    ("prefill_idx_in_drops_diagonal", "if (sel[e] < 0 || sel[e] > diag) sel[e] = -1;",
+     "if (sel[e] < 0 || sel[e] >= diag) sel[e] = -1;", False),
+    ("prefill_idx_in_last_slot_dropped", "        keff = K;\n", "        keff = K - 1;\n", False),
+    ("prefill_idx_in_ignored", "        memcpy(sel, a->idx_in +", "        if (0) memcpy(sel, a->idx_in +", False),
+    # the index branch's rows
+    ("index_scores_row_of_other_group", "double* srow = scores_out + ((size_t)b * Hkv + g) * max_blocks;",
+     "double* srow = scores_out + ((size_t)b * Hkv + (Hkv - 1 - g)) * max_blocks;", False),
 ]
 
 

@@ -331,6 +331,48 @@ def test_prefill_selection_and_tile_scores():
             assert list(r["idx"][tau, g]) == list(sel) + [d]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_idx_override(dtype):
+    """The prefill oracle's route that attends over given lists (the GPU tests fall back to it when
+    a GPU list differs from the oracle's inside the tie band):
+      * its own lists fed back reproduce the plain run bit for bit;
+      * a list with one selected block dropped, a -1 entry and entries above the tile's diagonal
+        block equals dense causal attention (torch SDPA, float64) whose mask keeps only the listed
+        blocks at or below the diagonal: those above it are ignored, the diagonal (the last slot,
+        position top_k) still counts."""
+    past, T, k, Hkv, G = 640, 150, 4, 2, 4
+    c = make_prefill_case(Hq=Hkv * G, Hkv=Hkv, past_len=past, T=T, top_k=k, dtype=dtype, seed=31)
+    kw = prefill_inputs(c)
+    r = oracle.prefill(**kw)
+    r2 = oracle.prefill(idx_in=r["idx"], **kw)
+    np.testing.assert_array_equal(r2["o"], r["o"])
+    np.testing.assert_array_equal(r2["lse"], r["lse"])
+    ntiles = (T + 63) // 64
+    idx = r["idx"].copy()
+    for tau in range(ntiles):
+        d = past // 64 + tau
+        for g in range(Hkv):
+            assert idx[tau, g, k] == d                     # k_eff = k here: the diagonal is the last slot
+            idx[tau, g, (tau + g) % k] = -1                # one selected block dropped
+            idx[tau, g, (tau + g + 1) % k] = d + 1 + g     # above the diagonal: ignored
+    rt = oracle.prefill(idx_in=idx, **kw)
+    N = past + T
+    K = as_f64(storage(np.concatenate([logical_kv(c.k_pool, c.block_table, 0, past), c.k_new]), dtype))
+    V = as_f64(storage(np.concatenate([logical_kv(c.v_pool, c.block_table, 0, past), c.v_new]), dtype))
+    q = as_f64(kw["q"])
+    for tau in range(ntiles):
+        rows = np.arange(tau * 64, min(T, tau * 64 + 64))
+        d = past // 64 + tau
+        for g in range(Hkv):
+            keep = [j for j in idx[tau, g] if 0 <= j <= d]
+            assert len(keep) == k - 1                      # k - 2 selected blocks + the diagonal
+            mask = np.isin(np.arange(N) // 64, keep)[None, :] & (np.arange(N)[None, :] <= (past + rows)[:, None])
+            heads = slice(g * G, (g + 1) * G)
+            o, lse = dense_gqa(q[rows][:, heads], K[:, g:g + 1], V[:, g:g + 1], c.scale, mask=mask)
+            np.testing.assert_allclose(rt["o"][rows][:, heads], o, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(rt["lse"][rows][:, heads], lse, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- index branch (R8)
 # The pages' literal Step 1: single-head index keys shared by every group, one index query per
 # group, token scores, Block Max Pool, TopK (oracle.select_index).
@@ -421,6 +463,26 @@ def test_index_invariances():
     ru = oracle.select_index(q_idx=round_to_bf16(q), index_keys=round_to_bf16(ik), block_table=table,
                              seq_lens=lens, top_k=3)
     assert np.array_equal(rb["scores"], ru["scores"]) and np.array_equal(rb["idx"], ru["idx"])
+
+
+def test_index_query_scaling_and_group_order():
+    """A positive factor on an index query scales every token score and hence every block maximum
+    by that factor (exactly for a power of two) and keeps the lists; permuting the groups of the
+    index queries permutes the score rows and the lists the same way."""
+    q, ik, table, lens = _index_case(lens=(200, 64, 131, 700), Hkv=4, Di=16, seed=17)
+    base = oracle.select_index(q_idx=q, index_keys=ik, block_table=table, seq_lens=lens, top_k=3)
+    fin = np.isfinite(base["scores"])
+    r4 = oracle.select_index(q_idx=q * np.float32(4.0), index_keys=ik, block_table=table, seq_lens=lens, top_k=3)
+    assert np.array_equal(r4["scores"][fin], 4.0 * base["scores"][fin])
+    assert np.array_equal(np.isfinite(r4["scores"]), fin) and np.array_equal(r4["idx"], base["idx"])
+    c = np.array([0.25, 8.0, 2.0, 0.5], np.float32)[None, :, None]    # a different factor per group
+    rc = oracle.select_index(q_idx=q * c, index_keys=ik, block_table=table, seq_lens=lens, top_k=3)
+    assert np.array_equal(rc["scores"][fin], (base["scores"] * c.astype(np.float64))[fin])
+    assert np.array_equal(rc["idx"], base["idx"])
+    perm = np.array([2, 0, 3, 1])
+    rp = oracle.select_index(q_idx=np.ascontiguousarray(q[:, perm]), index_keys=ik, block_table=table, seq_lens=lens,
+                             top_k=3)
+    assert np.array_equal(rp["scores"], base["scores"][:, perm]) and np.array_equal(rp["idx"], base["idx"][:, perm])
 
 
 def test_index_planted_token_and_bad_page():
