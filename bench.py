@@ -52,13 +52,14 @@ def selected_kv_bytes(idx, lens, P=64, D=128, elem=2):
     return total
 
 
-def timed_graph(fn_steps, nsteps_graph, torch):
-    """Capture nsteps_graph calls of fn_steps(i) (after one eager pass) in a HIP graph."""
+def timed_graph(fn_steps, nsteps_graph, torch, eager_first=True):
+    """Capture nsteps_graph calls of fn_steps(i) in a HIP graph; with eager_first, one eager call
+    on the capture stream first (so every kernel's code object is loaded before the capture)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(nsteps_graph):   # eager warm pass on the capture stream
-            fn_steps(i)
+    if eager_first:
+        with torch.cuda.stream(s):
+            fn_steps(0)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -131,6 +132,34 @@ def measured_peaks(torch, msa, read_bytes=4 << 30, mfma_workgroups=1024, mfma_it
                                                                          mfma_iters)}
 
 
+GRAPH_MAX_STEPS = 200
+
+
+def time_exact_steps(fn, steps, warmup, torch):
+    """Seconds per step over exactly `steps` calls fn(0), fn(1), ... replayed from HIP graphs of at
+    most GRAPH_MAX_STEPS calls (a full graph replayed steps // per times, then a graph of the
+    remainder), after exactly `warmup` untimed calls fn(0) .. fn(warmup - 1) on the same stream.
+    HIP events on the launch stream bracket the replays, with a device synchronisation on both
+    sides, so the launch of each graph is inside the timed interval."""
+    per = max(1, min(GRAPH_MAX_STEPS, steps))
+    full, rem = divmod(steps, per)
+    g_full = timed_graph(fn, per, torch)
+    g_rem = timed_graph(fn, rem, torch, eager_first=False) if rem else None
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
 def run_graph(g, replays, torch):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -147,11 +176,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
+    ap.add_argument("--layers", type=int, default=16,
+                    help="independent caches rotated over the steps (16 x 4 GiB of K/V at 1M tokens; the "
+                         "summaries and selected K/V the steps read total about 1.3 GB, about five times "
+                         "the 256 MB infinity cache)")
     ap.add_argument("--workload", default="decode_bf16_1m_paged")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 attend bandwidth line")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batch-8 x 131072-token decode line")
     ap.add_argument("--no-mixed", action="store_true", help="skip the batch-32 mixed-length decode line")
     ap.add_argument("--no-large-k", action="store_true", help="skip the 1M-token k=1024 operating-point line")
     ap.add_argument("--no-index", action="store_true", help="skip the 1M-token index-branch select line")
@@ -232,22 +264,20 @@ def main():
         counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
         return
 
-    # one graph holds up to 200 steps (whole rotations of the caches and queries), so the launch of
-    # the graph itself (~9 us) is spread over them; --steps below that shrinks the graph
+    # exactly --steps steps (step i: cache i % L, query i % R) from graphs of up to 200 steps, so the
+    # launch of a graph (~9 us, see single_step_warm) is spread over many steps, after exactly
+    # --warmup untimed steps
     rot = L * R // math.gcd(L, R) if L * R <= 64 else L
-    per_graph = rot * max(1, min(200, args.steps) // rot)
-    replays = max(1, args.steps // per_graph)
-    steps = replays * per_graph
-    wreplays = max(1, args.warmup // per_graph)
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+    per_graph = min(GRAPH_MAX_STEPS, steps)
 
     def timed(fn):
-        """seconds per call of fn(i), graph-replayed over the same rotation as the step"""
-        g = timed_graph(fn, per_graph, torch)
-        run_graph(g, wreplays, torch)
-        return run_graph(g, replays, torch) / steps
+        """seconds per call of fn(i) over the same schedule as the timed steps"""
+        return time_exact_steps(fn, steps, warmup, torch)
 
     t_step = timed(decode)
-    log("decode step: %.2f us" % (t_step * 1e6))
+    log("decode step: %.2f us (%d steps timed after %d warmup steps, %d caches rotated)"
+        % (t_step * 1e6, steps, warmup, L))
     t_warm1, t_cold = single_steps(decode, rot, torch)
     log("single decode steps timed alone (graph launch included): %.2f us warm, %.2f us after a 1 GiB "
         "scrub write" % (t_warm1 * 1e6, t_cold * 1e6))
@@ -291,6 +321,7 @@ def main():
     score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
     kv_gbps = kv_bytes / t_att / 1e9
     step_bytes = score_bytes + kv_bytes + 2 * B * Hq * D * elem + B * Hkv * k * 4
+    working_set = L * step_bytes   # what the rotation of the timed steps reads, in distinct bytes
     score_gbps = score_bytes / t_score / 1e9
     log("score %.2f us (%.0f GB/s); select %.2f us; attend %.2f us (%.0f GB/s of selected KV)"
         % (t_score * 1e6, score_gbps, t_sel * 1e6, t_att * 1e6, kv_gbps))
@@ -301,7 +332,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": wreplays * per_graph,
+        "warmup": warmup,
         "ms_per_step": t_step * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -310,7 +341,8 @@ def main():
         "data": "synthetic (seeded N(0,1) q/K/V, planted blocks, permuted 64-token pages)",
         "config": {"workload": args.workload, "batch": B, "context": int(max_len), "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "block": 64, "top_k": k,
-                   "caches_rotated": L, "graph_steps": per_graph},
+                   "caches_rotated": L, "step_working_set_bytes": working_set,
+                   "graph_steps": per_graph},
         "kv_GBps": kv_gbps,
         "kv_hbm_frac": kv_gbps / HBM_PEAK_GBPS,
         # the whole step's algorithmic bytes (summaries, table, scores, selected K/V, q twice, o, the
@@ -330,10 +362,10 @@ def main():
                             "frac": kv_gbps / HBM_PEAK_GBPS, "bytes_per_launch": kv_bytes},
     }
     if not args.no_large_k:
-        rec["large_k"] = bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph)
+        rec["large_k"] = bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot)
     if not args.no_bf16_summaries:
         rec["bf16_summaries"] = bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L,
-                                                     R, per_graph)
+                                                     R, rot)
     tr = recorded_traffic(score_bytes)
     if tr is not None:
         rec["roofline"]["traffic"] = tr["bytes_per_launch"]
@@ -341,7 +373,7 @@ def main():
     del caches, cases, q_ring, kn_ring, vn_ring, idx_bufs, ws
     torch.cuda.empty_cache()
     if not args.no_batched:
-        rec["batched_attend"] = bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev)
+        rec["batched_decode"] = bench_batched(args, torch, np, msa, make_decode_case_torch, workload, dev)
         torch.cuda.empty_cache()
     if not args.no_mixed:
         rec["mixed_batch"] = bench_mixed(args, torch, np, msa, make_decode_case_torch, workload, dev)
@@ -364,6 +396,8 @@ def main():
     rec["attend_roofline"]["frac_of_measured"] = rec["attend_roofline"]["achieved"] / peaks["hbm_read_GBps"]
     if rec.get("prefill"):
         rec["prefill"]["bf16_mfma_frac_of_measured"] = rec["prefill"]["TFLOPs"] / peaks["bf16_mfma_TFLOPs"]
+        rec["prefill"]["roofline"]["frac_of_measured"] = (rec["prefill"]["roofline"]["achieved"]
+                                                          / peaks["bf16_mfma_TFLOPs"])
     # ---- CPU oracle baseline (regenerates the first cache of the workload: same seed, same data)
     if not args.no_cpu_baseline:
         c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed))
@@ -468,11 +502,13 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
     cfg = msa.make_config(p.Hq, p.Hkv, p.top_k, dtype="bf16", softmax_scale=p.scale)
     msa.msa_build_summaries(cfg, cache, 1, p.past_len)
     out = torch.empty_like(p.q)
+    ntiles = (p.T + 63) // 64
+    idx = torch.empty((ntiles, p.Hkv, p.top_k + 1), dtype=torch.int32, device=dev)
     ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_PREFILL, 1, p.past_len + p.T, p.T),
                      dtype=torch.uint8, device=dev)
 
     def chunk(i):
-        msa.msa_prefill_chunk(cfg, p.q, p.k_new, p.v_new, cache, p.past_len, p.T, out, workspace=ws)
+        msa.msa_prefill_chunk(cfg, p.q, p.k_new, p.v_new, cache, p.past_len, p.T, out, idx_out=idx, workspace=ws)
 
     chunk(0)
     torch.cuda.synchronize()
@@ -483,7 +519,11 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
     run_graph(g, 2, torch)
     n = 6
     t = run_graph(g, n, torch) / (n * per)
-    ntiles = (p.T + 63) // 64
+    # Step 2 alone (msa_prefill_attend: one k_attend_prefill launch) over the chunk's own lists
+    ga = timed_graph(lambda i: msa.msa_prefill_attend(cfg, p.q, cache, p.past_len, p.T, idx, out), per, torch)
+    run_graph(ga, 2, torch)
+    t_att = run_graph(ga, n, torch) / (n * per)
+    del g, ga
     pairs = 0
     for tau in range(ntiles):
         rows = min(64, p.T - tau * 64)
@@ -491,19 +531,26 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
         pairs += rows * 64 * keff + rows * (rows + 1) // 2
     flops = 4.0 * p.D * p.Hq * pairs
     tf = flops / t / 1e12
-    log("prefill chunk: %.1f us, %.1f TFLOP/s (causal-visible, whole chunk)" % (t * 1e6, tf))
+    tfa = flops / t_att / 1e12
+    log("prefill chunk: %.1f us, %.1f TFLOP/s (causal-visible, whole chunk); attend alone %.1f us, %.1f TFLOP/s"
+        % (t * 1e6, tf, t_att * 1e6, tfa))
     return {"workload": "prefill_bf16_4k_on_256k", "chunk_us": t * 1e6, "TFLOPs": tf,
             "bf16_mfma_frac": tf / BF16_PEAK_TFLOPS, "flops": flops,
-            "note": "whole chunk: append + summaries + tile query + score + top-k + MFMA attend"}
+            "note": "whole chunk: append + summaries + tile query + score + top-k + MFMA attend",
+            "roofline": {"bound": "mfma", "kernel": "k_attend_prefill (msa_prefill_attend): Step 2 of the chunk",
+                         "achieved": tfa, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tfa / BF16_PEAK_TFLOPS,
+                         "flops_per_launch": flops, "us_per_launch": t_att * 1e6,
+                         "flops_rule": "4 * 128 * Hq * (causal-visible query-key pairs of the selected blocks)"}}
 
 
-def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload, dev):
-    """Gather-attend bandwidth on the batch-8, 131072-token workload (64 MiB of selected K/V per
-    launch, so the stage is less latency-bound than at batch 1). Two caches, eight queries each:
-    16 selected lists (1 GiB of selected K/V, beyond the infinity cache) attended in rotation."""
+def bench_batched(args, torch, np, msa, make_decode_case_torch, workload, dev, L=8, R=8):
+    """The batch-8, 131,072-token workload (32 q / 8 kv heads, k = 32, in-order pages): whole decode
+    steps (append + score + top-k + attend + merge), the scoring kernel alone and the attend stage
+    alone. L caches (4 GiB of K/V each) rotated with R fresh queries: a step reads 64 MiB of
+    summaries and 64 MiB of selected K/V, so the rotation of each stage reads several times the
+    256 MB infinity cache."""
     kw = workload("decode_bf16_b8_128k", seed=args.seed)
-    L, NQ = 2, 8
-    items = []
+    caches, cases = [], []
     for layer in range(L):
         c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed + 1000 * layer))
         table = torch.from_numpy(c.block_table).to(dev)
@@ -512,32 +559,62 @@ def bench_batched_attend(args, torch, np, msa, make_decode_case_torch, workload,
         cache = msa.KVCache(c.k_pool, c.v_pool, S, table, lens)
         cfg = msa.make_config(c.Hq, c.Hkv, c.top_k, dtype="bf16", softmax_scale=c.scale)
         msa.msa_build_summaries(cfg, cache, c.B, c.max_seq_len)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(args.seed + 77 + layer)
-        qs = [c.q] + [torch.randn(c.q.shape, generator=gen, device=dev, dtype=torch.float32).to(c.q.dtype)
-                      for _ in range(NQ - 1)]
-        for q in qs:
-            idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device=dev)
-            msa.msa_select(cfg, q, cache, c.B, c.max_seq_len, idx)
-            items.append((c, cache, idx, q))
-    c0 = items[0][0]
-    out = torch.empty_like(c0.q)
-    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, c0.B, c0.max_seq_len), dtype=torch.uint8,
-                     device=dev)
+        caches.append(cache)
+        cases.append(c)
+    c0 = cases[0]
+    B, Hq, Hkv, D, k, max_len = c0.B, c0.Hq, c0.Hkv, c0.D, c0.top_k, c0.max_seq_len
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 77)
+    q_ring = [torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    kn_ring = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    vn_ring = [torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    idx_bufs = [torch.empty((B, Hkv, k), dtype=torch.int32, device=dev) for _ in range(L)]
+    sc = torch.empty((B, Hkv, (max_len + 63) // 64), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    P = len(items)
-    g = timed_graph(lambda i: msa.msa_attend(cfg, items[i % P][3], items[i % P][1], c0.B, c0.max_seq_len,
-                                             items[i % P][2], out, workspace=ws), P, torch)
-    run_graph(g, 2, torch)
-    n = 12
-    t = run_graph(g, n, torch) / (P * n)
-    kv = float(np.mean([selected_kv_bytes(it[2], it[0].seq_lens) for it in items]))
-    log("batch-8 attend: %.2f us, %.0f GB/s of selected KV" % (t * 1e6, kv / t / 1e9))
-    return {"workload": "decode_bf16_b8_128k", "attend_us": t * 1e6, "kv_GBps": kv / t / 1e9,
-            "kv_hbm_frac": kv / t / 1e9 / HBM_PEAK_GBPS, "bytes_per_launch": kv}
+    per = L * R // math.gcd(L, R)
+    per = per * max(1, 64 // per)
+    n_rep = 10
+
+    def timed(fn, n=per):
+        g = timed_graph(fn, n, torch)
+        run_graph(g, 2, torch)
+        return run_graph(g, n_rep, torch) / (n * n_rep)
+    t_step = timed(lambda i: msa.msa_decode_step(cfg, q_ring[i % R], caches[i % L], B, max_len, out,
+                                                 k_new=kn_ring[i % R], v_new=vn_ring[i % R], idx_out=idx_bufs[i % L],
+                                                 lse_out=lse, workspace=ws))
+    t_score = timed(lambda i: msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc))
+    # Step 2 alone: one selected list per (cache, query) pair, L * R lists (4 GiB of selected K/V)
+    att = []
+    for l in range(L):
+        for r in range(R):
+            idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+            msa.msa_select(cfg, q_ring[r], caches[l], B, max_len, idx, workspace=ws)
+            att.append((caches[l], q_ring[r], idx, cases[l].seq_lens))
+    PA = len(att)
+    t_att = timed(lambda i: msa.msa_attend(cfg, att[i % PA][1], att[i % PA][0], B, max_len, att[i % PA][2], out,
+                                           lse_out=lse, workspace=ws), PA)
+    torch.cuda.synchronize()
+    kv = float(np.mean([selected_kv_bytes(a[2], a[3]) for a in att]))
+    nb_tot = sum((int(n) + 63) // 64 for n in c0.seq_lens)
+    score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * 2
+    step_bytes = score_bytes + kv + 2 * B * Hq * D * 2 + B * Hkv * k * 4
+    log("batch-8 x 131072: step %.2f us (%.0f tokens/s, %.0f GB/s of step bytes); score %.2f us (%.0f GB/s); "
+        "attend %.2f us (%.0f GB/s of selected KV)" % (t_step * 1e6, B / t_step, step_bytes / t_step / 1e9,
+                                                      t_score * 1e6, score_bytes / t_score / 1e9, t_att * 1e6,
+                                                      kv / t_att / 1e9))
+    del caches, cases, att
+    return {"workload": "decode_bf16_b8_128k", "batch": B, "context": int(max_len), "top_k": k,
+            "caches_rotated": L, "step_us": t_step * 1e6, "tokens_per_s": B / t_step,
+            "step_GBps": step_bytes / t_step / 1e9, "step_hbm_frac": step_bytes / t_step / 1e9 / HBM_PEAK_GBPS,
+            "step_bytes": step_bytes, "score_us": t_score * 1e6, "score_GBps": score_bytes / t_score / 1e9,
+            "score_bytes_per_launch": score_bytes, "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9,
+            "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS, "bytes_per_attend": kv}
 
 
-def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph, k=1024):
+def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot, k=1024):
     """The pages' operating point on the same 1M-token caches: k = 1024 of 16,384 blocks (~6 %),
     256 MiB of selected K/V per step. Whole decode steps, Step 1 (score + top-k) and Step 2."""
     c0 = cases[0]
@@ -549,6 +626,7 @@ def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring,
     ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     n_rep = 10
+    per_graph = rot * max(1, 32 // rot)   # whole rotations of the caches and queries
 
     def timed(fn):
         g = timed_graph(fn, per_graph, torch)
@@ -572,7 +650,7 @@ def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring,
             "note": "the pages' ~6 % operating point (16,384 blocks, k = 1024); same caches as the headline"}
 
 
-def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, per_graph):
+def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot):
     """The 1M-token decode with a bf16 summary pool (32 MiB instead of 64 MiB read by Step 1) on
     the same rotated K/V caches: whole decode steps and the scoring kernel alone."""
     c0 = cases[0]
@@ -592,6 +670,7 @@ def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, v
     ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     n_rep = 10
+    per_graph = rot * max(1, 32 // rot)   # whole rotations of the caches and queries
 
     def timed(fn):
         g = timed_graph(fn, per_graph, torch)
@@ -711,8 +790,12 @@ def bench_index(args, torch, np, msa, dev, L=2, R=8):
 
 
 def cpu_baseline(args, case, torch, np):
-    """The fp64 oracle (untuned) on a bounded sample of the same decode workload: select from
-    cached block summaries + attend, for as many steps as fit in about --cpu-seconds."""
+    """The fp64 oracle (untuned) on a bounded sample of the same decode workload: select from cached
+    block summaries + attend. One oracle call threads over the (sequence, KV group) units (8 at
+    batch 1); to use every host core of this process, independent steps run concurrently in as many
+    instances as the units divide into the cores (ctypes releases the interpreter lock during the
+    oracle call). Three runs of about --cpu-seconds / 3 each; the median rate is the value."""
+    import threading
     import oracle
 
     def host_storage(t):
@@ -725,20 +808,29 @@ def cpu_baseline(args, case, torch, np):
     S = oracle.summaries(k_pool=k, block_table=case.block_table, seq_lens=case.seq_lens, Hkv=case.Hkv,
                          D=case.D, P=case.P)
     units = case.B * case.Hkv
-    threads = min(oracle.default_threads(), units)
+    cores = oracle.default_threads()
+    per_inst = min(cores, units)
+    inst = max(1, cores // per_inst)
     kw = dict(q=q, k_pool=k, v_pool=v, block_table=case.block_table, seq_lens=case.seq_lens, Hq=case.Hq,
-              Hkv=case.Hkv, top_k=case.top_k, scale=case.scale, P=case.P, summaries_in=S, nthreads=threads)
-    one = float("inf")
-    for _ in range(2):   # calibrate on a warm call (the first one pays for cold caches)
+              Hkv=case.Hkv, top_k=case.top_k, scale=case.scale, P=case.P, summaries_in=S, nthreads=per_inst)
+
+    def run(n):
+        """wall seconds for inst concurrent instances of n oracle steps each"""
+        def worker():
+            for _ in range(n):
+                oracle.decode(**kw)
+        ts = [threading.Thread(target=worker) for _ in range(inst)]
         t0 = time.perf_counter()
-        oracle.decode(**kw)
-        one = min(one, time.perf_counter() - t0)
-    n = int(max(2, min(5000, args.cpu_seconds / max(one, 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(n):
-        oracle.decode(**kw)
-    dt = time.perf_counter() - t0
-    log("cpu oracle: %d steps in %.1f s on %d threads" % (n, dt, threads))
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        return time.perf_counter() - t0
+    one = min(run(1) for _ in range(2))   # calibration on warm calls (the first pays for cold caches)
+    n = int(max(2, min(5000, args.cpu_seconds / 3.0 / max(one, 1e-3))))
+    rates = sorted(inst * n * case.B / run(n) for _ in range(3))
+    log("cpu oracle: %d instances x %d threads, %d steps each per run, rates %s tokens/s"
+        % (inst, per_inst, n, ", ".join("%.1f" % r for r in rates)))
     # the same oracle on one thread, over a sample of about a fifth of the time
     kw1 = dict(kw, nthreads=1)
     t0 = time.perf_counter()
@@ -750,11 +842,12 @@ def cpu_baseline(args, case, torch, np):
         oracle.decode(**kw1)
     dt1 = time.perf_counter() - t0
     log("cpu oracle, one thread: %d steps in %.1f s" % (n1, dt1))
-    return {"value": n * case.B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "host_cores": os.cpu_count(), "single_thread_value": n1 * case.B / dt1,
-            "sample": "%d decode steps (select from cached fp64 summaries + attend) of the same 1M-token "
-                      "workload, fp64 C oracle, threads over (sequence, KV group) units; %d more steps on one "
-                      "thread for single_thread_value" % (n, n1)}
+    return {"value": rates[1], "unit": "tokens/s", "cores": inst * per_inst, "kind": "oracle",
+            "host_cores": cores, "runs": rates, "single_thread_value": n1 * case.B / dt1,
+            "sample": "median of 3 runs; each run: %d concurrent instances x %d decode steps (select from cached "
+                      "fp64 summaries + attend) of the same 1M-token workload, fp64 C oracle threaded over the %d "
+                      "(sequence, KV group) units, %d threads per instance; %d more steps on one thread for "
+                      "single_thread_value" % (inst, n, units, per_inst, n1)}
 
 
 if __name__ == "__main__":

@@ -210,6 +210,20 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
                              float* lse_out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Step 2 of a prefill chunk alone ([MGS §1 Step 2]; [MGS §3] prefill: the savings fall on this
+ * main attention): causal attention of the chunk's T queries (positions past_len ..
+ * past_len+T-1 of one sequence) over given per-tile lists, with the chunk's own K/V already in
+ * the cache (e.g. written by msa_prefill_chunk). For tile tau and group g, with diagonal block
+ * d = past_len/64 + tau: block d is always attended, causally (key position <= query position);
+ * list entries j with 0 <= j < d and a page id in [0, num_pages) are attended in full; every
+ * other entry (-1, d itself, blocks after d) is skipped. Entries must not repeat.
+ *   q        [T][Hq][128] bf16;  out [T][Hq][128] bf16;  lse_out nullable [T][Hq] float32
+ *   idx      [ceil(T/64)][Hkv][top_k+1] int32 (the layout msa_prefill_chunk writes)
+ * Only block_table[0], num_pages and the K/V pools of the cache are read. No workspace. */
+msa_status msa_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache,
+                              int32_t past_len, int32_t T, const int32_t* idx, void* out,
+                              float* lse_out, void* stream);
+
 /* Static text for a status code. */
 const char* msa_status_string(msa_status status);
 

@@ -7,6 +7,7 @@
 //                     -> attend -> split-K merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend
+//   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
 // HIP call, so an invalid call enqueues nothing.
 #include <cmath>
@@ -187,6 +188,27 @@ msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   return hip_status(launch_attend_decode(cfg->q_dtype == MSA_BF16, a, st));
 }
 
+// Step 2 of a prefill chunk on validated arguments
+msa_status run_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int past_len, int T,
+                              const int32_t* idx, void* out, float* lse, hipStream_t st) {
+  PrefillArgs p{};
+  p.q = q;
+  p.kpool = cache->k_pages;
+  p.vpool = cache->v_pages;
+  p.table = cache->block_table;
+  p.idx = idx;
+  p.num_pages = cache->num_pages;
+  p.past_len = past_len;
+  p.T = T;
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.k = cfg->top_k;
+  p.scale_log2 = cfg->softmax_scale * kLog2e;
+  p.out = out;
+  p.lse = lse;
+  return hip_status(launch_attend_prefill(p, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -349,22 +371,21 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   t.keep_sink = cfg->keep_sink;
   t.keep_local = cfg->keep_local;
   MSA_TRY(hip_status(launch_topk(t, st)));
-  PrefillArgs p{};
-  p.q = q;
-  p.kpool = cache->k_pages;
-  p.vpool = cache->v_pages;
-  p.table = cache->block_table;
-  p.idx = idx;
-  p.num_pages = cache->num_pages;
-  p.past_len = past_len;
-  p.T = T;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.k = cfg->top_k;
-  p.scale_log2 = cfg->softmax_scale * kLog2e;
-  p.out = out;
-  p.lse = lse_out;
-  return hip_status(launch_attend_prefill(p, st));
+  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, st);
+}
+
+msa_status msa_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t past_len,
+                              int32_t T, const int32_t* idx, void* out, float* lse_out, void* stream) {
+  MSA_TRY(check_config(cfg));
+  if (cache == nullptr || cache->block_table == nullptr || cache->k_pages == nullptr || cache->v_pages == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  if (cache->num_pages < 0 || cache->max_blocks < 1) return MSA_ERR_INVALID_ARG;
+  if (q == nullptr || idx == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (T < 1 || past_len < 0) return MSA_ERR_INVALID_ARG;
+  if ((long long)past_len + T > (long long)cache->max_blocks * MSA_BLOCK) return MSA_ERR_INVALID_ARG;
+  if (past_len % MSA_BLOCK != 0) return MSA_ERR_UNSUPPORTED;
+  if (cfg->q_dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, (hipStream_t)stream);
 }
 
 const char* msa_status_string(msa_status status) {

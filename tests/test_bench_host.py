@@ -52,3 +52,54 @@ def test_sources_digest_is_stable_and_content_based(tmp_path):
     assert bench.sources_digest([str(a)]) == bench.sources_digest([str(b)])
     b.write_text("y")
     assert bench.sources_digest([str(a)]) != bench.sources_digest([str(b)])
+
+
+class _FakeCuda:
+    """The parts of torch.cuda that bench.time_exact_steps touches, recording what runs when."""
+    def __init__(self, log):
+        self.log = log
+
+    def synchronize(self):
+        self.log.append("sync")
+
+    class Event:
+        def __init__(self, enable_timing=False):
+            self.t = 0.0
+
+        def record(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.0
+
+
+@pytest.mark.parametrize("steps,warmup", [(20, 5), (400, 40), (450, 0), (1, 1), (199, 3), (201, 7)])
+def test_exact_steps_and_warmup(monkeypatch, steps, warmup):
+    """bench.time_exact_steps runs exactly `warmup` untimed calls, then replays graphs holding
+    exactly `steps` calls in total (a full graph of up to 200, and a graph of the remainder)."""
+    log = []
+    calls = []
+
+    class FakeTorch:
+        cuda = _FakeCuda(log)
+
+    class FakeGraph:
+        def __init__(self, fn, n):
+            self.fn, self.n = fn, n
+
+        def replay(self):
+            log.append("replay%d" % self.n)
+            for i in range(self.n):
+                calls.append(("timed", i))
+
+    monkeypatch.setattr(bench, "timed_graph", lambda fn, n, torch, eager_first=True: FakeGraph(fn, n))
+
+    def fn(i):
+        calls.append(("eager", i))
+    t = bench.time_exact_steps(fn, steps, warmup, FakeTorch)
+    eager = [c for c in calls if c[0] == "eager"]
+    timed = [c for c in calls if c[0] == "timed"]
+    assert eager == [("eager", i) for i in range(warmup)]
+    assert len(timed) == steps
+    assert max(int(e[len("replay"):]) for e in log if e.startswith("replay")) <= bench.GRAPH_MAX_STEPS
+    assert t == pytest.approx(1e-3 / steps)

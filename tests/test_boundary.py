@@ -187,6 +187,28 @@ def test_prefill_errors():
     assert call(cfg(), nbytes=100) == L.MSA_ERR_WORKSPACE
 
 
+def test_prefill_attend_errors():
+    """msa_prefill_attend reads only the table, page count and K/V pools of the cache (no
+    summaries, no lengths, no workspace)."""
+    lib = L.load_library()
+    bare = fake_cache(max_blocks=80, num_pages=80, summaries=None, seq_lens=None)
+
+    def call(c=None, past=1024, T=256, q=FAKE, idx=FAKE, out=FAKE, cache=bare):
+        c = cfg() if c is None else c
+        return lib.msa_prefill_attend(ctypes.byref(c), q, ctypes.byref(cache), past, T, idx, out, None, None)
+    assert call(past=1000) == L.MSA_ERR_UNSUPPORTED       # past_len % 64 != 0
+    assert call(T=0) == L.MSA_ERR_INVALID_ARG
+    assert call(past=-64) == L.MSA_ERR_INVALID_ARG
+    assert call(past=80 * 64, T=1) == L.MSA_ERR_INVALID_ARG
+    assert call(q=None) == L.MSA_ERR_INVALID_ARG
+    assert call(idx=None) == L.MSA_ERR_INVALID_ARG
+    assert call(out=None) == L.MSA_ERR_INVALID_ARG
+    assert call(cache=fake_cache(max_blocks=80, num_pages=80, k_pages=None)) == L.MSA_ERR_INVALID_ARG
+    assert call(cache=fake_cache(max_blocks=80, num_pages=80, block_table=None)) == L.MSA_ERR_INVALID_ARG
+    assert call(c=cfg(dtype="f32")) == L.MSA_ERR_UNSUPPORTED
+    assert call(c=cfg(head_dim=64)) == L.MSA_ERR_UNSUPPORTED
+
+
 def test_select_index_errors():
     """The index branch reads only the table, lengths and page count of the cache; index_dim
     other than 64 or 128 is unsupported; score_mode is not read."""

@@ -286,14 +286,24 @@ def test_large_k_all_scores_tied(k):
             assert np.all(got[b, g, len(want):] == -1)
 
 
-def test_full_size_mixed_batch_sampled():
+@pytest.fixture(scope="module")
+def mixed_run():
+    """The batch-32 mixed-length workload, one decode step on the GPU."""
+    require_gpu()
     kw = workload("decode_bf16_mixed_b32", seed=0)
     c = make_decode_case_torch(**kw)
     d = to_device(c)
-    res = run_decode(d)
+    return c, d, run_decode(d)
+
+
+# ranks in ascending length order: the shortest, the longest and six between
+@pytest.mark.parametrize("ranks", [(0, 4, 9, 13), (18, 22, 27, 31)])
+def test_full_size_mixed_batch(mixed_run, ranks):
+    c, d, res = mixed_run
     lens = c.seq_lens
-    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), int(np.argsort(lens)[len(lens) // 2])})
-    for b in picks:
+    order = np.argsort(lens, kind="stable")
+    for b in (int(order[r]) for r in ranks):
+        print("mixed batch: sequence %d, %d tokens" % (b, int(lens[b])), flush=True)
         nb = (int(lens[b]) + 63) // 64
         pages = torch.from_numpy(c.block_table[b, :nb].astype(np.int64)).cuda()
         sub_k = host_store(d.k.index_select(0, pages))

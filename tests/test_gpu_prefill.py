@@ -162,17 +162,51 @@ def test_prefill_deterministic():
     np.testing.assert_array_equal(r1["idx"], r2["idx"])
 
 
-def test_prefill_full_size_sampled_tiles():
+@pytest.fixture(scope="module")
+def full_prefill():
+    """The 4096-token chunk on a 262,144-token cache, run once on the GPU; the host copies of the
+    pools from before the append feed the oracle."""
+    require_gpu()
     kw = workload("prefill_bf16_4k_on_256k", seed=0)
     p = make_prefill_case_torch(**kw)
     d = to_dev(p)
     k_before, v_before = host_store(d["k"]), host_store(d["v"])
     res = run_prefill(p, d)
-    for tiles in [(0, 1), (31, 32), (63, 64)]:
-        check_prefill(p, d, res, k_before, v_before, tiles=tiles)
-    # planted blocks are found (input-recipe sanity, not parity)
+    return p, d, res, k_before, v_before
+
+
+@pytest.mark.parametrize("tiles", [(0, 16), (16, 32), (32, 48), (48, 64)])
+def test_prefill_full_size(full_prefill, tiles):
+    """Every one of the 64 tiles of the full chunk, in four ranges (one oracle call each)."""
+    p, d, res, k_before, v_before = full_prefill
+    print("prefill 4096 on 262144: tiles %d..%d" % tiles, flush=True)
+    check_prefill(p, d, res, k_before, v_before, tiles=tiles)
+
+
+def test_prefill_full_size_planted(full_prefill):
+    """Planted blocks are found (input-recipe sanity, not parity)."""
+    p, d, res, _, _ = full_prefill
     hit = sum(int(j in res["idx"][tau, g]) for (tau, g), j in p.planted.items())
     assert hit / len(p.planted) > 0.8
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_prefill_attend_with_oracle_lists(name, kw):
+    """Step 2 alone (msa_prefill_attend) over the oracle's own lists, after the chunk's append."""
+    p = make_prefill_case(seed=45, dtype="bf16", permute=True, **kw)
+    d = to_dev(p)
+    k_before, v_before = host_store(d["k"]), host_store(d["v"])
+    run_prefill(p, d)                                     # appends the chunk's K/V
+    ref = oracle.prefill(q=host_store(d["q"]), k_new=host_store(d["kn"]), v_new=host_store(d["vn"]),
+                         k_pool=k_before, v_pool=v_before, block_table=p.block_table, past_len=p.past_len,
+                         Hq=p.Hq, Hkv=p.Hkv, top_k=p.top_k, scale=p.scale, P=p.P)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((p.T, p.Hq), dtype=torch.float32, device="cuda")
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    msa.msa_prefill_attend(d["cfg"], d["q"], d["cache"], p.past_len, p.T, idx, out, lse_out=lse)
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), ref["o"], "bf16", "prefill attend o")
+    assert_close(lse.cpu().numpy(), ref["lse"], "bf16", "prefill attend lse", lse=True)
 
 
 def test_prefill_graph_replays_match_eager():
