@@ -34,7 +34,8 @@
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; nothing is allocated or
- *     freed by the library and no state is kept between calls (reentrant).
+ *     freed by the library and no state is kept between calls (reentrant). The one exception is
+ *     msa_decode_step_noalloc, whose workspace is a per-GPU array inside the library (see there).
  *   - `stream` is a hipStream_t passed as void* (0 = the null stream). All work is enqueued
  *     asynchronously on it; no call synchronises the host or copies device data to the host.
  *   - batch <= MSA_MAX_BATCH (a larger batch returns MSA_ERR_UNSUPPORTED).
@@ -93,6 +94,7 @@ typedef enum msa_op {
 #define MSA_MAX_GROUP 8        /* Hq / Hkv */
 #define MSA_MAX_KV_HEADS 64
 #define MSA_MAX_BATCH 65535    /* sequences per decode / select / attend call */
+#define MSA_NOALLOC_SCRATCH_BYTES (32u << 20)   /* workspace of msa_decode_step_noalloc, per GPU */
 
 typedef struct msa_config {
     int32_t num_q_heads;      /* Hq */
@@ -192,6 +194,24 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
                            const void* v_new, int32_t* idx_out, float* scores_out, void* out,
                            float* lse_out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* msa_decode_step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, kernels, results and
+ * errors as msa_decode_step, without the workspace arguments: the workspace is a file-scope
+ * device array of MSA_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one per GPU, held until
+ * the process ends. A call whose msa_workspace_size(cfg, MSA_OP_DECODE, batch, max_seq_len, 0)
+ * exceeds that size returns MSA_ERR_WORKSPACE and enqueues nothing (e.g. batch 32 at 1M tokens
+ * and 8 KV heads needs about 17 MiB; batch 1 fits up to 16M tokens). The call allocates nothing;
+ * its first call on a device looks up that device's copy of the array (no allocation, no
+ * enqueued work), so make one call on each device before capturing it in a graph if the capture
+ * mode forbids such lookups. All calls on one GPU share the array: calls that overlap in time on
+ * one GPU (different streams, or concurrent host threads without ordering) race and must not be
+ * made. Nothing in the array needs to start at zero: every byte a step reads is written earlier
+ * in the same step. */
+msa_status msa_decode_step_noalloc(const msa_config* cfg, const void* q, const msa_kv_cache* cache,
+                                   int32_t batch, int32_t max_seq_len, const void* k_new,
+                                   const void* v_new, int32_t* idx_out, float* scores_out,
+                                   void* out, float* lse_out, void* stream);
 
 /* One prefill chunk of one sequence ([MGS §1 Steps 1-2]; [MGS §3] prefill): append T new
  * tokens (k_new/v_new [T][Hkv][128]) at positions past_len .. past_len+T-1 (pages already in

@@ -6,7 +6,7 @@ There is no CPU fallback; calling any entry point without the built library rais
 
 Entry points (same names as the C ABI):
   msa_workspace_size, msa_build_summaries, msa_score, msa_select, msa_select_index, msa_attend,
-  msa_decode_step, msa_prefill_chunk, msa_prefill_attend, msa_status_string
+  msa_decode_step, msa_decode_step_noalloc, msa_prefill_chunk, msa_prefill_attend, msa_status_string
 Measurement probes of the GPU itself (include/msa_probe.h): msa_probe_hbm_read, msa_probe_mfma_bf16
 """
 from __future__ import annotations
@@ -14,14 +14,14 @@ from __future__ import annotations
 from ._lib import (  # noqa: F401
     MSA_BF16, MSA_F32, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL, MSA_OP_SELECT, KVCache,
     MsaError, library_path, load_library, make_config, msa_attend, msa_build_summaries,
-    msa_decode_step, msa_prefill_attend, msa_prefill_chunk, msa_score, msa_select, msa_select_index, msa_status_string,
-    msa_workspace_size, msa_probe_hbm_read, msa_probe_mfma_bf16, PROBE_READ_SINK_FLOATS,
+    msa_decode_step, msa_decode_step_noalloc, msa_prefill_attend, msa_prefill_chunk, msa_score, msa_select, msa_select_index, msa_status_string,
+    msa_workspace_size, msa_probe_hbm_read, msa_probe_mfma_bf16, PROBE_READ_SINK_FLOATS, NOALLOC_SCRATCH_BYTES,
 )
 
 __all__ = [
     "MSA_BF16", "MSA_F32", "MSA_OP_ATTEND", "MSA_OP_DECODE", "MSA_OP_PREFILL", "MSA_OP_SELECT",
     "KVCache", "MsaError", "library_path", "load_library", "make_config", "msa_attend",
-    "msa_build_summaries", "msa_decode_step", "msa_prefill_attend", "msa_prefill_chunk", "msa_score", "msa_select",
+    "msa_build_summaries", "msa_decode_step", "msa_decode_step_noalloc", "msa_prefill_attend", "msa_prefill_chunk", "msa_score", "msa_select",
     "msa_select_index", "msa_status_string", "msa_workspace_size",
-    "msa_probe_hbm_read", "msa_probe_mfma_bf16", "PROBE_READ_SINK_FLOATS",
+    "msa_probe_hbm_read", "msa_probe_mfma_bf16", "PROBE_READ_SINK_FLOATS", "NOALLOC_SCRATCH_BYTES",
 ]

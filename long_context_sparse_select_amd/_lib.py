@@ -16,7 +16,8 @@ MSA_SCORE_MEAN_KEY, MSA_SCORE_MAX_TOKEN = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTEND, MSA_OP_DECODE, MSA_OP_PREFILL = range(4)
 
 EXPORTED = ("msa_workspace_size", "msa_build_summaries", "msa_score", "msa_select", "msa_select_index",
-            "msa_attend", "msa_decode_step", "msa_prefill_chunk", "msa_prefill_attend", "msa_status_string")
+            "msa_attend", "msa_decode_step", "msa_decode_step_noalloc", "msa_prefill_chunk", "msa_prefill_attend",
+            "msa_status_string")
 # measurement probes of the GPU itself (include/msa_probe.h)
 EXPORTED_PROBES = ("msa_probe_hbm_read", "msa_probe_mfma_bf16")
 
@@ -70,6 +71,7 @@ def load_library():
         lib.msa_decode_step.argtypes = [C, V, K, I, I, V, V, V, V, V, V, V, Z, V]
         lib.msa_prefill_chunk.argtypes = [C, V, V, V, K, I, I, V, V, V, V, V, Z, V]
         lib.msa_prefill_attend.argtypes = [C, V, K, I, I, V, V, V, V]
+        lib.msa_decode_step_noalloc.argtypes = [C, V, K, I, I, V, V, V, V, V, V, V]
         for name in EXPORTED[:-1]:
             getattr(lib, name).restype = ctypes.c_int
         lib.msa_status_string.argtypes = [ctypes.c_int]
@@ -195,6 +197,19 @@ def msa_decode_step(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: 
                                           _p(k_new), _p(v_new), _p(idx_out), _p(scores_out), _p(out),
                                           _p(lse_out), _p(ws), nbytes, _stream(stream, q)),
            "msa_decode_step")
+
+
+def msa_decode_step_noalloc(cfg: MsaConfig, q, cache: KVCache, batch: int, max_seq_len: int, out, k_new=None,
+                            v_new=None, idx_out=None, scores_out=None, lse_out=None, stream=None) -> None:
+    """msa_decode_step with the library's own per-GPU scratch array as the workspace (no allocation)."""
+    c = cache.struct()
+    _check(load_library().msa_decode_step_noalloc(ctypes.byref(cfg), _p(q), ctypes.byref(c), batch, max_seq_len,
+                                                  _p(k_new), _p(v_new), _p(idx_out), _p(scores_out), _p(out),
+                                                  _p(lse_out), _stream(stream, q)),
+           "msa_decode_step_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def msa_prefill_chunk(cfg: MsaConfig, q, k_new, v_new, cache: KVCache, past_len: int, T: int, out,

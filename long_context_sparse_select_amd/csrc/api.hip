@@ -8,11 +8,13 @@
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend
 //   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
+//   msa_decode_step_noalloc  msa_decode_step's launches with a file-scope device array as the workspace
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
 // HIP call, so an invalid call enqueues nothing.
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -188,6 +190,55 @@ msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   return hip_status(launch_attend_decode(cfg->q_dtype == MSA_BF16, a, st));
 }
 
+// Argument checks of a decode step (both entry points) and its workspace layout
+msa_status check_decode_step(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                             const void* k_new, const void* v_new, const void* out, Layout* L) {
+  MSA_TRY(check_config(cfg));
+  MSA_TRY(check_cache(cache, true, true));
+  MSA_TRY(check_batch(cache, B, max_len));
+  if (q == nullptr || out == nullptr || ((k_new == nullptr) != (v_new == nullptr))) return MSA_ERR_INVALID_ARG;
+  *L = decode_layout(cfg, MSA_OP_DECODE, B, max_len);
+  if (L->nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+// A decode step on validated arguments with a workspace of at least L.total bytes. Every
+// workspace byte the step reads is written earlier in the same step (scores, lists, page ids,
+// split partials), so the workspace needs no clearing.
+msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                           const void* k_new, const void* v_new, int32_t* idx_out, float* scores_out, void* out,
+                           float* lse_out, const Layout& L, void* ws, hipStream_t st) {
+  float* scores = scores_out ? scores_out : at<float>(ws, L.scores);
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
+  int32_t* pages = at<int32_t>(ws, L.pages);
+  MSA_TRY(run_select(cfg, q, cache, B, max_len, scores, L.row_stride, idx, pages, k_new, v_new, st));
+  return run_attend(cfg, q, cache, B, max_len, idx, pages, out, lse_out, L, ws, st);
+}
+
+// The no-allocation decode step's workspace: one file-scope device array. Every GPU the library
+// runs on holds its own copy (at its own address) until the process ends. In host code `scratch`
+// names a host-side stand-in, never device memory: its device address on the current device is
+// looked up once per device with hipGetSymbolAddress and only that address is handed to kernels.
+// Calls that overlap in time on one GPU share this array and race.
+__device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+msa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
 // Step 2 of a prefill chunk on validated arguments
 msa_status run_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int past_len, int T,
                               const int32_t* idx, void* out, float* lse, hipStream_t st) {
@@ -316,20 +367,25 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
                            int32_t max_seq_len, const void* k_new, const void* v_new, int32_t* idx_out,
                            float* scores_out, void* out, float* lse_out, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  MSA_TRY(check_config(cfg));
-  MSA_TRY(check_cache(cache, true, true));
-  MSA_TRY(check_batch(cache, batch, max_seq_len));
-  if (q == nullptr || out == nullptr || ((k_new == nullptr) != (v_new == nullptr))) return MSA_ERR_INVALID_ARG;
-  const Layout L = decode_layout(cfg, MSA_OP_DECODE, batch, max_seq_len);
-  if (L.nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;
+  Layout L;
+  MSA_TRY(check_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, out, &L));
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
-  const hipStream_t st = (hipStream_t)stream;
-  float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
-  int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
-  int32_t* pages = at<int32_t>(workspace, L.pages);
-  MSA_TRY(run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx, pages, k_new, v_new, st));
-  return run_attend(cfg, q, cache, batch, max_seq_len, idx, pages, out, lse_out, L, workspace, st);
+  return run_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, idx_out, scores_out, out, lse_out, L,
+                         workspace, (hipStream_t)stream);
+}
+
+msa_status msa_decode_step_noalloc(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t batch,
+                                   int32_t max_seq_len, const void* k_new, const void* v_new, int32_t* idx_out,
+                                   float* scores_out, void* out, float* lse_out, void* stream) {
+  Layout L;
+  MSA_TRY(check_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, out, &L));
+  if (L.total > (size_t)MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_WORKSPACE;
+  if (batch == 0) return MSA_OK;
+  void* ws = nullptr;
+  MSA_TRY(scratch_of_current_device(&ws));
+  return run_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, idx_out, scores_out, out, lse_out, L, ws,
+                         (hipStream_t)stream);
 }
 
 msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k_new, const void* v_new,

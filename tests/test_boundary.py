@@ -187,6 +187,34 @@ def test_prefill_errors():
     assert call(cfg(), nbytes=100) == L.MSA_ERR_WORKSPACE
 
 
+def test_decode_noalloc_errors():
+    """msa_decode_step_noalloc validates like msa_decode_step and rejects a decode whose workspace
+    would exceed its scratch array, before any HIP call (none of these calls touches a device)."""
+    lib = L.load_library()
+
+    def call(c=None, B=1, max_len=1024, cache=None, q=FAKE, out=FAKE, k_new=None, v_new=None):
+        c = cfg() if c is None else c
+        cache = fake_cache() if cache is None else cache
+        return lib.msa_decode_step_noalloc(ctypes.byref(c), q, ctypes.byref(cache), B, max_len, k_new, v_new, None,
+                                           None, out, None, None)
+    assert call(q=None) == L.MSA_ERR_INVALID_ARG
+    assert call(out=None) == L.MSA_ERR_INVALID_ARG
+    assert call(k_new=FAKE) == L.MSA_ERR_INVALID_ARG          # k_new without v_new
+    assert call(max_len=5000) == L.MSA_ERR_INVALID_ARG        # beyond the table
+    assert call(c=cfg(head_dim=64)) == L.MSA_ERR_UNSUPPORTED
+    assert call(B=0) == L.MSA_OK
+    # the limit: the same layout as msa_workspace_size reports for a decode step
+    big = fake_cache(max_blocks=1 << 16, num_pages=1 << 16)
+    for B, max_len in [(1, 1 << 20), (32, 1 << 20), (1, 1 << 22), (64, 1 << 20), (8, 1 << 22)]:
+        need = ws_size(cfg(), L.MSA_OP_DECODE, B, max_len)[1]
+        st = call(B=B, max_len=max_len, cache=big, q=None)       # q = None: stops before any launch
+        if need > L.NOALLOC_SCRATCH_BYTES:
+            assert call(B=B, max_len=max_len, cache=big) == L.MSA_ERR_WORKSPACE, (B, max_len)
+        assert st == L.MSA_ERR_INVALID_ARG
+    assert ws_size(cfg(), L.MSA_OP_DECODE, 32, 1 << 20)[1] <= L.NOALLOC_SCRATCH_BYTES
+    assert ws_size(cfg(), L.MSA_OP_DECODE, 64, 1 << 20)[1] > L.NOALLOC_SCRATCH_BYTES
+
+
 def test_prefill_attend_errors():
     """msa_prefill_attend reads only the table, page count and K/V pools of the cache (no
     summaries, no lengths, no workspace)."""
@@ -245,3 +273,10 @@ def test_summary_dtype_validation():
     c = cfg()
     c.summary_dtype = 7
     assert ws_size(c, L.MSA_OP_DECODE)[0] == L.MSA_ERR_INVALID_ARG
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MSA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m is not None
+    assert int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
