@@ -4,7 +4,8 @@
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
 //   msa_decode_step   [append: new K/V row, that block's summary and score | score] (one launch) -> top-k
-//                     -> attend -> split-K merge
+//                     -> attend -> split-K merge; for bf16, k <= 256 and no forced blocks:
+//                     [append | score + chunk maxima] -> select-and-attend -> split-K merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend
 //   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
@@ -29,10 +30,19 @@ using namespace msa;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t scores = 0, idx = 0, pages = 0, qtile = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t scores = 0, idx = 0, pages = 0, qtile = 0, part_o = 0, part_ml = 0, cmax = 0, total = 0;
   int row_stride = 0;   // scores per row
+  int cstride = 0;      // chunk maxima per row (fused decode step)
   int bps = 1, nsplit = 0;
+  bool fused = false;   // decode step: Step 1's TopK inside the attend launch
 };
+
+// A bf16 decode step without forced blocks, k <= kMaxFusedTopK and rows of at most
+// kMaxFusedChunks chunks selects inside its attend launch (launch_decode_select_attend).
+bool fused_decode(const msa_config* c, int row_stride) {
+  return c->q_dtype == MSA_BF16 && c->keep_sink == 0 && c->keep_local == 0 && c->top_k <= kMaxFusedTopK &&
+         row_stride <= kMaxFusedChunks * kScoreChunk;
+}
 
 // any_mode: the entry point does not read score_mode (msa_select_index)
 msa_status check_config(const msa_config* c, bool any_mode = false) {
@@ -74,6 +84,11 @@ Layout decode_layout(const msa_config* c, int op, int B, int max_len) {
   if (op == MSA_OP_DECODE) {
     L.idx = off;   off += align256(rows * (size_t)k * sizeof(int32_t));
     L.pages = off; off += align256(rows * (size_t)k * sizeof(int32_t));
+    L.fused = fused_decode(c, L.row_stride);
+    if (L.fused) {
+      L.cstride = (L.row_stride + kScoreChunk - 1) / kScoreChunk;
+      L.cmax = off; off += align256(rows * (size_t)(L.cstride > 0 ? L.cstride : 1) * sizeof(float));
+    }
   }
   if (att) {
     L.part_o = off;   off += align256((size_t)B * Hq * L.nsplit * kD * sizeof(float));
@@ -161,10 +176,19 @@ msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   return run_topk(cfg, cache, B, max_len, scores, row_stride, idx, pages, st);
 }
 
+AttendArgs attend_args(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                       const int32_t* idx, const int32_t* pages, void* out, float* lse, const Layout& L, void* ws);
+
 // Step 2 on validated arguments
 msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
                       const int32_t* idx, const int32_t* pages, void* out, float* lse, const Layout& L, void* ws,
                       hipStream_t st) {
+  const AttendArgs a = attend_args(cfg, q, cache, B, max_len, idx, pages, out, lse, L, ws);
+  return hip_status(launch_attend_decode(cfg->q_dtype == MSA_BF16, a, st));
+}
+
+AttendArgs attend_args(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
+                       const int32_t* idx, const int32_t* pages, void* out, float* lse, const Layout& L, void* ws) {
   AttendArgs a{};
   a.q = q;
   a.kpool = cache->k_pages;
@@ -187,7 +211,7 @@ msa_status run_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   a.part_ml = at<float>(ws, L.part_ml);
   a.out = out;
   a.lse = lse;
-  return hip_status(launch_attend_decode(cfg->q_dtype == MSA_BF16, a, st));
+  return a;
 }
 
 // Argument checks of a decode step (both entry points) and its workspace layout
@@ -209,6 +233,19 @@ msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
                            const void* k_new, const void* v_new, int32_t* idx_out, float* scores_out, void* out,
                            float* lse_out, const Layout& L, void* ws, hipStream_t st) {
   float* scores = scores_out ? scores_out : at<float>(ws, L.scores);
+  if (L.fused) {   // score (+ chunk maxima) -> select-and-attend -> merge
+    float* cmax = at<float>(ws, L.cmax);
+    MSA_TRY(hip_status(launch_score_decode(true, q, cache_args(cfg, cache), B, cfg->num_q_heads, cfg->num_kv_heads,
+                                           max_len, scores, L.row_stride, k_new, v_new, st, cmax, L.cstride)));
+    FusedArgs f{};
+    f.att = attend_args(cfg, q, cache, B, max_len, nullptr, nullptr, out, lse_out, L, ws);
+    f.scores = scores;
+    f.row_stride = L.row_stride;
+    f.cmax = cmax;
+    f.cstride = L.cstride;
+    f.idx_out = idx_out;
+    return hip_status(launch_decode_select_attend(f, st));
+  }
   int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
   int32_t* pages = at<int32_t>(ws, L.pages);
   MSA_TRY(run_select(cfg, q, cache, B, max_len, scores, L.row_stride, idx, pages, k_new, v_new, st));

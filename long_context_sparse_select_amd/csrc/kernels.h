@@ -30,9 +30,12 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
 // k_new / v_new (nullable, [B][Hkv][128]): the decode step's new token, already counted in seq_lens.
 // The same launch writes its K/V row at position seq_len-1, recomputes that block's summary from
 // its keys and scores the block from the stored summary.
+// cmax (nullable, [B][Hkv][cstride]): the largest score of each run of kScoreChunk blocks j < n_b,
+// the appended block's excepted (-inf for a run with none); cstride >= ceil(row_stride / kScoreChunk)
+constexpr int kScoreChunk = 16;
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
                                int max_len, float* scores, int row_stride, const void* k_new, const void* v_new,
-                               hipStream_t st);
+                               hipStream_t st, float* cmax = nullptr, int cstride = 0);
 // index branch (single-head index keys [num_pages][64][index_dim], q_index [B][Hkv][index_dim],
 // index_dim 64 or 128): block score = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
 hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, int index_dim,
@@ -89,6 +92,24 @@ struct AttendArgs {
 constexpr int kMaxDecodeSplit = 256;
 int decode_blocks_per_split(int B, int Hkv, int k);
 hipError_t launch_attend_decode(bool bf16, const AttendArgs& a, hipStream_t st);
+// the split-K merge alone (bf16 output), for a.nsplit > 1
+hipError_t launch_merge_bf16(const AttendArgs& a, hipStream_t st);
+
+// ---- Steps 1 (TopK) and 2 of a bf16 decode step in one launch (then the merge when split):
+// every attend workgroup selects its row's top-k from the scores and chunk maxima of the scoring
+// launch and attends its split of the list. For k <= kMaxFusedTopK, no forced blocks and rows of
+// at most kMaxFusedChunks * kScoreChunk blocks.
+constexpr int kMaxFusedTopK = 64;
+constexpr int kMaxFusedChunks = 1024;
+struct FusedArgs {
+  AttendArgs att;        // idx / pages unused
+  const float* scores;   // [B][Hkv][row_stride]
+  int row_stride;
+  const float* cmax;     // [B][Hkv][cstride]
+  int cstride;
+  int32_t* idx_out;      // nullable [B][Hkv][k]
+};
+hipError_t launch_decode_select_attend(const FusedArgs& f, hipStream_t st);
 
 // ---- Step 2, prefill (bf16, MFMA)
 struct PrefillArgs {

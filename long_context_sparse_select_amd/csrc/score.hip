@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
                                                       float* __restrict__ scores, int row_stride,
                                                       const TQ* __restrict__ k_new, const TQ* __restrict__ v_new,
                                                       TQ* __restrict__ kpool, TQ* __restrict__ vpool, void* S_app,
-                                                      int napp) {
+                                                      int napp, float* __restrict__ cmax, int cstride) {
   const int Hkv = HKV > 0 ? HKV : hkv_arg;
   extern __shared__ float s_qidx[];             // [Hkv][128] index queries, then [Hkv][kChunk] scores
   const int b = blockIdx.y;
@@ -147,7 +147,8 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
                           scores, row_stride, b, (int)blockIdx.x, s_qidx);
     return;
   }
-  const int j0 = ((int)blockIdx.x - napp) * kChunk;
+  const int chunk = (int)blockIdx.x - napp;
+  const int j0 = chunk * kChunk;
   const int tid = threadIdx.x;
   const int jend = min(j0 + kChunk, row_stride);
   constexpr int kLanes = SB ? 16 : 32;   // lanes per (block, group) pair, 16 B each
@@ -161,6 +162,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       const int g = e / kChunk, jl = e % kChunk;
       if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
     }
+    if (cmax != nullptr && tid < Hkv) cmax[((long long)b * Hkv + tid) * cstride + chunk] = -INFINITY;
     return;
   }
 
@@ -191,6 +193,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       const int g = e / kChunk, jl = e % kChunk;
       if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
     }
+    if (cmax != nullptr && tid < Hkv) cmax[((long long)b * Hkv + tid) * cstride + chunk] = -INFINITY;
     return;
   }
   summary_loads(0);
@@ -282,6 +285,17 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
     const int g = e / kChunk, jl = e % kChunk;
     if (j0 + jl < jend && j0 + jl != jskip) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = s_sc[e];
   }
+  // the chunk's maximum per group (for the fused select-and-attend), over the scores written here:
+  // the appended block's score is the append workgroup's and is not in it
+  if (cmax != nullptr && tid < Hkv) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int jl = 0; jl < kChunk; ++jl) {
+      const int j = j0 + jl;
+      if (j < jend && j < nb && j != jskip) m = fmaxf(m, s_sc[tid * kChunk + jl]);
+    }
+    cmax[((long long)b * Hkv + tid) * cstride + chunk] = m;
+  }
 }
 
 // prefill scores: a 64-tile x 64-block fp32 product per workgroup on fp32 MFMA
@@ -368,7 +382,8 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
 
 template <typename TQ, bool SB>
 void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
-                        int row_stride, const TQ* k_new, const TQ* v_new, hipStream_t st) {
+                        int row_stride, const TQ* k_new, const TQ* v_new, float* cmax, int cstride, hipStream_t st) {
+  static_assert(kChunk == kScoreChunk, "chunk maxima cover the scoring kernel's chunks");
   const int napp = k_new != nullptr ? Hkv : 0;
   const dim3 grid(napp + (row_stride + kChunk - 1) / kChunk, B);
   const int lds_floats = Hkv * (kD + kChunk) > 4 * kD + 2 ? Hkv * (kD + kChunk) : 4 * kD + 2;
@@ -379,7 +394,7 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
   case H:                                                                                                  \
     k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \
                                                       Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, \
-                                                      c.S, napp);                                          \
+                                                      c.S, napp, cmax, cstride);                           \
     break;
   switch (Hkv) {
     MSA_SCORE_CASE(1)
@@ -392,7 +407,7 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
     default:
       k_score_decode<TQ, 0, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq,
                                                         Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, c.S,
-                                                        napp);
+                                                        napp, cmax, cstride);
   }
 #undef MSA_SCORE_CASE
 }
@@ -400,10 +415,12 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
 }  // namespace
 
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
-                               float* scores, int row_stride, const void* k_new, const void* v_new, hipStream_t st) {
+                               float* scores, int row_stride, const void* k_new, const void* v_new, hipStream_t st,
+                               float* cmax, int cstride) {
   if (B == 0 || row_stride == 0) return hipSuccess;
-#define MSA_SCORE_TYPED(T, SB) \
-  launch_score_typed<T, SB>((const T*)q, c, B, Hq, Hkv, max_len, scores, row_stride, (const T*)k_new, (const T*)v_new, st)
+#define MSA_SCORE_TYPED(T, SB)                                                                                 \
+  launch_score_typed<T, SB>((const T*)q, c, B, Hq, Hkv, max_len, scores, row_stride, (const T*)k_new, (const T*)v_new, \
+                            cmax, cstride, st)
   if (bf16) {
     if (c.s_bf16) MSA_SCORE_TYPED(uint16_t, true); else MSA_SCORE_TYPED(uint16_t, false);
   } else {

@@ -25,6 +25,7 @@
 // only on the scores.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace msa {
 
@@ -39,64 +40,6 @@ constexpr int kMaxK = 4096;
 constexpr int kSmallK = 256;    // k_eff up to this uses the survivor path; larger k the exact select
 constexpr int kRowRank = 512;   // survivors ranked 16 lanes each up to this count
 constexpr int kLBins = 1024;    // bins per pass of the exact select
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-// wave-uniform max / min: DPP within each 16-lane row, then the four rows through readlane
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));
-  v = max(v, dpp_u32<0x4E>(v));
-  v = max(v, dpp_u32<0x141>(v));
-  v = max(v, dpp_u32<0x140>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp_u32<0xB1>(v));
-  v = min(v, dpp_u32<0x4E>(v));
-  v = min(v, dpp_u32<0x141>(v));
-  v = min(v, dpp_u32<0x140>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return min(min(a, b), min(c, d));
-}
-
-// block-wide integer sum (all threads get it); s_tmp holds NT/64 ints
-template <int NT>
-__device__ int block_sum(int v, int* s_tmp) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) s_tmp[wave] = v;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) total += s_tmp[w];
-  __syncthreads();
-  return total;
-}
-
-// exclusive count of `pred` over threads in index order; *total gets the block's count
-template <int NT>
-__device__ int block_excl_count(bool pred, int* s_tmp, int* total) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned long long m = __ballot(pred);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) s_tmp[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int c = s_tmp[w];
-    before += (w < wave) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + in_wave;
-}
 
 struct TopkShared {
   unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
@@ -206,12 +149,6 @@ __device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&po
     pos[i] = sh.pre[i * kW + wave] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm[i], 0u));
   return sh.cnt;
 }
-
-// The score an order key came from (keys of NaN payloads give NaN; the forced key is not a score).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-constexpr uint32_t kPosInfKey = 0xff800000u;   // order_key(+inf)
 
 // Bin of a key on a linear score scale from vlo (bins of 1/vscale): monotone in the key, with
 // every key above +inf's (NaN payloads, the forced key) in the top bin and NaN below -inf in bin 0.
