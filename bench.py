@@ -422,10 +422,22 @@ def counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
         msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
     for i in range(n):
         msa.msa_score(cfg, q_ring[i % R], caches[i % L], B, max_len, sc_buf)
+    # whole decode steps without a new token (k_score_decode, k_decode_select_attend, k_merge
+    # dispatches): the selected K/V of each step, counted from its lists
+    import numpy as np
+    Hq0, Hkv0 = int(cfg.num_q_heads), int(cfg.num_kv_heads)
+    dout = torch.empty((B, Hq0, 128), dtype=q_ring[0].dtype, device=dev)
+    dws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
+    didx = [torch.empty((B, Hkv0, int(cfg.top_k)), dtype=torch.int32, device=dev) for _ in range(L)]
+    for i in range(n):
+        msa.msa_decode_step(cfg, q_ring[i % R], caches[i % L], B, max_len, dout, idx_out=didx[i % L], workspace=dws)
+    torch.cuda.synchronize()
+    step_kv_bytes = float(np.mean([selected_kv_bytes(didx[l], caches[l].seq_lens.cpu().numpy(),
+                                                     elem=2 if int(cfg.q_dtype) == msa.MSA_BF16 else 4)
+                                   for l in range(min(L, n))]))
     # the k = 1024 operating point: one selection per cache, then eager attends over those lists
     # (k_attend_decode_mfma + k_merge dispatches; the selections add k_score_decode dispatches
     # of the same work)
-    import numpy as np
     bf16 = int(cfg.q_dtype) == msa.MSA_BF16
     cfg_k = msa.make_config(int(cfg.num_q_heads), int(cfg.num_kv_heads), 1024, dtype="bf16" if bf16 else "f32",
                             softmax_scale=float(cfg.softmax_scale))
@@ -459,7 +471,9 @@ def counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L + L, "attend_launches": n,
+    print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L + L + n,
+                      "decode_step_launches": n, "decode_step_selected_kv_bytes": step_kv_bytes,
+                      "attend_launches": n,
                       "attend_bytes_per_launch": attend_bytes, "index_launches": n,
                       "index_score_bytes_per_launch": index_bytes, "copy_launches": 4,
                       "copy_bytes": COPY_BYTES}), flush=True)

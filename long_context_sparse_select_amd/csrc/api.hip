@@ -84,7 +84,10 @@ Layout decode_layout(const msa_config* c, int op, int B, int max_len) {
   if (op == MSA_OP_DECODE) {
     L.idx = off;   off += align256(rows * (size_t)k * sizeof(int32_t));
     L.pages = off; off += align256(rows * (size_t)k * sizeof(int32_t));
-    L.fused = fused_decode(c, L.row_stride);
+    // rows attended by one workgroup each (no split) keep the separate top-k launch: there the
+    // fused selection sits in front of a long attend with nothing to overlap it (batch 32 over
+    // mixed lengths up to 1M: a whole step of 181 us fused against 172 us unfused)
+    L.fused = fused_decode(c, L.row_stride) && L.nsplit > 1;
     if (L.fused) {
       L.cstride = (L.row_stride + kScoreChunk - 1) / kScoreChunk;
       L.cmax = off; off += align256(rows * (size_t)(L.cstride > 0 ? L.cstride : 1) * sizeof(float));

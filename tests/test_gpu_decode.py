@@ -409,3 +409,48 @@ def test_full_size_decode_1m_with_append():
     t = int(c.seq_lens[0]) - 1
     page = int(c.block_table[0, t // 64])
     assert torch.equal(d.k[page, :, t % 64], kn[0]) and torch.equal(d.v[page, :, t % 64], vn[0])
+
+
+@pytest.mark.parametrize("entry", ["decode_step", "attend"])
+def test_bf16_p_rounding_bound(entry):
+    """The bf16 attend kernels weight V by P rounded to bf16 (relative error <= 2^-8, round to
+    nearest) while the softmax denominator sums the fp32 P; with the bf16 rounding of the output the
+    error is bounded per element by 2^-8 (sum_t w_t |v_t| + |o|) + 1e-6 (w: the oracle's exact
+    weights). Near-flat logits (a small query) spread the weight over every token, and V is distinct
+    per token with a large common offset, which is where a mismatch of numerator and denominator
+    weights shows most. k covers every block, so the oracle's weight list is in token order."""
+    c = make_decode_case(B=2, Hq=8, Hkv=2, lens=[700, 2000], top_k=40, dtype="bf16", seed=61)
+    r = np.random.default_rng(61)
+    c.q = (0.05 * r.standard_normal(c.q.shape)).astype(np.float32)
+    nb_pages = c.v_pool.shape[0]
+    t_index = np.arange(64, dtype=np.float32)[None, None, :, None]
+    c.v_pool = (3.0 + 0.01 * (t_index + 64 * np.arange(nb_pages, dtype=np.float32)[:, None, None, None] % 97)
+                + 0.1 * r.standard_normal(c.v_pool.shape)).astype(np.float32)
+    d = to_device(c)
+    if entry == "decode_step":
+        res = run_decode(d)
+        out, lse = res["o"], res["lse"]
+    else:
+        idx = torch.from_numpy(np.tile(np.arange(40, dtype=np.int32), (c.B, c.Hkv, 1))).cuda()
+        out = torch.empty_like(d.q)
+        lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
+        msa.msa_attend(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, out, lse_out=lse)
+        torch.cuda.synchronize()
+    inputs = oracle_inputs(d)
+    ref = oracle.decode(want_weights=True, **inputs)
+    v64 = host_f64(d.v)
+    G = c.Hq // c.Hkv
+    got = host_f64(out)
+    for b in range(c.B):
+        N = int(c.seq_lens[b])
+        assert list(ref["idx"][b, 0][:(N + 63) // 64]) == list(range((N + 63) // 64))
+        t = np.arange(N)
+        for h in range(c.Hq):
+            g = h // G
+            vt = v64[c.block_table[b, t // 64], g, t % 64, :]        # [N][D] in token order
+            w = ref["w"][b, h, :N]
+            assert abs(w.sum() - 1.0) < 1e-12
+            bound = 2.0 ** -8 * (w @ np.abs(vt) + np.abs(ref["o"][b, h])) + 1e-6
+            err = np.abs(got[b, h] - ref["o"][b, h])
+            assert np.all(err <= bound), (entry, b, h, float((err / bound).max()))
+    assert_close(lse.cpu().numpy(), ref["lse"], "bf16", "lse", lse=True)
