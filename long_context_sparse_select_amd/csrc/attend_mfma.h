@@ -90,16 +90,16 @@ struct MfmaAttend {
   float acc[G][8];                   // PV layout: head h, dims d0 .. d0+7
   float m_h[G];                      // wave-uniform running max per head
 
-  // Issues the block's eight 16-byte loads; the scheduling barrier keeps them ahead of the
-  // arithmetic that follows in program order.
+  // Issues the block's eight 16-byte loads, non-temporal (a selected block is read once per
+  // launch); the scheduling barrier keeps them ahead of the arithmetic that follows in program order.
   __device__ __forceinline__ void load(KVRegs& r, int page) const {
     const long long base = (long long)page * page_stride + head_off;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)   // A operand: key 16w + hq, dims 32kk + 8c
-      r.k[kk] = *reinterpret_cast<const uint4*>(kpool + base + (16 * wave + hq) * kD + 32 * kk + 8 * c);
+      r.k[kk] = load_nt(kpool + base + (16 * wave + hq) * kD + 32 * kk + 8 * c);
 #pragma unroll
     for (int i = 0; i < 4; ++i)      // PV layout: token 16w + 4i + row, dims d0
-      r.v[i] = *reinterpret_cast<const uint4*>(vpool + base + (16 * wave + 4 * i + row) * kD + d0);
+      r.v[i] = load_nt(vpool + base + (16 * wave + 4 * i + row) * kD + d0);
     __builtin_amdgcn_sched_barrier(0);
   }
 

@@ -110,6 +110,14 @@ __device__ __forceinline__ float across_rows_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load marked non-temporal (the "nt" bit): for data read once per launch (block
+// summaries, the selected K/V, index keys), so the stream does not displace reused lines.
+typedef unsigned int u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 2^(a-b) for a <= b, with a = -inf giving 0 and a = b = -inf giving 0 (no NaN).
 __device__ __forceinline__ float rescale(float a, float b) {
   return (a == -INFINITY) ? 0.0f : fast_exp2(a - b);

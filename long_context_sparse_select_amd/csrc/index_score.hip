@@ -37,7 +37,7 @@ struct TokenPair {
     for (int k = 0; k < 2; ++k) {
       const uint4* row = reinterpret_cast<const uint4*>(block + (long long)(t + 32 * k) * DI);
 #pragma unroll
-      for (int i = 0; i < kC; ++i) w[k][i] = row[c + 8 * i];
+      for (int i = 0; i < kC; ++i) w[k][i] = load_nt(row + c + 8 * i);
     }
   }
   // token k's partial dot product with an index query held in LDS in storage form

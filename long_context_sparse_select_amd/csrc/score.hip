@@ -11,7 +11,7 @@
 // walks (block, group) pairs with 16 B per lane -- 32 lanes per fp32 pair, in passes of 8 blocks,
 // or 16 lanes per bf16 pair, in one pass of 16 -- so for Hkv = 8 it reads the chunk's 16 pages
 // as 16 contiguous 4 KiB (2 KiB) runs, whatever the page permutation. Each lane reads its pairs' page ids from the table and issues all of its
-// summary loads of a pass first; the Hkv index queries are built in LDS while the first pass
+// summary loads of a pass first, non-temporal (the pool is streamed once per launch); the Hkv index queries are built in LDS while the first pass
 // is in flight. The chunk's scores are staged in LDS and leave as one contiguous run per row.
 // The number of KV heads is a template parameter for the power-of-two cases, so the pair-index
 // arithmetic is shifts, not divisions.
@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       live[u] = (p < npairs) & (tp[u] >= 0) & (tp[u] < num_pages);   // the length is applied later
       const int page = live[u] ? tp[u] : 0;   // page 0: a valid address, result unused
       const long long row = (long long)page * Hkv + p % Hkv;   // 16 B per lane, either pool type
-      sv[u] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(S) + row * kD * (SB ? 2 : 4))[lp];
+      sv[u] = load_nt(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(S) + row * kD * (SB ? 2 : 4)) + lp);
     }
   };
   table_loads(0);
