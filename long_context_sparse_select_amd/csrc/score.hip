@@ -280,21 +280,21 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   __syncthreads();
   // each row's chunk of scores leaves as one contiguous run; with a new token, its block's score
   // is the append workgroup's
+  // The chunk's maximum per group (for the fused select-and-attend) is taken over the scores
+  // written here, in the same pass: the 16 scores of a group are one 16-lane row (kChunk = 16
+  // and every pass covers whole rows), so a row reduction gives it. The appended block's score is
+  // the append workgroup's and is not in it.
+  static_assert(kChunk == 16 && 256 % kChunk == 0, "one group's chunk of scores per 16-lane row");
   const int jskip = napp > 0 ? nb - 1 : -1;
   for (int e = tid; e < Hkv * kChunk; e += 256) {
     const int g = e / kChunk, jl = e % kChunk;
-    if (j0 + jl < jend && j0 + jl != jskip) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = s_sc[e];
-  }
-  // the chunk's maximum per group (for the fused select-and-attend), over the scores written here:
-  // the appended block's score is the append workgroup's and is not in it
-  if (cmax != nullptr && tid < Hkv) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int jl = 0; jl < kChunk; ++jl) {
-      const int j = j0 + jl;
-      if (j < jend && j < nb && j != jskip) m = fmaxf(m, s_sc[tid * kChunk + jl]);
+    const int j = j0 + jl;
+    const float v = s_sc[e];
+    if (j < jend && j != jskip) scores[((long long)b * Hkv + g) * row_stride + j] = v;
+    if (cmax != nullptr) {   // uniform
+      const float mrow = row16_max(j < jend && j < nb && j != jskip ? v : -INFINITY);
+      if (jl == 0) cmax[((long long)b * Hkv + g) * cstride + chunk] = mrow;
     }
-    cmax[((long long)b * Hkv + tid) * cstride + chunk] = m;
   }
 }
 
