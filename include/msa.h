@@ -48,6 +48,17 @@
  *     visible token gets o = 0 and lse = -inf.
  *   - Non-finite q / K / V values are not supported and not checked.
  *   - Calls that share a workspace must not overlap in time (same stream, or synchronised).
+ *   - Diagnostics, both off by default and read from the environment once per process (a value
+ *     other than empty or "0" turns them on):
+ *     MSA_LOG: every entry point prints one line with its arguments and chosen layout, and every
+ *       kernel launch one line (kernel, template parameters, grid, threads, LDS), on stderr.
+ *     MSA_DEVICE_CHECKS: every entry point that reads a paged cache first checks on the device
+ *       what the kernels otherwise tolerate silently: seq_lens outside
+ *       [0, min(max_seq_len, max_blocks * block_size)], a visible block's page id outside
+ *       [0, num_pages), and (msa_attend) a valid block listed twice in one row. The first
+ *       violation is printed on stderr and the call returns MSA_ERR_INVALID_ARG with nothing
+ *       else enqueued. This mode synchronises the stream (the one exception to the rule above),
+ *       allocates nothing, and stands aside while the stream is being captured into a graph.
  *
  * Layouts (row-major, element type per msa_config):
  *   q            decode [B][Hq][D]; prefill [T][Hq][D]

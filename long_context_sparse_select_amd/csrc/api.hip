@@ -115,6 +115,48 @@ Layout prefill_layout(const msa_config* c, int max_len, int T) {
   return L;
 }
 
+// one line per decode-side entry point when MSA_LOG is set (kernels.h): the arguments and the layout
+void log_layout(const char* entry, const msa_config* c, int B, int max_len, const Layout& L, size_t ws_bytes,
+                const char* extra) {
+  if (!log_enabled()) return;
+  log_call("%s: batch %d, max_seq_len %d, %d q / %d kv heads, top_k %d, %s; row stride %d, %d split(s) of %d "
+           "block(s)%s; workspace %zu of %zu B%s",
+           entry, B, max_len, c->num_q_heads, c->num_kv_heads, c->top_k, c->q_dtype == MSA_BF16 ? "bf16" : "f32",
+           L.row_stride, L.nsplit, L.bps, L.fused ? ", top-k inside the attend launch" : "", L.total, ws_bytes, extra);
+}
+
+// MSA_DEVICE_CHECKS (kernels.h): the caller's lengths, page ids and, for attend, lists, checked on
+// the device before anything else is enqueued
+msa_status cache_check(const char* entry, const msa_kv_cache* c, int B, int max_len, const int32_t* idx, int k,
+                       int Hkv, hipStream_t st) {
+  if (!checks_enabled()) return MSA_OK;
+  CheckArgs a;
+  a.table = c->block_table;
+  a.lens = c->seq_lens;
+  a.B = B;
+  a.max_blocks = c->max_blocks;
+  a.max_len = max_len;
+  a.num_pages = c->num_pages;
+  a.idx = idx;
+  a.k = k;
+  a.Hkv = Hkv;
+  const int r = device_check(entry, a, st);
+  return r == 0 ? MSA_OK : r > 0 ? MSA_ERR_INVALID_ARG : MSA_ERR_HIP;
+}
+
+msa_status prefill_check(const char* entry, const msa_kv_cache* c, int len, hipStream_t st) {
+  if (!checks_enabled()) return MSA_OK;
+  CheckArgs a;
+  a.table = c->block_table;
+  a.fixed_len = len;
+  a.B = 1;
+  a.max_blocks = c->max_blocks;
+  a.max_len = len;
+  a.num_pages = c->num_pages;
+  const int r = device_check(entry, a, st);
+  return r == 0 ? MSA_OK : r > 0 ? MSA_ERR_INVALID_ARG : MSA_ERR_HIP;
+}
+
 template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
 
 msa_status check_cache(const msa_kv_cache* cache, bool need_kv, bool need_lens) {
@@ -318,10 +360,12 @@ msa_status msa_workspace_size(const msa_config* cfg, int32_t op, int32_t batch, 
         if (L.nsplit > kMaxDecodeSplit) return MSA_ERR_UNSUPPORTED;   // never: the split rule bounds it
         *bytes = L.total;
       }
+      log_call("msa_workspace_size: op %d, batch %d, max_seq_len %d -> %zu B", op, batch, max_seq_len, *bytes);
       return MSA_OK;
     case MSA_OP_PREFILL:
       if (chunk_len < 1 || batch != 1 || max_seq_len < chunk_len) return MSA_ERR_INVALID_ARG;
       *bytes = prefill_layout(cfg, max_seq_len, chunk_len).total;
+      log_call("msa_workspace_size: prefill, max_seq_len %d, chunk %d -> %zu B", max_seq_len, chunk_len, *bytes);
       return MSA_OK;
     default:
       return MSA_ERR_INVALID_ARG;
@@ -335,6 +379,9 @@ msa_status msa_build_summaries(const msa_config* cfg, const msa_kv_cache* cache,
   if (cache->k_pages == nullptr) return MSA_ERR_INVALID_ARG;
   MSA_TRY(check_batch(cache, batch, max_seq_len));
   if (batch == 0) return MSA_OK;
+  MSA_TRY(cache_check("msa_build_summaries", cache, batch, max_seq_len, nullptr, 0, 0, (hipStream_t)stream));
+  log_call("msa_build_summaries: batch %d, max_seq_len %d, %d kv heads, %s summaries", batch, max_seq_len,
+           cfg->num_kv_heads, cfg->summary_dtype == MSA_BF16 ? "bf16" : "f32");
   return hip_status(launch_build_summaries(cfg->kv_dtype == MSA_BF16, cache_args(cfg, cache), batch, cfg->num_kv_heads,
                                            max_seq_len, (hipStream_t)stream));
 }
@@ -347,6 +394,9 @@ msa_status msa_score(const msa_config* cfg, const void* q, const msa_kv_cache* c
   if (q == nullptr || scores_out == nullptr) return MSA_ERR_INVALID_ARG;
   if (batch == 0) return MSA_OK;
   const int row_stride = (max_seq_len + MSA_BLOCK - 1) / MSA_BLOCK;
+  MSA_TRY(cache_check("msa_score", cache, batch, max_seq_len, nullptr, 0, 0, (hipStream_t)stream));
+  log_call("msa_score: batch %d, max_seq_len %d, %d q / %d kv heads, row stride %d", batch, max_seq_len,
+           cfg->num_q_heads, cfg->num_kv_heads, row_stride);
   return hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), batch, cfg->num_q_heads,
                                         cfg->num_kv_heads, max_seq_len, scores_out, row_stride, nullptr, nullptr,
                                         (hipStream_t)stream));
@@ -362,6 +412,8 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   const Layout L = decode_layout(cfg, MSA_OP_SELECT, batch, max_seq_len);
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
+  MSA_TRY(cache_check("msa_select", cache, batch, max_seq_len, nullptr, 0, 0, (hipStream_t)stream));
+  log_layout("msa_select", cfg, batch, max_seq_len, L, workspace_bytes, "");
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
                     (hipStream_t)stream);
@@ -381,6 +433,8 @@ msa_status msa_select_index(const msa_config* cfg, const void* q_index, const vo
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
+  MSA_TRY(cache_check("msa_select_index", cache, batch, max_seq_len, nullptr, 0, 0, st));
+  log_layout("msa_select_index", cfg, batch, max_seq_len, L, workspace_bytes, index_dim == 64 ? ", index dim 64" : ", index dim 128");
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   MSA_TRY(hip_status(launch_score_index(cfg->q_dtype == MSA_BF16, q_index, index_keys, index_dim,
                                         cache_args(cfg, cache), batch, cfg->num_kv_heads, max_seq_len, scores,
@@ -400,6 +454,8 @@ msa_status msa_attend(const msa_config* cfg, const void* q, const msa_kv_cache* 
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
   const hipStream_t st = (hipStream_t)stream;
+  MSA_TRY(cache_check("msa_attend", cache, batch, max_seq_len, idx, cfg->top_k, cfg->num_kv_heads, st));
+  log_layout("msa_attend", cfg, batch, max_seq_len, L, workspace_bytes, "");
   return run_attend(cfg, q, cache, batch, max_seq_len, idx, nullptr, out, lse_out, L, workspace, st);
 }
 
@@ -411,6 +467,9 @@ msa_status msa_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
   MSA_TRY(check_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, out, &L));
   if (workspace_bytes < L.total || workspace == nullptr) return MSA_ERR_WORKSPACE;
   if (batch == 0) return MSA_OK;
+  MSA_TRY(cache_check("msa_decode_step", cache, batch, max_seq_len, nullptr, 0, 0, (hipStream_t)stream));
+  log_layout("msa_decode_step", cfg, batch, max_seq_len, L, workspace_bytes,
+             k_new != nullptr ? ", appending a new token" : "");
   return run_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, idx_out, scores_out, out, lse_out, L,
                          workspace, (hipStream_t)stream);
 }
@@ -424,6 +483,9 @@ msa_status msa_decode_step_noalloc(const msa_config* cfg, const void* q, const m
   if (batch == 0) return MSA_OK;
   void* ws = nullptr;
   MSA_TRY(scratch_of_current_device(&ws));
+  MSA_TRY(cache_check("msa_decode_step_noalloc", cache, batch, max_seq_len, nullptr, 0, 0, (hipStream_t)stream));
+  log_layout("msa_decode_step_noalloc", cfg, batch, max_seq_len, L, (size_t)MSA_NOALLOC_SCRATCH_BYTES,
+             k_new != nullptr ? ", appending a new token; workspace = the per-GPU scratch array" : "; workspace = the per-GPU scratch array");
   return run_decode_step(cfg, q, cache, batch, max_seq_len, k_new, v_new, idx_out, scores_out, out, lse_out, L, ws,
                          (hipStream_t)stream);
 }
@@ -449,6 +511,9 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   float* qtile = at<float>(workspace, L.qtile);
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
+  MSA_TRY(prefill_check("msa_prefill_chunk", cache, max_len, st));
+  log_call("msa_prefill_chunk: past_len %d, T %d (%d tiles), %d q / %d kv heads, top_k %d; row stride %d; "
+           "workspace %zu of %zu B", past_len, T, ntiles, Hq, Hkv, cfg->top_k, L.row_stride, L.total, workspace_bytes);
 
   MSA_TRY(hip_status(launch_prefill_prologue(true, ca, k_new, v_new, q, past_blocks, T, Hq, Hkv, qtile, st)));
   MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, st)));
@@ -481,6 +546,9 @@ msa_status msa_prefill_attend(const msa_config* cfg, const void* q, const msa_kv
   if ((long long)past_len + T > (long long)cache->max_blocks * MSA_BLOCK) return MSA_ERR_INVALID_ARG;
   if (past_len % MSA_BLOCK != 0) return MSA_ERR_UNSUPPORTED;
   if (cfg->q_dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  MSA_TRY(prefill_check("msa_prefill_attend", cache, past_len + T, (hipStream_t)stream));
+  log_call("msa_prefill_attend: past_len %d, T %d, %d q / %d kv heads, top_k %d", past_len, T, cfg->num_q_heads,
+           cfg->num_kv_heads, cfg->top_k);
   return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, (hipStream_t)stream);
 }
 

@@ -345,6 +345,9 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
 template <typename T>
 hipError_t launch_merge(const AttendArgs& a, hipStream_t st) {
   const dim3 grid(a.Hq, a.B);
+  if (log_enabled())
+    log_launch("k_merge", grid, 256, 0, "%s, splits/8 = %d", sizeof(T) == 2 ? "bf16" : "f32",
+               a.nsplit <= 8 ? 1 : a.nsplit <= 32 ? 4 : kMaxSplit / 8);
   if (a.nsplit <= 8) k_merge<T, 1><<<grid, 256, 0, st>>>(a);
   else if (a.nsplit <= 32) k_merge<T, 4><<<grid, 256, 0, st>>>(a);
   else k_merge<T, kMaxSplit / 8><<<grid, 256, 0, st>>>(a);
@@ -354,6 +357,11 @@ hipError_t launch_merge(const AttendArgs& a, hipStream_t st) {
 template <typename T, int G>
 hipError_t launch_attend_g(const AttendArgs& a, hipStream_t st) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
+  if (log_enabled()) {
+    if (sizeof(T) == 2) log_launch("k_attend_decode_mfma", grid, 256, 0, "G=%d, blocks in flight %d", G,
+                                   a.blocks_per_split >= 4 ? 4 : 2);
+    else log_launch("k_attend_decode", grid, 256, 0, "f32, G=%d", G);
+  }
   if constexpr (sizeof(T) == 2) {
     if (a.blocks_per_split >= 4) k_attend_decode_mfma<G, 4><<<grid, 256, 0, st>>>(a);
     else k_attend_decode_mfma<G, 2><<<grid, 256, 0, st>>>(a);

@@ -317,6 +317,7 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid((a.T + kP - 1) / kP, a.Hkv);
+  if (log_enabled()) log_launch("k_attend_prefill", grid, 128 * G, 0, "G=%d, k=%d", G, a.k);
   switch (G) {
     case 1: k_attend_prefill<1><<<grid, 128, 0, st>>>(a); break;
     case 2: k_attend_prefill<2><<<grid, 256, 0, st>>>(a); break;

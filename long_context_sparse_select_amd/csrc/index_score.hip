@@ -140,6 +140,7 @@ hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_
   const dim3 grid((row_stride + kIB - 1) / kIB, B);
   // LDS: the Hkv index queries in storage form, then the [kIB][Hkv][16] row maxima
   const size_t lds = (size_t)Hkv * index_dim * (bf16 ? 2 : 4) + (size_t)kIB * Hkv * 16 * sizeof(float);
+  if (log_enabled()) log_launch("k_score_index", grid, 256, lds, "%s, index dim %d", bf16 ? "bf16" : "f32", index_dim);
 #define MSA_INDEX(TT, DD)                                                                                 \
   k_score_index<TT, DD><<<grid, 256, lds, st>>>((const TT*)q_index, (const TT*)index_keys, c.table, c.lens, \
                                                 c.num_pages, c.max_blocks, Hkv, max_len, scores, row_stride)

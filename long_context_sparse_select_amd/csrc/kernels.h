@@ -7,6 +7,31 @@
 
 namespace msa {
 
+// Launch logging (diag.hip): with MSA_LOG set (non-empty, not "0"), entry points and kernel
+// launches print one line each on stderr. log_launch's fmt describes the template parameters.
+bool log_enabled();
+void log_call(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void log_launch(const char* kernel, dim3 grid, int threads, size_t lds_bytes, const char* fmt, ...)
+    __attribute__((format(printf, 5, 6)));
+
+// Device-side checks of the caller's index data (diag.hip), on with MSA_DEVICE_CHECKS set
+// (non-empty, not "0"): lens (or fixed_len when lens is null) against
+// [0, min(max_len, max_blocks * 64)], the page ids of the visible blocks against [0, num_pages),
+// and, when idx is given ([B][Hkv][k] attend lists), repeated valid entries in a row (rows of up to
+// kCheckMaxBits blocks are checked in full). device_check returns 0 (clean, or checks off, or the
+// stream is capturing), 1 (a violation, printed on stderr) or -1 (a HIP error). It synchronises st.
+constexpr long long kCheckMaxBits = 1 << 18;   // 32 KiB of LDS bitmap per row
+struct CheckArgs {
+  const int32_t* table = nullptr;
+  const int32_t* lens = nullptr;
+  int fixed_len = 0;
+  int B = 0, max_blocks = 0, max_len = 0, num_pages = 0;
+  const int32_t* idx = nullptr;
+  int k = 0, Hkv = 0;
+};
+bool checks_enabled();
+int device_check(const char* entry, const CheckArgs& a, hipStream_t st);
+
 struct CacheArgs {
   void* k;               // [num_pages][Hkv][64][128]
   void* v;

@@ -67,6 +67,7 @@ extern "C" {
 msa_status msa_probe_hbm_read(const void* buf, size_t bytes, float* sink, void* stream) {
   if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0) return MSA_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return MSA_ERR_INVALID_ARG;
+  if (msa::log_enabled()) msa::log_launch("k_probe_read", dim3(msa::kReadBlocks), 256, 0, "%zu B", bytes);
   msa::k_probe_read<<<msa::kReadBlocks, 256, 0, (hipStream_t)stream>>>(
       static_cast<const uint4*>(buf), (long long)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -74,6 +75,7 @@ msa_status msa_probe_hbm_read(const void* buf, size_t bytes, float* sink, void* 
 
 msa_status msa_probe_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, void* stream) {
   if (sink == nullptr || workgroups < 1 || workgroups > 65535 || iters < 1) return MSA_ERR_INVALID_ARG;
+  if (msa::log_enabled()) msa::log_launch("k_probe_mfma", dim3(workgroups), 256, 0, "%d rounds", iters);
   msa::k_probe_mfma<<<workgroups, 256, 0, (hipStream_t)stream>>>(sink, iters);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }

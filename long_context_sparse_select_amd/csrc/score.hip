@@ -390,6 +390,10 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
   const size_t lds = (size_t)lds_floats * sizeof(float);
   TQ* kp = static_cast<TQ*>(c.k);
   TQ* vp = static_cast<TQ*>(c.v);
+  if (log_enabled())
+    log_launch("k_score_decode", grid, 256, lds, "%s q, Hkv=%d, %s summaries%s%s", sizeof(TQ) == 2 ? "bf16" : "f32",
+               Hkv, SB ? "bf16" : "f32", napp > 0 ? ", with the new token's append" : "",
+               cmax != nullptr ? ", chunk maxima" : "");
 #define MSA_SCORE_CASE(H)                                                                                  \
   case H:                                                                                                  \
     k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \
@@ -434,6 +438,7 @@ hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st) {
   const dim3 grid((row_stride + kPB - 1) / kPB, Hkv, (ntiles + kPT - 1) / kPT);
+  if (log_enabled()) log_launch("k_score_prefill", grid, 256, 0, "%s summaries", c.s_bf16 ? "bf16" : "f32");
   if (c.s_bf16)
     k_score_prefill<true><<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
                                                 row_stride);

@@ -171,6 +171,8 @@ hipError_t launch_build_summaries(bool bf16, const CacheArgs& c, int B, int Hkv,
   const long long units = (long long)B * mb * Hkv;
   if (units == 0) return hipSuccess;
   const dim3 grid((unsigned)((units + 3) / 4));
+  if (log_enabled())
+    log_launch("k_build_summaries", grid, 256, 0, "%s keys, %s summaries", bf16 ? "bf16" : "f32", c.s_bf16 ? "bf16" : "f32");
 #define MSA_BUILD(T, SB)                                                                                       \
   k_build_summaries<T, SB><<<grid, 256, 0, st>>>((const T*)c.k, c.S, c.table, c.lens, c.num_pages, c.max_blocks, \
                                                  B, Hkv, max_len, mb)
@@ -190,6 +192,9 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
   if (ntiles == 0) return hipSuccess;
   const int n_app = (ntiles * Hkv + 7) / 8;
   const dim3 grid(n_app + ntiles * Hkv);
+  if (log_enabled())
+    log_launch("k_prefill_prologue", grid, 512, 0, "%s, %s summaries, %d append workgroups", bf16 ? "bf16" : "f32",
+               c.s_bf16 ? "bf16" : "f32", n_app);
 #define MSA_PROLOGUE(TT, SB)                                                                                  \
   k_prefill_prologue<TT, SB><<<grid, 512, 0, st>>>((TT*)c.k, (TT*)c.v, c.S, c.table, c.num_pages, (const TT*)k_new, \
                                                    (const TT*)v_new, (const TT*)q, past_blocks, T, Hq, Hkv, n_app,  \

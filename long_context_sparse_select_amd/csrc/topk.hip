@@ -494,7 +494,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   // CU); longer rows or larger k on 1024
   const bool prefill = a.lens == nullptr;
   const long long n_max = prefill ? (long long)a.base_blocks + (a.rows - 1) / a.Hkv : ((long long)a.max_len + kP - 1) / kP;
-  if (n_max <= 512 * kPer && a.k <= 512) k_topk<512><<<a.rows, 512, 0, st>>>(a);
+  const int nt = n_max <= 512 * kPer && a.k <= 512 ? 512 : kThreads;
+  if (log_enabled())
+    log_launch("k_topk", dim3(a.rows), nt, 0, "%d threads; k=%d, row length up to %lld%s", nt, a.k, n_max,
+               prefill ? ", prefill rows" : "");
+  if (nt == 512) k_topk<512><<<a.rows, 512, 0, st>>>(a);
   else k_topk<kThreads><<<a.rows, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
