@@ -23,9 +23,12 @@
 //      exactly by (key desc, index asc) against the others (one thread per candidate); ranks <
 //      k_eff are kept and placed in ascending block order by counting. A candidate's page id is
 //      read in the same round trip as its score, so the attend's K/V loads follow directly;
-//   3. the workgroup attends its own entries [split * bps, (split + 1) * bps) of that list with
-//      the MFMA attend of attend_mfma.h, writes those entries of the index list, and writes the
-//      output (one split) or its split partial for k_merge.
+//   3. the workgroup attends the kept blocks of ranks [split * bps, (split + 1) * bps) with the
+//      MFMA attend of attend_mfma.h, and writes the output (one split) or its split partial for
+//      k_merge. With those blocks' K/V loads in flight, each kept block's position in ascending
+//      order (the number of kept blocks with a smaller index) is counted, and the blocks whose
+//      positions fall in the same range are written to the index list: the ordering is off the
+//      path to the first load.
 // Rows whose survivors or candidates overflow the LDS lists (mass ties) take an exact path: a
 // bitwise search for the k_eff-th key over the row's scores, then an ordered compaction.
 // Reading the row per workgroup is redundant across a row's splits, but it is ~10 KiB of L2 hits
@@ -107,15 +110,18 @@ __device__ __forceinline__ void select_exact(const float* srow, const int32_t* t
   __syncthreads();
 }
 
-// The row's k_eff kept blocks in ascending order -> sh.sorted[0 .. keff), their page ids (as the
-// table holds them, unchecked) -> sh.sortedpg. All threads call it; it ends with a barrier.
-__device__ __forceinline__ void select_row(const float* srow, const float* crow, const int32_t* trow, int n, int keff,
+// The row's k_eff kept blocks and their page ids (as the table holds them, unchecked). Returns
+// true when they are in sh.sel / sh.selpg by rank (score descending, index ascending; sh.sel is
+// padded with INT_MAX up to kMaxFusedTopK), false when they are in sh.sorted / sh.sortedpg in
+// ascending order (every block kept, or the exact path). All threads call it; it ends with a
+// barrier.
+__device__ __forceinline__ bool select_row(const float* srow, const float* crow, const int32_t* trow, int n, int keff,
                            SelectShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (keff >= n) {   // every block is kept (uniform)
     for (int e = tid; e < n; e += kFT) { sh.sorted[e] = e; sh.sortedpg[e] = trow[e]; }
     __syncthreads();
-    return;
+    return false;
   }
   const int nch = (n + kScoreChunk - 1) / kScoreChunk;
   uint32_t ck[kCPer];
@@ -258,7 +264,7 @@ __device__ __forceinline__ void select_row(const float* srow, const float* crow,
   }
   if (exact) {
     select_exact(srow, trow, n, keff, sh);
-    return;
+    return false;
   }
   const int m = sh.ncand;   // >= keff by the choice of T0
   // ---- rank = number of larger composites: four lanes (a quad) per candidate, each over every
@@ -280,7 +286,14 @@ __device__ __forceinline__ void select_row(const float* srow, const float* crow,
     if (qp == 0 && e < m && c < keff) { sh.sel[c] = (int)~(uint32_t)ce; sh.selpg[c] = sh.comppg[e]; }
   }
   __syncthreads();
-  // ---- ascending block order: position = kept blocks with a smaller index (one thread each)
+  return true;
+}
+
+// Index-list entries [e0, e1) of a row selected by rank (sh.sel, INT_MAX-padded): the kept block
+// of rank r goes to position (number of kept blocks with a smaller index); one thread per kept
+// block, entries at positions >= k_eff are -1. No barrier: sh.sel is only read.
+__device__ __forceinline__ void write_ordered(const SelectShared& sh, int keff, int e0, int e1, int32_t* out) {
+  const int tid = threadIdx.x;
   if (tid < keff) {
     const int vj = sh.sel[tid];
     int pos = 0;
@@ -290,10 +303,9 @@ __device__ __forceinline__ void select_row(const float* srow, const float* crow,
       const int4 v = s4[f];
       pos += (v.x < vj) + (v.y < vj) + (v.z < vj) + (v.w < vj);
     }
-    sh.sorted[pos] = vj;
-    sh.sortedpg[pos] = sh.selpg[tid];
+    if (pos >= e0 && pos < e1) out[pos] = vj;
   }
-  __syncthreads();
+  for (int e = max(e0, keff) + tid; e < e1; e += kFT) out[e] = -1;
 }
 
 template <int G, int U>
@@ -339,18 +351,25 @@ __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   }
 
   const int32_t* trow = a.table + (long long)b * a.max_blocks;
+  bool by_rank = false;
   if (keff > 0 && e0 < keff)   // uniform: this split holds kept blocks
-    select_row(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff, sh);
-  if (f.idx_out != nullptr) {   // this split's entries of the index list
-    for (int e = e0 + tid; e < e1; e += kFT) f.idx_out[rowbg * a.k + e] = e < keff ? sh.sorted[e] : -1;
+    by_rank = select_row(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff, sh);
+  // the blocks this split attends: ranks [e0, e1) (by_rank) or positions [e0, e1) of the ascending list
+  const int* lst = by_rank ? sh.sel : sh.sorted;
+  const int* lstpg = by_rank ? sh.selpg : sh.sortedpg;
+  int32_t* idx_row = f.idx_out != nullptr ? f.idx_out + rowbg * a.k : nullptr;
+  bool listed = idx_row == nullptr;   // this split's index-list entries written
+  if (!by_rank && !listed) {
+    for (int e = e0 + tid; e < e1; e += kFT) idx_row[e] = e < keff ? sh.sorted[e] : -1;
+    listed = true;
   }
   const int e1k = min(e1, keff);
   for (int base = e0; base < e1k; base += 64) {
     // lane e: page and live token count of kept block base + e (-1: not attended)
     int my_page = -1, my_ntok = 0;
     if (lane < e1k - base) {
-      const int j = sh.sorted[base + lane];
-      const int page = sh.sortedpg[base + lane];
+      const int j = lst[base + lane];
+      const int page = lstpg[base + lane];
       if (page_ok(page, a.num_pages)) {
         my_page = page;
         my_ntok = min(kP, N - j * kP);
@@ -368,11 +387,16 @@ __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
       KVRegs r[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) at.load(r[u], bcast(ent.x, min(t0 + u, cnt - 1)));
+      if (!listed) {   // uniform: the index-list entries, while the first K/V loads are in flight
+        write_ordered(sh, keff, e0, e1, idx_row);
+        listed = true;
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (u == 0 || t0 + u < cnt) at.step(r[u], bcast(ent.y, min(t0 + u, 63)), s_p[wave]);
     }
   }
+  if (!listed) write_ordered(sh, keff, e0, e1, idx_row);   // no live block in this split
   float lsum = at.l_l + __shfl_xor(at.l_l, 16);
   lsum += __shfl_xor(lsum, 32);
 #pragma unroll
