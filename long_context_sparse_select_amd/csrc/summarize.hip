@@ -8,7 +8,7 @@
 // even on store), which halves what the decode scoring pass reads.
 //
 // The prefill chunk's append shares a launch with the tile index queries (k_prefill_prologue):
-// the two are independent, so they overlap.
+// one workgroup does both jobs of one new block and group, so their loads overlap.
 //
 // Work mapping: one wavefront per (block, KV head). A wave reads a 64 x 128 block as 16
 // loads of 4 rows; lane l owns dims 8*(l%16) .. +7 of rows l/16, l/16+4, ... so each load
@@ -72,58 +72,75 @@ __global__ void __launch_bounds__(256) k_build_summaries(const T* __restrict__ k
   write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
 }
 
-// prefill append, one wave per unit = (new block jn, group g): T new tokens after past_len (a
-// multiple of 64) fill whole new blocks; the wave copies the block's rows into its page and
-// writes the block's summary
+// The prefill chunk's first step, one 512-thread workgroup per (tile tau, group g). Each tile is
+// one new block (past_len is a multiple of 64), so the workgroup does both of that block's jobs
+// for group g, with all of their loads in flight together:
+//   * the tile index query: qtile[tau][g][d] = mean over the tile's rows and the group's heads.
+//     Thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (2G 16 B loads); the 64
+//     rows are then summed per dim through LDS, in row order;
+//   * the append: thread (row r = tid/16, 8 dims 8*(tid%16)..) copies rows r and r + 32 of the
+//     block's new K and V into its page and sums their keys; the 32 row groups are summed per
+//     dim across each wave's four (cross-lane moves), then across the 8 waves through LDS, in
+//     wave order, and the mean is written as the block's summary.
+// One barrier serves both. A launch of ntiles * Hkv workgroups (512 for a 4096-token chunk with
+// 8 groups) fits the chip in one round.
 template <typename T, bool SB>
-__device__ __forceinline__ void append_unit(T* __restrict__ kpool, T* __restrict__ vpool, void* __restrict__ S,
-                                            const int32_t* __restrict__ table, int num_pages,
-                                            const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                            int past_blocks, int T_new, int Hkv, int unit) {
-  const int lane = threadIdx.x & 63;
+__global__ void __launch_bounds__(512) k_prefill_prologue(T* __restrict__ kpool, T* __restrict__ vpool,
+                                                          void* __restrict__ S, const int32_t* __restrict__ table,
+                                                          int num_pages, const T* __restrict__ k_new,
+                                                          const T* __restrict__ v_new, const T* __restrict__ q,
+                                                          int past_blocks, int T_new, int Hq, int Hkv,
+                                                          float* __restrict__ qtile) {
+  __shared__ float s_rows[kP][kD + 1];
+  __shared__ float s_wsum[8][kD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = (T_new + kP - 1) / kP;
-  if (unit >= ntiles * Hkv) return;
-  const int g = unit % Hkv, jn = unit / Hkv;
-  const int n = min(kP, T_new - jn * kP);
-  const int page = table[past_blocks + jn];
-  if (!page_ok(page, num_pages)) return;
-  const long long head = ((long long)page * Hkv + g) * kP * kD;
-  const int d0 = (lane & 15) * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int r = lane >> 4; r < n; r += 4) {
-    const long long src = ((long long)(jn * kP + r) * Hkv + g) * kD + d0;
-    Vec8<T> kv, vv;
-    kv.load(k_new + src);
-    vv.load(v_new + src);
-    kv.store(kpool + head + (long long)r * kD + d0);
-    vv.store(vpool + head + (long long)r * kD + d0);
-    kv.add_to(acc);
-  }
-  write_mean<SB>(acc, n, S, (long long)page * Hkv + g, lane);
-}
-
-// tile index query (512 threads): qtile[tau][g][d] = mean over the tile's rows and the group's
-// heads. Thread (row i = tid/8, 16 dims 16*(tid%8)..) sums its row's G heads (2G 16 B loads in
-// flight at once); the 64 rows are then summed per dim through LDS, in row order.
-template <typename TQ>
-__device__ __forceinline__ void tile_query(const TQ* __restrict__ q, int T, int Hq, int Hkv, float* __restrict__ qtile,
-                                           int tau, int g, float (*s_rows)[kD + 1]) {
-  const int tid = threadIdx.x;
+  const int tau = (int)blockIdx.x % ntiles, g = (int)blockIdx.x / ntiles;
   const int G = Hq / Hkv;
-  const int i0 = tau * kP, n = min(T, i0 + kP) - i0;
-  const int i = tid >> 3, d0 = (tid & 7) * 16;
+  const int i0 = tau * kP, n = min(T_new, i0 + kP) - i0;
+  // tile query loads: the row's 16 dims of each head
+  const int i = tid >> 3, dq = (tid & 7) * 16;
   const int row = i0 + min(i, n - 1);
-  Vec8<TQ> v[kMaxGroup][2];   // the row's 16 dims of each head: 16 B vector loads, all in flight
+  Vec8<T> v[kMaxGroup][2];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
-    const TQ* src = q + ((long long)row * Hq + g * G + min(h, G - 1)) * kD + d0;
+    const T* src = q + ((long long)row * Hq + g * G + min(h, G - 1)) * kD + dq;
     v[h][0].load(src);
     v[h][1].load(src + 8);
   }
-  float acc[16];
+  // append loads: rows r and r + 32 of the block (a row past the chunk re-reads row n - 1; unused)
+  const int page = table[past_blocks + tau];
+  const bool app = page_ok(page, num_pages);   // uniform
+  const int r = tid >> 4, da = (tid & 15) * 8;
+  Vec8<T> kv[2], vv[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int u = 0; u < 2; ++u) {
+    const long long src = ((long long)(i0 + min(r + 32 * u, n - 1)) * Hkv + g) * kD + da;
+    kv[u].load(k_new + src);
+    vv[u].load(v_new + src);
+  }
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (app) {
+    const long long head = ((long long)page * Hkv + g) * kP * kD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (r + 32 * u < n) {
+        kv[u].store(kpool + head + (long long)(r + 32 * u) * kD + da);
+        vv[u].store(vpool + head + (long long)(r + 32 * u) * kD + da);
+        kv[u].add_to(acc);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = across_rows_sum(acc[e]);   // the wave's four row groups
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_wsum[wave][da + e] = acc[e];
+    }
+  }
+  // tile query: the row's sum over the group's heads
+  float qs[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) qs[e] = 0.f;
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h < G) {
@@ -131,37 +148,26 @@ __device__ __forceinline__ void tile_query(const TQ* __restrict__ q, int T, int 
       v[h][0].to_f32(f);
       v[h][1].to_f32(f + 8);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] += f[e];
+      for (int e = 0; e < 16; ++e) qs[e] += f[e];
     }
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s_rows[i][d0 + e] = i < n ? acc[e] : 0.f;
+  for (int e = 0; e < 16; ++e) s_rows[i][dq + e] = i < n ? qs[e] : 0.f;
   __syncthreads();
   if (tid < kD) {
-    float acc = 0.f;
-    for (int r = 0; r < n; ++r) acc += s_rows[r][tid];
-    qtile[((long long)tau * Hkv + g) * kD + tid] = acc / (float)(n * G);
+    float t = 0.f;
+    for (int rr = 0; rr < n; ++rr) t += s_rows[rr][tid];
+    qtile[((long long)tau * Hkv + g) * kD + tid] = t / (float)(n * G);
+    if (app) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) sum += s_wsum[w][tid];
+      const float m = sum / (float)n;
+      const long long si = ((long long)page * Hkv + g) * kD + tid;
+      if constexpr (SB) reinterpret_cast<uint16_t*>(S)[si] = (uint16_t)(pack_bf16x2(m, 0.f) & 0xffffu);
+      else reinterpret_cast<float*>(S)[si] = m;
+    }
   }
-}
-
-// The prefill chunk's two independent first steps in one launch: workgroups [0, n_app) append
-// (eight (new block, group) units each, one per wave), the others compute one tile index query
-// each, so the two overlap instead of running back to back.
-template <typename T, bool SB>
-__global__ void __launch_bounds__(512) k_prefill_prologue(T* __restrict__ kpool, T* __restrict__ vpool,
-                                                          void* __restrict__ S, const int32_t* __restrict__ table,
-                                                          int num_pages, const T* __restrict__ k_new,
-                                                          const T* __restrict__ v_new, const T* __restrict__ q,
-                                                          int past_blocks, int T_new, int Hq, int Hkv, int n_app,
-                                                          float* __restrict__ qtile) {
-  __shared__ float s_rows[kP][kD + 1];
-  if ((int)blockIdx.x < n_app) {   // uniform per workgroup
-    append_unit<T, SB>(kpool, vpool, S, table, num_pages, k_new, v_new, past_blocks, T_new, Hkv,
-                       (int)blockIdx.x * 8 + (int)(threadIdx.x >> 6));
-    return;
-  }
-  const int e = (int)blockIdx.x - n_app, ntiles = (T_new + kP - 1) / kP;
-  tile_query<T>(q, T_new, Hq, Hkv, qtile, e % ntiles, e / ntiles, s_rows);
 }
 
 }  // namespace
@@ -190,15 +196,12 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
                                    hipStream_t st) {
   const int ntiles = (T + kP - 1) / kP;
   if (ntiles == 0) return hipSuccess;
-  const int n_app = (ntiles * Hkv + 7) / 8;
-  const dim3 grid(n_app + ntiles * Hkv);
+  const dim3 grid(ntiles * Hkv);
   if (log_enabled())
-    log_launch("k_prefill_prologue", grid, 512, 0, "%s, %s summaries, %d append workgroups", bf16 ? "bf16" : "f32",
-               c.s_bf16 ? "bf16" : "f32", n_app);
+    log_launch("k_prefill_prologue", grid, 512, 0, "%s, %s summaries", bf16 ? "bf16" : "f32", c.s_bf16 ? "bf16" : "f32");
 #define MSA_PROLOGUE(TT, SB)                                                                                  \
   k_prefill_prologue<TT, SB><<<grid, 512, 0, st>>>((TT*)c.k, (TT*)c.v, c.S, c.table, c.num_pages, (const TT*)k_new, \
-                                                   (const TT*)v_new, (const TT*)q, past_blocks, T, Hq, Hkv, n_app,  \
-                                                   qtile)
+                                                   (const TT*)v_new, (const TT*)q, past_blocks, T, Hq, Hkv, qtile)
   if (bf16) {
     if (c.s_bf16) MSA_PROLOGUE(uint16_t, true); else MSA_PROLOGUE(uint16_t, false);
   } else {
