@@ -213,11 +213,13 @@ msa_status run_topk(const msa_config* cfg, const msa_kv_cache* cache, int B, int
 
 // Step 1 on validated arguments; the appended token (k_new / v_new, nullable) goes into the
 // scoring launch
+// pad: the scores go to a caller's buffer, which gets its -inf entries past each sequence's end
 msa_status run_select(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int B, int max_len,
                       float* scores, int row_stride, int32_t* idx, int32_t* pages, const void* k_new,
-                      const void* v_new, hipStream_t st) {
+                      const void* v_new, bool pad, hipStream_t st) {
   MSA_TRY(hip_status(launch_score_decode(cfg->q_dtype == MSA_BF16, q, cache_args(cfg, cache), B, cfg->num_q_heads,
-                                         cfg->num_kv_heads, max_len, scores, row_stride, k_new, v_new, st)));
+                                         cfg->num_kv_heads, max_len, scores, row_stride, k_new, v_new, st, nullptr, 0,
+                                         pad)));
   return run_topk(cfg, cache, B, max_len, scores, row_stride, idx, pages, st);
 }
 
@@ -281,7 +283,8 @@ msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
   if (L.fused) {   // score (+ chunk maxima) -> select-and-attend -> merge
     float* cmax = at<float>(ws, L.cmax);
     MSA_TRY(hip_status(launch_score_decode(true, q, cache_args(cfg, cache), B, cfg->num_q_heads, cfg->num_kv_heads,
-                                           max_len, scores, L.row_stride, k_new, v_new, st, cmax, L.cstride)));
+                                           max_len, scores, L.row_stride, k_new, v_new, st, cmax, L.cstride,
+                                           scores_out != nullptr)));
     FusedArgs f{};
     f.att = attend_args(cfg, q, cache, B, max_len, nullptr, nullptr, out, lse_out, L, ws);
     f.scores = scores;
@@ -293,7 +296,8 @@ msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
   }
   int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, L.idx);
   int32_t* pages = at<int32_t>(ws, L.pages);
-  MSA_TRY(run_select(cfg, q, cache, B, max_len, scores, L.row_stride, idx, pages, k_new, v_new, st));
+  MSA_TRY(run_select(cfg, q, cache, B, max_len, scores, L.row_stride, idx, pages, k_new, v_new, scores_out != nullptr,
+                     st));
   return run_attend(cfg, q, cache, B, max_len, idx, pages, out, lse_out, L, ws, st);
 }
 
@@ -416,7 +420,7 @@ msa_status msa_select(const msa_config* cfg, const void* q, const msa_kv_cache* 
   log_layout("msa_select", cfg, batch, max_seq_len, L, workspace_bytes, "");
   float* scores = scores_out ? scores_out : at<float>(workspace, L.scores);
   return run_select(cfg, q, cache, batch, max_seq_len, scores, L.row_stride, idx_out, nullptr, nullptr, nullptr,
-                    (hipStream_t)stream);
+                    scores_out != nullptr, (hipStream_t)stream);
 }
 
 msa_status msa_select_index(const msa_config* cfg, const void* q_index, const void* index_keys, int32_t index_dim,

@@ -57,10 +57,12 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
 // its keys and scores the block from the stored summary.
 // cmax (nullable, [B][Hkv][cstride]): the largest score of each run of kScoreChunk blocks j < n_b,
 // the appended block's excepted (-inf for a run with none); cstride >= ceil(row_stride / kScoreChunk)
+// pad: also write -inf for the whole runs past n_b (a caller's score buffer); without it those
+// entries are left as they are (the library's own consumers read a row only up to n_b)
 constexpr int kScoreChunk = 16;
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
                                int max_len, float* scores, int row_stride, const void* k_new, const void* v_new,
-                               hipStream_t st, float* cmax = nullptr, int cstride = 0);
+                               hipStream_t st, float* cmax = nullptr, int cstride = 0, bool pad = true);
 // index branch (single-head index keys [num_pages][64][index_dim], q_index [B][Hkv][index_dim],
 // index_dim 64 or 128): block score = max over the block's valid tokens of <q_index[b][g], K_idx[t]>
 hipError_t launch_score_index(bool bf16, const void* q_index, const void* index_keys, int index_dim,

@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
                                                       float* __restrict__ scores, int row_stride,
                                                       const TQ* __restrict__ k_new, const TQ* __restrict__ v_new,
                                                       TQ* __restrict__ kpool, TQ* __restrict__ vpool, void* S_app,
-                                                      int napp, float* __restrict__ cmax, int cstride) {
+                                                      int napp, float* __restrict__ cmax, int cstride, int pad) {
   const int Hkv = HKV > 0 ? HKV : hkv_arg;
   extern __shared__ float s_qidx[];             // [Hkv][128] index queries, then [Hkv][kChunk] scores
   const int b = blockIdx.y;
@@ -188,7 +188,10 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   };
   table_loads(0);
   const int nb = (clamp_len(lens[b], max_len) + kP - 1) / kP;   // in flight with the table loads
-  if (j0 >= nb) {   // a chunk past the sequence's end (batches of mixed lengths): -inf, no summary reads
+  if (j0 >= nb) {   // a chunk past the sequence's end (batches of mixed lengths): no summary reads;
+    // its -inf scores are written only for a caller's score buffer (pad), since every consumer in
+    // the library reads a row only up to the sequence's length
+    if (!pad) return;
     for (int e = tid; e < Hkv * kChunk; e += 256) {
       const int g = e / kChunk, jl = e % kChunk;
       if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
@@ -382,7 +385,8 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
 
 template <typename TQ, bool SB>
 void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
-                        int row_stride, const TQ* k_new, const TQ* v_new, float* cmax, int cstride, hipStream_t st) {
+                        int row_stride, const TQ* k_new, const TQ* v_new, float* cmax, int cstride, int pad,
+                        hipStream_t st) {
   static_assert(kChunk == kScoreChunk, "chunk maxima cover the scoring kernel's chunks");
   const int napp = k_new != nullptr ? Hkv : 0;
   const dim3 grid(napp + (row_stride + kChunk - 1) / kChunk, B);
@@ -398,7 +402,7 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
   case H:                                                                                                  \
     k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \
                                                       Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, \
-                                                      c.S, napp, cmax, cstride);                           \
+                                                      c.S, napp, cmax, cstride, pad);                      \
     break;
   switch (Hkv) {
     MSA_SCORE_CASE(1)
@@ -411,7 +415,7 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
     default:
       k_score_decode<TQ, 0, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq,
                                                         Hkv, max_len, scores, row_stride, k_new, v_new, kp, vp, c.S,
-                                                        napp, cmax, cstride);
+                                                        napp, cmax, cstride, pad);
   }
 #undef MSA_SCORE_CASE
 }
@@ -420,11 +424,11 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
 
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len,
                                float* scores, int row_stride, const void* k_new, const void* v_new, hipStream_t st,
-                               float* cmax, int cstride) {
+                               float* cmax, int cstride, bool pad) {
   if (B == 0 || row_stride == 0) return hipSuccess;
 #define MSA_SCORE_TYPED(T, SB)                                                                                 \
   launch_score_typed<T, SB>((const T*)q, c, B, Hq, Hkv, max_len, scores, row_stride, (const T*)k_new, (const T*)v_new, \
-                            cmax, cstride, st)
+                            cmax, cstride, pad ? 1 : 0, st)
   if (bf16) {
     if (c.s_bf16) MSA_SCORE_TYPED(uint16_t, true); else MSA_SCORE_TYPED(uint16_t, false);
   } else {
