@@ -301,9 +301,13 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   }
 }
 
-// prefill scores: a 64-tile x 64-block fp32 product per workgroup on fp32 MFMA
-// (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 accumulation); tile tau scores the blocks
-// j < past_blocks + tau (its causal candidates), -inf elsewhere in the row.
+// prefill scores: a 64-tile x 65-block fp32 product per workgroup, 64 blocks on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 accumulation) and the 65th on the vector
+// ALU; tile tau scores the blocks j < past_blocks + tau (its causal candidates), -inf elsewhere
+// in the row. 65 rather than 64 blocks per workgroup: a 4096-token chunk on a cache of a multiple
+// of 4096 tokens has 64k + 64 candidate blocks, and 65-block groups make that 64k + 64 = 65 m
+// groups, 512 workgroups at 8 KV groups, which run in one round at two per CU instead of 520 in
+// two.
 // Staging: the 64 tile queries and the 64 block summaries (512 B rows) are read coalesced, 32
 // lanes per row, all 16 loads of a thread in flight at once, and stored to LDS rows padded to
 // 132 floats. Wave w then computes the 32 x 32 output tile (tiles 32*(w/2) .., blocks
@@ -311,8 +315,12 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
 // dims 64h .. 64h+63 of one tile row (A) and one block row (B) as 16 B LDS reads (row pitch
 // 132 floats: the 16 rows a read touches fall on distinct banks).
 constexpr int kPT = 64;     // tiles per workgroup
-constexpr int kPB = 64;     // blocks per workgroup
+constexpr int kPB = 64;     // blocks per workgroup on MFMA
+constexpr int kPBW = kPB + 1;   // blocks per workgroup: the MFMA ones and one on the vector ALU
 constexpr int kRowP = 132;  // LDS row pitch (floats)
+__device__ __forceinline__ int pgx_of(const int32_t* table, int j, int ncand_max) {
+  return table[min(j, max(ncand_max - 1, 0))];
+}
 typedef float f32x16s __attribute__((ext_vector_type(16)));
 
 template <bool SB>
@@ -321,10 +329,10 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
                                                        int past_blocks, int ntiles, int Hkv,
                                                        float* __restrict__ scores, int row_stride) {
   __shared__ __align__(16) float s_a[kPT * kRowP];
-  __shared__ __align__(16) float s_b[kPB * kRowP];
+  __shared__ __align__(16) float s_b[kPBW * kRowP];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = blockIdx.y;
-  const int tz = blockIdx.z * kPT, jz = blockIdx.x * kPB;
+  const int tz = blockIdx.z * kPT, jz = blockIdx.x * kPBW;
   const int ncand_max = past_blocks + ntiles - 1;      // candidates of the last tile
   {
     // thread -> rows (tid/32) + 8*it, float4 column tid%32; table entries first, then the rows
@@ -332,7 +340,9 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
     int pg[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) pg[it] = table[min(jz + (tid >> 5) + 8 * it, max(ncand_max - 1, 0))];
-    float4 av[8], bv[8];
+    // the 65th block's row: threads 0..31, one float4 each
+    const int pgx = table[min(jz + kPB, max(ncand_max - 1, 0))];
+    float4 av[8], bv[8], bx = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = (tid >> 5) + 8 * it;
@@ -346,12 +356,23 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
         bv[it] = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(S) + srow * kD)[c4];
       }
     }
+    if (tid < 32) {
+      const int page = page_ok(pgx, num_pages) ? pgx : 0;
+      const long long srow = (long long)page * Hkv + g;
+      if constexpr (SB) {
+        const uint2 w = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(S) + srow * kD)[c4];
+        bx = make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+      } else {
+        bx = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(S) + srow * kD)[c4];
+      }
+    }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = (tid >> 5) + 8 * it;
       *reinterpret_cast<float4*>(s_a + r * kRowP + 4 * c4) = av[it];
       *reinterpret_cast<float4*>(s_b + r * kRowP + 4 * c4) = bv[it];
     }
+    if (tid < 32) *reinterpret_cast<float4*>(s_b + kPB * kRowP + 4 * c4) = bx;
   }
   __syncthreads();
   const int i = lane & 31, h = lane >> 5;
@@ -369,6 +390,29 @@ __global__ void __launch_bounds__(256) k_score_prefill(const float* __restrict__
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, b4.y, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, b4.z, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, b4.w, acc, 0, 0, 0);
+  }
+  {  // the 65th block on the vector ALU: thread -> (tile tid/4, dims 32 (tid%4) ..), fp32 FMAs in
+     // dim order, then a sum over the quad
+    const int t = tid >> 2, q4 = tid & 3;
+    const float* ar = s_a + t * kRowP + 32 * q4;
+    const float* br = s_b + kPB * kRowP + 32 * q4;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4 a4 = *reinterpret_cast<const float4*>(ar + 4 * e);
+      const float4 b4 = *reinterpret_cast<const float4*>(br + 4 * e);
+      part = fmaf(a4.x, b4.x, part);
+      part = fmaf(a4.y, b4.y, part);
+      part = fmaf(a4.z, b4.z, part);
+      part = fmaf(a4.w, b4.w, part);
+    }
+    part += dpp_mov<0xB1>(part);   // quad_perm [1,0,3,2]
+    part += dpp_mov<0x4E>(part);   // quad_perm [2,3,0,1]
+    const int jx = jz + kPB, tau = tz + t;
+    if (q4 == 0 && jx < row_stride && tau < ntiles) {
+      const bool okx = jx < ncand_max && page_ok(pgx_of(table, jx, ncand_max), num_pages);
+      scores[((long long)tau * Hkv + g) * row_stride + jx] = (okx && jx < past_blocks + tau) ? part : -INFINITY;
+    }
   }
   // lane l holds block jz + jb + l%32 of tiles tz + ta + 8*(r/4) + 4*(l/32) + r%4
   const int j = jz + jb + i;
@@ -441,7 +485,7 @@ hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int
 
 hipError_t launch_score_prefill(const float* qtile, const CacheArgs& c, int past_blocks, int ntiles, int Hkv,
                                 float* scores, int row_stride, hipStream_t st) {
-  const dim3 grid((row_stride + kPB - 1) / kPB, Hkv, (ntiles + kPT - 1) / kPT);
+  const dim3 grid((row_stride + kPBW - 1) / kPBW, Hkv, (ntiles + kPT - 1) / kPT);
   if (log_enabled()) log_launch("k_score_prefill", grid, 256, 0, "%s summaries", c.s_bf16 ? "bf16" : "f32");
   if (c.s_bf16)
     k_score_prefill<true><<<grid, 256, 0, st>>>(qtile, c.S, c.table, c.num_pages, past_blocks, ntiles, Hkv, scores,
