@@ -454,3 +454,30 @@ def test_bf16_p_rounding_bound(entry):
             err = np.abs(got[b, h] - ref["o"][b, h])
             assert np.all(err <= bound), (entry, b, h, float((err / bound).max()))
     assert_close(lse.cpu().numpy(), ref["lse"], "bf16", "lse", lse=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_outputs_do_not_depend_on_workspace_contents(dtype):
+    """Workspace scores are written only up to each sequence's length (the top-k and the fused
+    selection read no further), so a workspace full of NaN bytes must give the same step and the
+    same selection as a zeroed one. Mixed lengths, so most chunks of the short rows are skipped;
+    bf16 takes the fused select-and-attend path, f32 the separate top-k."""
+    c = make_decode_case(B=4, Hq=8, Hkv=2, lens=[100, 3000, 64 * 700 - 3, 9000], top_k=8, dtype=dtype, seed=81)
+    d = to_device(c)
+    B, max_len = c.B, c.max_seq_len
+    n = msa.msa_workspace_size(d.cfg, msa.MSA_OP_DECODE, B, max_len)
+    results = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(d.q)
+        lse = torch.empty((B, c.Hq), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
+        msa.msa_decode_step(d.cfg, d.q, d.cache, B, max_len, out, idx_out=idx, lse_out=lse, workspace=ws)
+        sel = torch.empty_like(idx)
+        ws.fill_(fill)
+        msa.msa_select(d.cfg, d.q, d.cache, B, max_len, sel, workspace=ws)
+        torch.cuda.synchronize()
+        results.append((out, lse, idx, sel))
+    for name, x, y in zip(("o", "lse", "idx", "select"), results[0], results[1]):
+        assert torch.equal(x, y), name
+    assert torch.equal(results[0][2], results[0][3])
