@@ -93,6 +93,19 @@ def step_and_check(d, pool, seed, sink=0, local=0, append=True):
     else:
         check_f32_summaries(d)
         full_decode_check(d, res)
+    # the same step again with its scores in a workspace full of NaN bytes (so written only up to
+    # each sequence's length, and never read further): the append is idempotent, so the outputs,
+    # lse and lists must be bit-identical
+    c = d.case
+    ws = torch.full((msa.msa_workspace_size(d.cfg, msa.MSA_OP_DECODE, c.B, c.max_seq_len),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.q)
+    lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
+    idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
+    msa.msa_decode_step(d.cfg, d.q, d.cache, c.B, c.max_seq_len, out, k_new=kn if append else None,
+                        v_new=vn if append else None, idx_out=idx, lse_out=lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, res["o"]) and torch.equal(lse, res["lse"]) and torch.equal(idx, res["idx"])
     return res
 
 
