@@ -85,7 +85,8 @@ template <typename T, int G>
 __global__ void __launch_bounds__(256) k_attend_decode(AttendArgs a) {
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ float s_o[4][G][kD];
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const SplitRow sr = split_row_of_block();
+  const int split = sr.split, g = sr.g, b = sr.b;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, row = lane >> 4;
   const int d0 = (lane & 15) * 8;
   const int N = clamp_len(a.lens[b], a.max_len);
@@ -183,7 +184,8 @@ __global__ void __launch_bounds__(256) k_attend_decode_mfma(AttendArgs a) {
   __shared__ float s_o[4][G][kD];
   __shared__ uint16_t s_p[4][G][4][4];     // per wave: [head][token row r][pair slot i] -> key 4i + r
   __shared__ int2 s_list[4][64];           // per wave: (page, live tokens) of the attended blocks
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const SplitRow sr = split_row_of_block();
+  const int split = sr.split, g = sr.g, b = sr.b;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = clamp_len(a.lens[b], a.max_len);
   const int nb = (N + kP - 1) / kP;
@@ -281,7 +283,17 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
   __shared__ float s_w[8 * NB];
   __shared__ float s_ML[2];
   __shared__ float4 s_red[8][kD / 4];
-  const int hq = blockIdx.x, b = blockIdx.y;
+  // (sequence, head) from the linear id as the attend launches place rows: row r = id % R on XCD
+  // r % 8 when R = Hkv * B is a multiple of 8 (see split_row_of_block), its G heads at id / R
+  int hq = blockIdx.x, b = blockIdx.y;
+  {
+    const int G = a.Hq / a.Hkv, R = a.Hkv * (int)gridDim.y;
+    if ((R & 7) == 0) {
+      const int id = (int)(blockIdx.x + gridDim.x * blockIdx.y), r = id % R;
+      b = r / a.Hkv;
+      hq = (r % a.Hkv) * G + id / R;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, c = tid & 31, sg = tid >> 5;
   const int ns = a.nsplit;
   const long long unit0 = ((long long)b * a.Hq + hq) * ns;   // split s -> unit0 + s

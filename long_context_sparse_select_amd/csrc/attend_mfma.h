@@ -15,6 +15,20 @@ namespace {
 
 constexpr int kMaxSplit = kMaxDecodeSplit;
 
+// Workgroup -> (split, group, sequence) for a grid (nsplit, Hkv, B). Workgroups go to the 8 XCDs
+// round-robin by linear id, so when the row count R = Hkv * B is a multiple of 8, taking
+// row = id % R and split = id / R puts every split of a row on XCD row % 8, the XCD whose L2 then
+// holds the row's partials for k_merge (which maps its workgroups the same way). Any mapping is
+// correct; this one only places work.
+struct SplitRow { int split, g, b; };
+__device__ __forceinline__ SplitRow split_row_of_block() {
+  const int R = (int)(gridDim.y * gridDim.z);
+  if ((R & 7) != 0) return {(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  const int id = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int row = id % R;
+  return {id / R, row % (int)gridDim.y, row / (int)gridDim.y};
+}
+
 template <typename T> __device__ __forceinline__ void store_out2(T* out, long long i, float a, float b);
 template <> __device__ __forceinline__ void store_out2<uint16_t>(uint16_t* out, long long i, float a, float b) {
   reinterpret_cast<uint32_t*>(out)[i / 2] = pack_bf16x2(a, b);

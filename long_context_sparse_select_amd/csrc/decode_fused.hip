@@ -316,7 +316,8 @@ __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   __shared__ float s_o[4][G][kD];
   __shared__ uint16_t s_p[4][G][4][4];
   __shared__ int2 s_list[4][64];
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const SplitRow sr = split_row_of_block();
+  const int split = sr.split, g = sr.g, b = sr.b;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = clamp_len(a.lens[b], a.max_len);
   const int nb = (N + kP - 1) / kP;
