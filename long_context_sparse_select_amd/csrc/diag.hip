@@ -132,13 +132,14 @@ int device_check(const char* entry, const CheckArgs& a, hipStream_t st) {
   if (hipMemcpyAsync(h, w, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return -1;
   if (hipStreamSynchronize(st) != hipSuccess) return -1;
   if (h[0] == 0) return 0;
-  static const char* what[] = {"", "seq_lens[%d] = %d is outside [0, min(max_seq_len, max_blocks * 64)]%.0d",
-                               "block_table[%d][%d] = %d is not a page id in [0, num_pages)",
-                               "idx[%d][%d][%d] = %d repeats a block already listed in its row"};
   char msg[256];
-  if (h[0] == 1) std::snprintf(msg, sizeof(msg), what[1], h[1], h[3], 0);
-  else if (h[0] == 2) std::snprintf(msg, sizeof(msg), what[2], h[1], h[2], h[3]);
-  else std::snprintf(msg, sizeof(msg), what[3], h[1], h[2] / a.k, h[2] % a.k, h[3]);
+  if (h[0] == 1)
+    std::snprintf(msg, sizeof(msg), "seq_lens[%d] = %d is outside [0, min(max_seq_len, max_blocks * 64)]", h[1], h[3]);
+  else if (h[0] == 2)
+    std::snprintf(msg, sizeof(msg), "block_table[%d][%d] = %d is not a page id in [0, num_pages)", h[1], h[2], h[3]);
+  else
+    std::snprintf(msg, sizeof(msg), "idx[%d][%d][%d] = %d repeats a block already listed in its row", h[1],
+                  h[2] / a.k, h[2] % a.k, h[3]);
   std::lock_guard<std::mutex> lock(g_log_mutex);
   std::fprintf(stderr, "[msa] MSA_DEVICE_CHECKS: %s: %s\n", entry, msg);
   return 1;
