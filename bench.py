@@ -195,8 +195,8 @@ def main():
                          "k = 1024 attend and of the index-branch select, then of a 256 MiB device copy (the "
                          "byte-count calibration), for rocprofv3 --pmc; no timing")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="only the prefill chunk line (its own JSON object), e.g. for rocprofv3 --pmc passes "
-                         "over the MFMA attend")
+                    help="only the prefill chunk line (its own JSON object), then a 256 MiB device copy (the "
+                         "byte-count calibration), e.g. for rocprofv3 --pmc passes over the MFMA attend")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -210,8 +210,10 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     if args.prefill_only:
-        print(json.dumps({"prefill": bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev)}),
-              flush=True)
+        rec = {"prefill": bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev)}
+        calibration_copies(torch, dev)   # after the timing: the byte-count calibration of counter passes
+        rec["copy_launches"], rec["copy_bytes"] = 4, COPY_BYTES
+        print(json.dumps(rec), flush=True)
         return
     kw = workload(args.workload, seed=args.seed)
     L = max(1, args.layers)
@@ -320,6 +322,7 @@ def main():
     # algorithmic bytes of one scoring launch: summaries + block-table entries read, scores written
     score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
     kv_gbps = kv_bytes / t_att / 1e9
+    hbm_gbps = hbm_bytes / t_att / 1e9
     step_bytes = score_bytes + kv_bytes + 2 * B * Hq * D * elem + B * Hkv * k * 4
     working_set = L * step_bytes   # what the rotation of the timed steps reads, in distinct bytes
     score_gbps = score_bytes / t_score / 1e9
@@ -396,8 +399,9 @@ def main():
     rec["attend_roofline"]["frac_of_measured"] = rec["attend_roofline"]["achieved"] / peaks["hbm_read_GBps"]
     if rec.get("prefill"):
         rec["prefill"]["bf16_mfma_frac_of_measured"] = rec["prefill"]["TFLOPs"] / peaks["bf16_mfma_TFLOPs"]
-        rec["prefill"]["roofline"]["frac_of_measured"] = (rec["prefill"]["roofline"]["achieved"]
-                                                          / peaks["bf16_mfma_TFLOPs"])
+        pr = rec["prefill"]["roofline"]
+        pr["frac_of_measured"] = pr["achieved"] / (peaks["hbm_read_GBps"] if pr["bound"] == "hbm"
+                                                   else peaks["bf16_mfma_TFLOPs"])
     # ---- CPU oracle baseline (regenerates the first cache of the workload: same seed, same data)
     if not args.no_cpu_baseline:
         c = make_decode_case_torch(device=dev, **dict(kw, seed=args.seed))
@@ -465,18 +469,25 @@ def counter_pass(args, torch, msa, cfg, q_ring, caches, B, max_len, sc_buf, dev)
     nbi = (icases[0].max_seq_len + 63) // 64
     index_bytes = nbi * 64 * 128 * 2 + nbi * 4 + 8 * 128 * 2 + 8 * nbi * 4
     del icases
-    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
-    src.fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(4):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    calibration_copies(torch, dev)
     print(json.dumps({"counter_pass": args.workload, "score_launches": n + 2 * L + L + n,
                       "decode_step_launches": n, "decode_step_selected_kv_bytes": step_kv_bytes,
                       "attend_launches": n,
                       "attend_bytes_per_launch": attend_bytes, "index_launches": n,
                       "index_score_bytes_per_launch": index_bytes, "copy_launches": 4,
                       "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def calibration_copies(torch, dev, n=4):
+    """n device copies of COPY_BYTES: a kernel of known traffic, which scales the FETCH_SIZE /
+    WRITE_SIZE counts of the same rocprofv3 pass to bytes"""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def sources_digest(paths):
@@ -544,17 +555,36 @@ def bench_prefill(args, torch, np, msa, make_prefill_case_torch, workload, dev):
         keff = min(p.top_k, p.past_len // 64 + tau)
         pairs += rows * 64 * keff + rows * (rows + 1) // 2
     flops = 4.0 * p.D * p.Hq * pairs
+    # every (tile, group) reads the K and V of its diagonal block and of its selected blocks; the
+    # launch also reads the chunk's queries and writes its outputs (bf16)
+    blocks = p.Hkv * sum(1 + min(p.top_k, p.past_len // 64 + tau) for tau in range(ntiles))
+    kv_bytes = blocks * 2 * 64 * p.D * 2
+    hbm_bytes = kv_bytes + 2 * p.T * p.Hq * p.D * 2
     tf = flops / t / 1e12
     tfa = flops / t_att / 1e12
-    log("prefill chunk: %.1f us, %.1f TFLOP/s (causal-visible, whole chunk); attend alone %.1f us, %.1f TFLOP/s"
-        % (t * 1e6, tf, t_att * 1e6, tfa))
+    kv_gbps = kv_bytes / t_att / 1e9
+    hbm_gbps = hbm_bytes / t_att / 1e9
+    log("prefill chunk: %.1f us, %.1f TFLOP/s (causal-visible, whole chunk); attend alone %.1f us, %.1f TFLOP/s, "
+        "%.0f GB/s (selected K/V, queries, outputs)" % (t * 1e6, tf, t_att * 1e6, tfa, hbm_gbps))
+    # the kernel's two floors: its FLOPs at the bf16 MFMA peak and its K/V bytes at the HBM peak;
+    # the larger one is the bound
+    views = {"mfma": {"achieved": tfa, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tfa / BF16_PEAK_TFLOPS,
+                      "floor_us": flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6},
+             "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
+                     "floor_us": hbm_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6}}
+    bound = max(views, key=lambda v: views[v]["floor_us"])
+    roof = {"bound": bound, "kernel": "k_attend_prefill (msa_prefill_attend): Step 2 of the chunk"}
+    roof.update({k: views[bound][k] for k in ("achieved", "peak", "unit", "frac")})
+    roof.update({"flops_per_launch": flops, "hbm_bytes_per_launch": hbm_bytes, "kv_bytes_per_launch": kv_bytes,
+                 "us_per_launch": t_att * 1e6,
+                 "flops_rule": "4 * 128 * Hq * (causal-visible query-key pairs of the selected blocks)",
+                 "hbm_bytes_rule": "Hkv * sum over tiles of (1 + k_eff) blocks * (K + V) * 64 tokens * 128 dims * 2 B"
+                                   " + queries read + outputs written (T * Hq * 128 * 2 B each)",
+                 "views": views})
     return {"workload": "prefill_bf16_4k_on_256k", "chunk_us": t * 1e6, "TFLOPs": tf,
             "bf16_mfma_frac": tf / BF16_PEAK_TFLOPS, "flops": flops,
             "note": "whole chunk: append + summaries + tile query + score + top-k + MFMA attend",
-            "roofline": {"bound": "mfma", "kernel": "k_attend_prefill (msa_prefill_attend): Step 2 of the chunk",
-                         "achieved": tfa, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tfa / BF16_PEAK_TFLOPS,
-                         "flops_per_launch": flops, "us_per_launch": t_att * 1e6,
-                         "flops_rule": "4 * 128 * Hq * (causal-visible query-key pairs of the selected blocks)"}}
+            "roofline": roof}
 
 
 def bench_batched(args, torch, np, msa, make_decode_case_torch, workload, dev, L=8, R=8):
