@@ -7,7 +7,9 @@
 // tile's diagonal block is always attended, causally (key position <= query position).
 //
 // One workgroup per (tile, KV group): rows = 64 tokens x G heads (256 for G = 4), 2G waves of
-// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). The diagonal block is attended first,
+// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). A group of more than 4 heads is split over
+// two workgroups of ceil(G/2) heads each, which stage the same blocks: one workgroup of 2G waves
+// would need more registers per lane than 2G > 8 waves of a CU can hold. The diagonal block is attended first,
 // then the selected blocks in list order (the online softmax does not depend on the order).
 // For each block (64 keys):
 //   * K (row-major, padded) and V (transposed, [dim][key], padded) are staged in LDS by the
@@ -214,6 +216,8 @@ constexpr int kVBuf = kD * kVPitch;    // bf16 elements of one staged V^T block
 
 template <int G>
 __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
+  // G here is the heads of one workgroup; a group of more heads is split over gridDim.z
+  // workgroups of G heads (the last may hold fewer: its other waves stage and wait only)
   // two staging buffers: block i is read from buffer i%2 while block i+1 is written to the other,
   // so one barrier per block separates the two
   __shared__ __align__(16) uint16_t sK[2 * kKBuf];
@@ -224,7 +228,10 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
   const int i0 = tau * kP;
   const int rows_valid = min(kP, a.T - i0);
   const int diag = a.past_len / kP + tau;
-  const int qhead = g * G + h;
+  const int group = a.Hq / a.Hkv;
+  const int h0 = blockIdx.z * G;
+  const bool head_ok = h0 + h < group;                  // uniform per wave
+  const int qhead = g * group + min(h0 + h, group - 1);
 
   PrefillWave<G> wv;
   PrefillBlockLoader<G> ld;
@@ -281,7 +288,7 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
     int buf = 0;
     bool diag_block = e < 0;
     for (;;) {
-      wv.step(sK + buf * kKBuf, sV + buf * kVBuf, diag_block);
+      if (head_ok) wv.step(sK + buf * kKBuf, sV + buf * kVBuf, diag_block);
       if (e2 > a.k) break;
       ld.store(sK + (buf ^ 1) * kKBuf, sV + (buf ^ 1) * kVBuf, tid, kP);
       int pe3 = -1;
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
 
   // ---- normalise and write: lane (n, c) holds dims 32dt + 8(i/4) + 4c + (i%4) of its row
   const float ltot = wv.l + __shfl_xor(wv.l, 32);
-  if (!row_ok) return;
+  if (!row_ok || !head_ok) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((long long)(i0 + wv.il) * a.Hq + qhead) * kD;
 #pragma unroll
@@ -315,18 +322,18 @@ __global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st) {
+  // groups of up to 4 heads take one workgroup; wider groups are split over two workgroups of
+  // ceil(G / 2) heads, so that no instance needs more than 512 threads (and their registers)
   const int G = a.Hq / a.Hkv;
-  const dim3 grid((a.T + kP - 1) / kP, a.Hkv);
-  if (log_enabled()) log_launch("k_attend_prefill", grid, 128 * G, 0, "G=%d, k=%d", G, a.k);
-  switch (G) {
+  const int nsplit = G > 4 ? 2 : 1;
+  const int hw = (G + nsplit - 1) / nsplit;
+  const dim3 grid((a.T + kP - 1) / kP, a.Hkv, nsplit);
+  if (log_enabled()) log_launch("k_attend_prefill", grid, 128 * hw, 0, "G=%d, heads per workgroup=%d, k=%d", G, hw, a.k);
+  switch (hw) {
     case 1: k_attend_prefill<1><<<grid, 128, 0, st>>>(a); break;
     case 2: k_attend_prefill<2><<<grid, 256, 0, st>>>(a); break;
     case 3: k_attend_prefill<3><<<grid, 384, 0, st>>>(a); break;
     case 4: k_attend_prefill<4><<<grid, 512, 0, st>>>(a); break;
-    case 5: k_attend_prefill<5><<<grid, 640, 0, st>>>(a); break;
-    case 6: k_attend_prefill<6><<<grid, 768, 0, st>>>(a); break;
-    case 7: k_attend_prefill<7><<<grid, 896, 0, st>>>(a); break;
-    case 8: k_attend_prefill<8><<<grid, 1024, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
