@@ -418,10 +418,10 @@ template <int G>
 hipError_t launch_fused_g(const FusedArgs& f, hipStream_t st) {
   const AttendArgs& a = f.att;
   const dim3 grid(a.nsplit, a.Hkv, a.B);
-  if (log_enabled())
-    log_launch("k_decode_select_attend", grid, kFT, 0, "G=%d, blocks in flight %d", G, a.blocks_per_split >= 4 ? 4 : 2);
-  if (a.blocks_per_split >= 4) k_decode_select_attend<G, 4><<<grid, kFT, 0, st>>>(f);
-  else k_decode_select_attend<G, 2><<<grid, kFT, 0, st>>>(f);
+  // two blocks in flight per wave, looping over the split's blocks: four measured no faster at
+  // G <= 5 and, beyond 256 registers per lane at G >= 6 (one workgroup per CU), ~20 % slower
+  if (log_enabled()) log_launch("k_decode_select_attend", grid, kFT, 0, "G=%d, blocks in flight %d", G, 2);
+  k_decode_select_attend<G, 2><<<grid, kFT, 0, st>>>(f);
   return hipGetLastError();
 }
 
