@@ -214,8 +214,11 @@ struct PrefillWave {
 constexpr int kKBuf = kP * kKPitch;    // bf16 elements of one staged K block
 constexpr int kVBuf = kD * kVPitch;    // bf16 elements of one staged V^T block
 
+// G = 2 (four waves) is held to 256 registers per lane so that two workgroups share a CU, two
+// waves per SIMD (unbounded, the compiler took 312 and one workgroup per CU ran 40 % slower);
+// G = 3 at three waves per SIMD would spill, and G = 4 runs two per SIMD within its own bound
 template <int G>
-__global__ void __launch_bounds__(128 * G) k_attend_prefill(PrefillArgs a) {
+__global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(PrefillArgs a) {
   // G here is the heads of one workgroup; a group of more heads is split over gridDim.z
   // workgroups of G heads (the last may hold fewer: its other waves stage and wait only)
   // two staging buffers: block i is read from buffer i%2 while block i+1 is written to the other,
