@@ -322,7 +322,6 @@ def main():
     # algorithmic bytes of one scoring launch: summaries + block-table entries read, scores written
     score_bytes = nb_tot * Hkv * D * 4 + nb_tot * 4 + nb_tot * Hkv * 4 + B * Hq * D * elem
     kv_gbps = kv_bytes / t_att / 1e9
-    hbm_gbps = hbm_bytes / t_att / 1e9
     step_bytes = score_bytes + kv_bytes + 2 * B * Hq * D * elem + B * Hkv * k * 4
     working_set = L * step_bytes   # what the rotation of the timed steps reads, in distinct bytes
     score_gbps = score_bytes / t_score / 1e9

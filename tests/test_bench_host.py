@@ -103,3 +103,32 @@ def test_exact_steps_and_warmup(monkeypatch, steps, warmup):
     assert len(timed) == steps
     assert max(int(e[len("replay"):]) for e in log if e.startswith("replay")) <= bench.GRAPH_MAX_STEPS
     assert t == pytest.approx(1e-3 / steps)
+
+
+def _undefined_globals(path):
+    """(function, name) for every name a function reads as a global that the module never binds
+    and that is not a builtin: the mistakes only a run of that function would otherwise show"""
+    import builtins
+    import symtable
+    top = symtable.symtable(open(path).read(), path, "exec")
+    bound = {s.get_name() for s in top.get_symbols() if s.is_assigned() or s.is_imported() or s.is_namespace()}
+    bad = []
+
+    def walk(t):
+        for ch in t.get_children():
+            for s in ch.get_symbols():
+                name = s.get_name()
+                if s.is_referenced() and s.is_global() and name not in bound and not hasattr(builtins, name):
+                    bad.append((ch.get_name(), name))
+            walk(ch)
+    walk(top)
+    return bad
+
+
+@pytest.mark.parametrize("rel", ["bench.py", "__graft_entry__.py", "long_context_sparse_select_amd/__init__.py",
+                                 "long_context_sparse_select_amd/_lib.py"])
+def test_no_undefined_globals(rel):
+    """bench.py's GPU paths (and the build / binding modules) never run on the CPU: a name read
+    before it is bound anywhere would only surface as a NameError on the GPU"""
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), rel)
+    assert _undefined_globals(path) == []
