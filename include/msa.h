@@ -234,7 +234,10 @@ msa_status msa_decode_step_noalloc(const msa_config* cfg, const void* q, const m
  *              block, then -1 padding)
  *   scores_out nullable [ceil(T/64)][Hkv][past_len/64 + ceil(T/64)] float32, -inf for
  *              non-candidates
- * cache->seq_lens is not read or written. */
+ * cache->seq_lens is not read or written. A short chunk (fewer than 256 (tile, group) attend
+ * workgroups) splits each tile's list over several workgroups and merges their partial softmax
+ * states in a second launch; msa_workspace_size(MSA_OP_PREFILL) then includes T * Hq * splits
+ * partials of 130 floats, and the outputs equal the unsplit ones up to fp32 summation order. */
 msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k_new,
                              const void* v_new, const msa_kv_cache* cache, int32_t past_len,
                              int32_t T, int32_t* idx_out, float* scores_out, void* out,

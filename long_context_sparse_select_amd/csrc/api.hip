@@ -111,6 +111,12 @@ Layout prefill_layout(const msa_config* c, int max_len, int T) {
   L.scores = off; off += align256(rows * (size_t)(L.row_stride > 0 ? L.row_stride : 1) * sizeof(float));
   L.qtile = off;  off += align256(rows * (size_t)kD * sizeof(float));
   L.idx = off;    off += align256(rows * (size_t)(k + 1) * sizeof(int32_t));
+  L.nsplit = prefill_splits(T, c->num_q_heads, Hkv, k);   // split-K of short chunks' lists
+  if (L.nsplit > 1) {
+    const size_t units = (size_t)T * c->num_q_heads * L.nsplit;
+    L.part_o = off;  off += align256(units * kD * sizeof(float));
+    L.part_ml = off; off += align256(units * 2 * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -325,9 +331,11 @@ msa_status scratch_of_current_device(void** ptr) {
   return MSA_OK;
 }
 
-// Step 2 of a prefill chunk on validated arguments
+// Step 2 of a prefill chunk on validated arguments; nsplit > 1: the lists split over that many
+// workgroups, whose partials (part_o, part_ml) a merge launch combines
 msa_status run_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int past_len, int T,
-                              const int32_t* idx, void* out, float* lse, hipStream_t st) {
+                              const int32_t* idx, void* out, float* lse, int nsplit, float* part_o, float* part_ml,
+                              hipStream_t st) {
   PrefillArgs p{};
   p.q = q;
   p.kpool = cache->k_pages;
@@ -343,6 +351,9 @@ msa_status run_prefill_attend(const msa_config* cfg, const void* q, const msa_kv
   p.scale_log2 = cfg->softmax_scale * kLog2e;
   p.out = out;
   p.lse = lse;
+  p.nsplit = nsplit;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
   return hip_status(launch_attend_prefill(p, st));
 }
 
@@ -517,7 +528,8 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
   MSA_TRY(prefill_check("msa_prefill_chunk", cache, max_len, st));
   log_call("msa_prefill_chunk: past_len %d, T %d (%d tiles), %d q / %d kv heads, top_k %d; row stride %d; "
-           "workspace %zu of %zu B", past_len, T, ntiles, Hq, Hkv, cfg->top_k, L.row_stride, L.total, workspace_bytes);
+           "%d list split(s); workspace %zu of %zu B", past_len, T, ntiles, Hq, Hkv, cfg->top_k, L.row_stride, L.nsplit,
+           L.total, workspace_bytes);
 
   MSA_TRY(hip_status(launch_prefill_prologue(true, ca, k_new, v_new, q, past_blocks, T, Hq, Hkv, qtile, st)));
   MSA_TRY(hip_status(launch_score_prefill(qtile, ca, past_blocks, ntiles, Hkv, scores, L.row_stride, st)));
@@ -536,7 +548,9 @@ msa_status msa_prefill_chunk(const msa_config* cfg, const void* q, const void* k
   t.keep_sink = cfg->keep_sink;
   t.keep_local = cfg->keep_local;
   MSA_TRY(hip_status(launch_topk(t, st)));
-  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, st);
+  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, L.nsplit,
+                            L.nsplit > 1 ? at<float>(workspace, L.part_o) : nullptr,
+                            L.nsplit > 1 ? at<float>(workspace, L.part_ml) : nullptr, st);
 }
 
 msa_status msa_prefill_attend(const msa_config* cfg, const void* q, const msa_kv_cache* cache, int32_t past_len,
@@ -553,7 +567,7 @@ msa_status msa_prefill_attend(const msa_config* cfg, const void* q, const msa_kv
   MSA_TRY(prefill_check("msa_prefill_attend", cache, past_len + T, (hipStream_t)stream));
   log_call("msa_prefill_attend: past_len %d, T %d, %d q / %d kv heads, top_k %d", past_len, T, cfg->num_q_heads,
            cfg->num_kv_heads, cfg->top_k);
-  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, (hipStream_t)stream);
+  return run_prefill_attend(cfg, q, cache, past_len, T, idx, out, lse_out, 1, nullptr, nullptr, (hipStream_t)stream);
 }
 
 const char* msa_status_string(msa_status status) {

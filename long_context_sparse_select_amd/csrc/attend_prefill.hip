@@ -27,6 +27,8 @@
 // The kernel is bound by LDS fragment reads (each 32-row wave reads the whole K and V^T block:
 // 1 KiB of LDS per 32 KFLOP of MFMA), not by HBM; the fragment reads are issued four MFMAs
 // ahead, and the first V^T fragments are requested before the softmax.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -219,8 +221,9 @@ constexpr int kVBuf = kD * kVPitch;    // bf16 elements of one staged V^T block
 // G = 3 at three waves per SIMD would spill, and G = 4 runs two per SIMD within its own bound
 template <int G>
 __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(PrefillArgs a) {
-  // G here is the heads of one workgroup; a group of more heads is split over gridDim.z
-  // workgroups of G heads (the last may hold fewer: its other waves stage and wait only)
+  // G here is the heads of one workgroup; a group of more heads is split over hsplit workgroups
+  // of G heads (the last may hold fewer: its other waves stage and wait only); with a.nsplit > 1
+  // the tile's list is split too (gridDim.z = hsplit * a.nsplit)
   // two staging buffers: block i is read from buffer i%2 while block i+1 is written to the other,
   // so one barrier per block separates the two
   __shared__ __align__(16) uint16_t sK[2 * kKBuf];
@@ -232,7 +235,9 @@ __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(Pref
   const int rows_valid = min(kP, a.T - i0);
   const int diag = a.past_len / kP + tau;
   const int group = a.Hq / a.Hkv;
-  const int h0 = blockIdx.z * G;
+  const int hsplit = (group + G - 1) / G;
+  const int hs = (int)blockIdx.z % hsplit, ks = (int)blockIdx.z / hsplit;
+  const int h0 = hs * G;
   const bool head_ok = h0 + h < group;                  // uniform per wave
   const int qhead = g * group + min(h0 + h, group - 1);
 
@@ -261,10 +266,13 @@ __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(Pref
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.kpool);
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.vpool);
   auto block_head = [&](int page) { return ((long long)page * a.Hkv + g) * kP * kD; };
-  // selected entries: indices below the diagonal with a valid page (the list also holds the
+  // Split ks of a.nsplit attends the list slots [e_lo, e_hi) and, the first one, the diagonal
+  // block. Selected entries: indices below the diagonal with a valid page (the list also holds the
   // diagonal itself and -1 padding, both skipped here)
+  const int per = (a.k + a.nsplit) / a.nsplit;    // ceil((k + 1) / nsplit)
+  const int e_lo = min(a.k + 1, ks * per), e_hi = min(a.k + 1, e_lo + per);
   auto next_valid = [&](int e, int* page) -> int {
-    for (; e <= a.k; ++e) {
+    for (; e < e_hi; ++e) {
       const int j = ids[e];
       if (j < 0 || j >= diag) continue;
       const int p = a.table[j];
@@ -277,26 +285,27 @@ __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(Pref
   // not depend on the order. The loop stages block i+1 into one LDS buffer while block i is read
   // from the other, with the loads of block i+2 in flight: one barrier per block.
   const int pdiag = a.table[diag];
+  const bool with_diag = ks == 0 && page_ok(pdiag, a.num_pages);
   int pe = -1;
-  int e;                                           // list position of the staged block; -1 = diagonal
-  if (page_ok(pdiag, a.num_pages)) { e = -1; pe = pdiag; }
-  else e = next_valid(0, &pe);
-  if (e <= a.k) {
+  int e;                                           // list position of the staged block; e_lo - 1 = diagonal
+  if (with_diag) { e = e_lo - 1; pe = pdiag; }
+  else e = next_valid(e_lo, &pe);
+  if (e < e_hi) {
     ld.load(kpool + block_head(pe), vpool + block_head(pe), tid);
-    ld.store(sK, sV, tid, e < 0 ? rows_valid : kP);
+    ld.store(sK, sV, tid, with_diag ? rows_valid : kP);
     int pe2 = -1;
     int e2 = next_valid(e + 1, &pe2);
-    if (e2 <= a.k) ld.load(kpool + block_head(pe2), vpool + block_head(pe2), tid);
+    if (e2 < e_hi) ld.load(kpool + block_head(pe2), vpool + block_head(pe2), tid);
     __syncthreads();
     int buf = 0;
-    bool diag_block = e < 0;
+    bool diag_block = with_diag;
     for (;;) {
       if (head_ok) wv.step(sK + buf * kKBuf, sV + buf * kVBuf, diag_block);
-      if (e2 > a.k) break;
+      if (e2 >= e_hi) break;
       ld.store(sK + (buf ^ 1) * kKBuf, sV + (buf ^ 1) * kVBuf, tid, kP);
       int pe3 = -1;
       const int e3 = next_valid(e2 + 1, &pe3);
-      if (e3 <= a.k) ld.load(kpool + block_head(pe3), vpool + block_head(pe3), tid);
+      if (e3 < e_hi) ld.load(kpool + block_head(pe3), vpool + block_head(pe3), tid);
       e2 = e3;
       buf ^= 1;
       diag_block = false;
@@ -307,8 +316,24 @@ __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(Pref
   // ---- normalise and write: lane (n, c) holds dims 32dt + 8(i/4) + 4c + (i%4) of its row
   const float ltot = wv.l + __shfl_xor(wv.l, 32);
   if (!row_ok || !head_ok) return;
+  const long long orow_i = (long long)(i0 + wv.il) * a.Hq + qhead;
+  if (a.nsplit > 1) {   // split-K partial: O and l relative to the reference max m (log2 domain)
+    const long long unit = orow_i * a.nsplit + ks;
+    float* po = a.part_o + unit * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * i4 + 4 * wv.c) =
+            make_float4(wv.o[dt][4 * i4 + 0], wv.o[dt][4 * i4 + 1], wv.o[dt][4 * i4 + 2], wv.o[dt][4 * i4 + 3]);
+    if (wv.c == 0) {
+      a.part_ml[unit * 2] = wv.m;
+      a.part_ml[unit * 2 + 1] = ltot;
+    }
+    return;
+  }
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((long long)(i0 + wv.il) * a.Hq + qhead) * kD;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + orow_i * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -319,19 +344,72 @@ __global__ void __launch_bounds__(128 * G, G == 2 ? 2 : 1) k_attend_prefill(Pref
       *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * wv.c) = pk;
     }
   if (a.lse != nullptr && wv.c == 0)
-    a.lse[(long long)(i0 + wv.il) * a.Hq + qhead] = ltot > 0.f ? (wv.m + log2f(ltot)) * kLn2 : -INFINITY;
+    a.lse[orow_i] = ltot > 0.f ? (wv.m + log2f(ltot)) * kLn2 : -INFINITY;
+}
+
+// Log-sum-exp merge of the list splits of every (token, head) row of a split prefill chunk:
+// 32 lanes per row (4 of its 128 dims each), 8 rows per workgroup. Split s of a row holds O_s and
+// l_s relative to its own reference m_s (m_s = -inf: the split attended nothing); with
+// M = max_s m_s, the row's O = sum_s 2^(m_s - M) O_s, l = sum_s 2^(m_s - M) l_s, out = O / l and
+// lse = (M + log2 l) ln 2.
+__global__ void __launch_bounds__(256) k_merge_prefill(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml, int rows, int ns,
+                                                       uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int l32 = threadIdx.x & 31;
+  const long long row = (long long)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row * ns;
+  const float4* po = reinterpret_cast<const float4*>(part_o + row * ns * kD) + l32;   // split s at + 32 s
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) {
+    const float2 v = ml[s];
+    const float4 o = po[32 * s];
+    const float wgt = rescale(v.x, M);   // 0 for a split that attended nothing
+    L = fmaf(v.y, wgt, L);
+    acc.x = fmaf(o.x, wgt, acc.x); acc.y = fmaf(o.y, wgt, acc.y);
+    acc.z = fmaf(o.z, wgt, acc.z); acc.w = fmaf(o.w, wgt, acc.w);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<uint2*>(out + row * kD + 4 * l32) =
+      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  if (lse != nullptr && l32 == 0) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
+int prefill_splits(int T, int Hq, int Hkv, int k) {
+  const int hsplit = Hq / Hkv > 4 ? 2 : 1;
+  const long long units = (long long)((T + kP - 1) / kP) * Hkv * hsplit;
+  if (units >= kPrefillSplitTarget) return 1;
+  const int s = (int)((kPrefillSplitTarget + units - 1) / units);
+  return std::max(1, std::min({s, (k + 1) / 2, kMaxDecodeSplit}));
+}
+
+hipError_t launch_merge_prefill(const PrefillArgs& a, hipStream_t st) {
+  const int rows = a.T * a.Hq;
+  const dim3 grid((rows + 7) / 8);
+  if (log_enabled()) log_launch("k_merge_prefill", grid, 256, 0, "%d rows x %d splits", rows, a.nsplit);
+  k_merge_prefill<<<grid, 256, 0, st>>>(a.part_o, a.part_ml, rows, a.nsplit, reinterpret_cast<uint16_t*>(a.out),
+                                        a.lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st) {
   // groups of up to 4 heads take one workgroup; wider groups are split over two workgroups of
-  // ceil(G / 2) heads, so that no instance needs more than 512 threads (and their registers)
+  // ceil(G / 2) heads, so that no instance needs more than 512 threads (and their registers);
+  // a.nsplit > 1 splits every tile's list over that many workgroups as well
   const int G = a.Hq / a.Hkv;
-  const int nsplit = G > 4 ? 2 : 1;
-  const int hw = (G + nsplit - 1) / nsplit;
-  const dim3 grid((a.T + kP - 1) / kP, a.Hkv, nsplit);
-  if (log_enabled()) log_launch("k_attend_prefill", grid, 128 * hw, 0, "G=%d, heads per workgroup=%d, k=%d", G, hw, a.k);
+  const int hsplit = G > 4 ? 2 : 1;
+  const int hw = (G + hsplit - 1) / hsplit;
+  if (a.nsplit < 1 || (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr))) return hipErrorInvalidValue;
+  const dim3 grid((a.T + kP - 1) / kP, a.Hkv, hsplit * a.nsplit);
+  if (log_enabled())
+    log_launch("k_attend_prefill", grid, 128 * hw, 0, "G=%d, heads per workgroup=%d, list splits=%d, k=%d", G, hw,
+               a.nsplit, a.k);
   switch (hw) {
     case 1: k_attend_prefill<1><<<grid, 128, 0, st>>>(a); break;
     case 2: k_attend_prefill<2><<<grid, 256, 0, st>>>(a); break;
@@ -339,7 +417,9 @@ hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st) {
     case 4: k_attend_prefill<4><<<grid, 512, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.nsplit == 1) return err;
+  return launch_merge_prefill(a, st);
 }
 
 }  // namespace msa

@@ -149,7 +149,16 @@ struct PrefillArgs {
   float scale_log2;
   void* out;            // [T][Hq][128] bf16
   float* lse;           // nullable [T][Hq]
+  int nsplit;           // workgroups per (tile, group) list: 1 writes out / lse; more write partials
+  float* part_o;        // [T][Hq][nsplit][128]: O relative to the split's reference max (nsplit > 1)
+  float* part_ml;       // [T][Hq][nsplit][2]: that max (log2 domain) and the split's sum l
 };
+// Short chunks leave the chip idle with one workgroup per (tile, group): their lists are split
+// so that about kPrefillSplitTarget workgroups run (at least two list slots each), and a second
+// launch merges the partials of every (token, head) row.
+constexpr int kPrefillSplitTarget = 256;
+int prefill_splits(int T, int Hq, int Hkv, int k);
+// the attend launch, then (a.nsplit > 1) the merge launch
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t st);
 
 }  // namespace msa

@@ -80,6 +80,32 @@ def test_workspace_sizes():
     assert ws_size(c, 17)[0] == L.MSA_ERR_INVALID_ARG
 
 
+def _prefill_base(Hq, Hkv, k, max_len, T):
+    """the unsplit prefill workspace: scores, tile queries and lists (256-aligned arrays)"""
+    a = lambda x: (x + 255) // 256 * 256
+    rows = (T + 63) // 64 * Hkv
+    return a(rows * ((max_len + 63) // 64) * 4) + a(rows * 128 * 4) + a(rows * (k + 1) * 4)
+
+
+@pytest.mark.parametrize("Hq,Hkv,k,T", [(32, 8, 32, 4096), (32, 8, 32, 2048), (32, 8, 32, 1024), (32, 8, 32, 512),
+                                        (32, 8, 32, 64), (64, 8, 32, 1024), (64, 8, 32, 2048), (8, 1, 64, 300),
+                                        (32, 8, 1, 64), (32, 8, 2, 64), (32, 8, 3, 64), (4, 4, 4096, 64)])
+def test_prefill_split_workspace(Hq, Hkv, k, T):
+    """Short chunks split every tile's list over several workgroups so that about 256 workgroups
+    run (1 when (tiles x groups x head splits) already reaches 256), at least two list slots per
+    split and at most 256 splits; the workspace then also holds T * Hq * splits partials of
+    128 + 2 floats."""
+    hsplit = 2 if Hq // Hkv > 4 else 1
+    units = (T + 63) // 64 * Hkv * hsplit
+    want = 1 if units >= 256 else max(1, min(-(-256 // units), (k + 1) // 2, 256))
+    max_len = 262144 + T
+    st, pre = ws_size(cfg(num_q_heads=Hq, num_kv_heads=Hkv, top_k=k), L.MSA_OP_PREFILL, 1, max_len, T)
+    assert st == 0
+    a = lambda x: (x + 255) // 256 * 256
+    extra = 0 if want == 1 else a(T * Hq * want * 128 * 4) + a(T * Hq * want * 2 * 4)
+    assert pre == _prefill_base(Hq, Hkv, k, max_len, T) + extra
+
+
 @pytest.mark.parametrize("B,Hq,Hkv", [(1, 8, 1), (1, 4, 2), (1, 32, 8), (2, 8, 1), (3, 16, 8), (8, 32, 8),
                                       (31, 32, 8), (32, 32, 8), (300, 8, 1)])
 def test_attend_splits_fit_one_merge_workgroup(B, Hq, Hkv):

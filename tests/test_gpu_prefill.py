@@ -126,6 +126,10 @@ SMALL = [
     ("past4096_T256_g8", dict(Hq=8, Hkv=1, past_len=4096, T=256, top_k=16)),
     ("past128_T1_g1", dict(Hq=4, Hkv=4, past_len=128, T=1, top_k=2)),
     ("past2048_T300_g2_bigk", dict(Hq=4, Hkv=2, past_len=2048, T=300, top_k=40)),
+    # short chunks on long caches: each tile's list split over several workgroups (4 and 4, the
+    # second with the group's 8 heads over two workgroups as well), partials merged
+    ("past65536_T512_g4_split", dict(Hq=32, Hkv=8, past_len=65536, T=512, top_k=32)),
+    ("past8192_T200_g8_split", dict(Hq=64, Hkv=8, past_len=8192, T=200, top_k=24)),
 ]
 
 
