@@ -7,10 +7,13 @@
 // tile's diagonal block is always attended, causally (key position <= query position).
 //
 // One workgroup per (tile, KV group): rows = 64 tokens x G heads (256 for G = 4), 2G waves of
-// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). A group of more than 4 heads is split over
-// two workgroups of ceil(G/2) heads each, which stage the same blocks: one workgroup of 2G waves
-// would need more registers per lane than 2G > 8 waves of a CU can hold. The diagonal block is attended first,
-// then the selected blocks in list order (the online softmax does not depend on the order).
+// 32 rows (wave w -> head w/2, tokens 32*(w%2) .. +31). A group of more than 4 heads is split
+// over two workgroups of ceil(G/2) heads each, which stage the same blocks: one workgroup of
+// 2G > 8 waves would need more registers per lane than a CU holds for them. A short chunk also
+// splits each tile's list over several workgroups (too few (tile, group) pairs to fill the chip),
+// which write partial softmax states that k_merge_prefill combines. The diagonal block is
+// attended first, then the selected blocks in list order (the online softmax does not depend on
+// the order).
 // For each block (64 keys):
 //   * K (row-major, padded) and V (transposed, [dim][key], padded) are staged in LDS by the
 //     whole workgroup into one of two buffers while the other is read; the loads of the block
@@ -24,9 +27,12 @@
 //   * online softmax in the log2 domain, fp32 statistics, fp32 accumulation in the MFMA; the
 //     reference max moves only when a row's max outgrows it by 2^8, so the O rescale is rare;
 //     the causal mask is a branch taken on the diagonal block only.
-// The kernel is bound by LDS fragment reads (each 32-row wave reads the whole K and V^T block:
-// 1 KiB of LDS per 32 KFLOP of MFMA), not by HBM; the fragment reads are issued four MFMAs
-// ahead, and the first V^T fragments are requested before the softmax.
+// At the roofline the kernel is bound by HBM: at k = 32 each (tile, group) streams 33 blocks of
+// K and V for ~250 FLOP per byte, under the chip's ridge. It runs well below that floor, limited
+// on chip: each 32-row wave reads the whole K and V^T block from LDS (1 KiB per 32 KFLOP of
+// MFMA), and the two waves of a SIMD meet the same barrier, so MFMA, LDS and softmax phases add
+// up. The fragment reads are issued four MFMAs ahead, and the first V^T fragments are requested
+// before the softmax.
 #include <algorithm>
 
 #include "common.h"
