@@ -308,6 +308,7 @@ __device__ __forceinline__ void write_ordered(const SelectShared& sh, int keff, 
   for (int e = max(e0, keff) + tid; e < e1; e += kFT) out[e] = -1;
 }
 
+// G: heads per group; U: blocks whose K/V loads each wave keeps in flight (the launcher uses 2)
 template <int G, int U>
 __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   const AttendArgs& a = f.att;
