@@ -4,10 +4,10 @@
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
 //   msa_decode_step   [append: new K/V row, that block's summary and score | score] (one launch) -> top-k
-//                     -> attend -> split-K merge; for bf16, k <= 256 and no forced blocks:
-//                     [append | score + chunk maxima] -> select-and-attend -> split-K merge
+//                     -> attend -> split-K merge; for bf16, k <= 64 and rows split over several
+//                     workgroups: [append | score + chunk maxima] -> select-and-attend -> split-K merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
-//                     -> attend
+//                     -> attend (-> merge of the list splits, for short chunks)
 //   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
 //   msa_decode_step_noalloc  msa_decode_step's launches with a file-scope device array as the workspace
 // Everything is enqueued on the caller's stream; nothing is allocated; validation precedes any
@@ -37,11 +37,10 @@ struct Layout {
   bool fused = false;   // decode step: Step 1's TopK inside the attend launch
 };
 
-// A bf16 decode step without forced blocks, k <= kMaxFusedTopK and rows of at most
+// A bf16 decode step with k <= kMaxFusedTopK and rows of at most
 // kMaxFusedChunks chunks selects inside its attend launch (launch_decode_select_attend).
 bool fused_decode(const msa_config* c, int row_stride) {
-  return c->q_dtype == MSA_BF16 && c->keep_sink == 0 && c->keep_local == 0 && c->top_k <= kMaxFusedTopK &&
-         row_stride <= kMaxFusedChunks * kScoreChunk;
+  return c->q_dtype == MSA_BF16 && c->top_k <= kMaxFusedTopK && row_stride <= kMaxFusedChunks * kScoreChunk;
 }
 
 // any_mode: the entry point does not read score_mode (msa_select_index)
@@ -296,6 +295,8 @@ msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
     f.scores = scores;
     f.row_stride = L.row_stride;
     f.cmax = cmax;
+    f.keep_sink = cfg->keep_sink;
+    f.keep_local = cfg->keep_local;
     f.cstride = L.cstride;
     f.idx_out = idx_out;
     return hip_status(launch_decode_select_attend(f, st));

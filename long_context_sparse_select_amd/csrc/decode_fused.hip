@@ -81,22 +81,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 
 // Exact selection straight from the row's scores (mass ties): T = the k_eff-th largest key by a
 // bitwise search, then the keys > T and the first ties == T, in ascending order, into sh.sorted.
-__device__ __forceinline__ void select_exact(const float* srow, const int32_t* trow, int n, int keff, SelectShared& sh) {
+template <bool FORCED>
+__device__ __forceinline__ void select_exact(const float* srow, const int32_t* trow, int n, int keff, int sink,
+                                             int local, SelectShared& sh) {
+  auto key_of = [&](int j) { return FORCED ? forced_or_key(j, n, sink, local, srow[j]) : order_key(srow[j]); };
   const int tid = threadIdx.x;
   uint32_t T = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
-    for (int j = tid; j < n; j += kFT) c += order_key(srow[j]) >= cand;
+    for (int j = tid; j < n; j += kFT) c += key_of(j) >= cand;
     if (block_sum<kFT>(c, sh.tmp) >= keff) T = cand;
   }
   int gt = 0;
-  for (int j = tid; j < n; j += kFT) gt += order_key(srow[j]) > T;
+  for (int j = tid; j < n; j += kFT) gt += key_of(j) > T;
   const int need_eq = keff - block_sum<kFT>(gt, sh.tmp);
   int run_eq = 0, run_sel = 0;
   for (int base = 0; base < n; base += kFT) {
     const int j = base + tid;
-    const uint32_t key = j < n ? order_key(srow[j]) : 0u;
+    const uint32_t key = j < n ? key_of(j) : 0u;
     const bool is_gt = j < n && key > T;
     const bool is_eq = j < n && key == T;
     int tot_eq, tot_sel;
@@ -115,8 +118,10 @@ __device__ __forceinline__ void select_exact(const float* srow, const int32_t* t
 // padded with INT_MAX up to kMaxFusedTopK), false when they are in sh.sorted / sh.sortedpg in
 // ascending order (every block kept, or the exact path). All threads call it; it ends with a
 // barrier.
+// FORCED: the first `sink` and last `local` blocks of the row are kept whatever their scores
+template <bool FORCED>
 __device__ __forceinline__ bool select_row(const float* srow, const float* crow, const int32_t* trow, int n, int keff,
-                           SelectShared& sh) {
+                                           int sink, int local, SelectShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (keff >= n) {   // every block is kept (uniform)
     for (int e = tid; e < n; e += kFT) { sh.sorted[e] = e; sh.sortedpg[e] = trow[e]; }
@@ -131,6 +136,8 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
     const int c = tid + kFT * i;
     cv[i] = c < nch;
     ck[i] = order_key(crow[min(c, nch - 1)]);
+    // a chunk holding a forced block has that block's key as its maximum
+    if (FORCED && (kScoreChunk * c < sink || (local > 0 && kScoreChunk * (c + 1) > n - local))) ck[i] = kForcedKey;
   }
   if (tid == 0) { sh.nsurv = 0; sh.ncand = 0; }
   if (tid < kFBins) sh.hist[tid] = 0u;
@@ -239,7 +246,7 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
       int tot = 0;
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
-        take[r] = jj[r] < n && order_key(v[r]) >= T0;
+        take[r] = jj[r] < n && (FORCED ? forced_or_key(jj[r], n, sink, local, v[r]) : order_key(v[r])) >= T0;
         bal[r] = __ballot(take[r]);
         tot += __popcll(bal[r]);
       }
@@ -252,7 +259,8 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
           const int p = run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[r] >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[r], 0u));
           if (take[r] && p < kCandCap) {
-            sh.comp[p] = ((unsigned long long)order_key(v[r]) << 32) | (uint32_t)(~(uint32_t)jj[r]);
+            const uint32_t key = FORCED ? forced_or_key(jj[r], n, sink, local, v[r]) : order_key(v[r]);
+            sh.comp[p] = ((unsigned long long)key << 32) | (uint32_t)(~(uint32_t)jj[r]);
             sh.comppg[p] = pg[r];
           }
           run += __popcll(bal[r]);
@@ -263,7 +271,7 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
     exact = sh.ncand > kCandCap;   // uniform
   }
   if (exact) {
-    select_exact(srow, trow, n, keff, sh);
+    select_exact<FORCED>(srow, trow, n, keff, sink, local, sh);
     return false;
   }
   const int m = sh.ncand;   // >= keff by the choice of T0
@@ -308,8 +316,9 @@ __device__ __forceinline__ void write_ordered(const SelectShared& sh, int keff, 
   for (int e = max(e0, keff) + tid; e < e1; e += kFT) out[e] = -1;
 }
 
-// G: heads per group; U: blocks whose K/V loads each wave keeps in flight (the launcher uses 2)
-template <int G, int U>
+// G: heads per group; U: blocks whose K/V loads each wave keeps in flight (the launcher uses 2);
+// FORCED: forced sink / local blocks (keep_sink or keep_local nonzero)
+template <int G, int U, bool FORCED>
 __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   const AttendArgs& a = f.att;
   __shared__ SelectShared sh;
@@ -355,7 +364,8 @@ __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   const int32_t* trow = a.table + (long long)b * a.max_blocks;
   bool by_rank = false;
   if (keff > 0 && e0 < keff)   // uniform: this split holds kept blocks
-    by_rank = select_row(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff, sh);
+    by_rank = select_row<FORCED>(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff,
+                                 f.keep_sink, f.keep_local, sh);
   // the blocks this split attends: ranks [e0, e1) (by_rank) or positions [e0, e1) of the ascending list
   const int* lst = by_rank ? sh.sel : sh.sorted;
   const int* lstpg = by_rank ? sh.selpg : sh.sortedpg;
@@ -422,7 +432,8 @@ hipError_t launch_fused_g(const FusedArgs& f, hipStream_t st) {
   // two blocks in flight per wave, looping over the split's blocks: four measured no faster at
   // G <= 5 and, beyond 256 registers per lane at G >= 6 (one workgroup per CU), ~20 % slower
   if (log_enabled()) log_launch("k_decode_select_attend", grid, kFT, 0, "G=%d, blocks in flight %d", G, 2);
-  k_decode_select_attend<G, 2><<<grid, kFT, 0, st>>>(f);
+  if (f.keep_sink > 0 || f.keep_local > 0) k_decode_select_attend<G, 2, true><<<grid, kFT, 0, st>>>(f);
+  else k_decode_select_attend<G, 2, false><<<grid, kFT, 0, st>>>(f);
   return hipGetLastError();
 }
 

@@ -124,8 +124,9 @@ hipError_t launch_merge_bf16(const AttendArgs& a, hipStream_t st);
 
 // ---- Steps 1 (TopK) and 2 of a bf16 decode step in one launch (then the merge when split):
 // every attend workgroup selects its row's top-k from the scores and chunk maxima of the scoring
-// launch and attends its split of the list. For k <= kMaxFusedTopK, no forced blocks and rows of
-// at most kMaxFusedChunks * kScoreChunk blocks.
+// launch and attends its split of the list. For k <= kMaxFusedTopK and rows of at most
+// kMaxFusedChunks * kScoreChunk blocks; forced sink / local blocks take a key above every score,
+// and so does the maximum of every chunk that holds one.
 constexpr int kMaxFusedTopK = 64;
 constexpr int kMaxFusedChunks = 1024;
 struct FusedArgs {
@@ -135,6 +136,7 @@ struct FusedArgs {
   const float* cmax;     // [B][Hkv][cstride]
   int cstride;
   int32_t* idx_out;      // nullable [B][Hkv][k]
+  int keep_sink, keep_local;   // forced blocks: the first / last of each row's blocks
 };
 hipError_t launch_decode_select_attend(const FusedArgs& f, hipStream_t st);
 

@@ -38,6 +38,14 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 constexpr uint32_t kPosInfKey = 0xff800000u;   // order_key(+inf)
+// A forced block's key sits above every order key (even a NaN's), so every selection path keeps
+// it; forced blocks tie among themselves and fit in k_eff, so all of them are kept.
+constexpr uint32_t kForcedKey = 0xffffffffu;
+// the selection key of block j of a row of n blocks: forced (the first `sink` or the last
+// `local` blocks) or the order key of its score
+__device__ __forceinline__ uint32_t forced_or_key(int j, int n, int sink, int local, float s) {
+  return (j < sink || j >= n - local) ? kForcedKey : order_key(s);
+}
 
 // block-wide integer sum (all threads get it); s_tmp holds NT/64 ints
 template <int NT>

@@ -54,12 +54,8 @@ struct TopkShared {
   int cnt;
 };
 
-// A forced block's key sits above every order key (even a NaN's), so every selection path keeps
-// it; forced blocks tie among themselves and fit in k_eff, so all of them are kept.
-constexpr uint32_t kForcedKey = 0xffffffffu;
-
 __device__ __forceinline__ uint32_t select_key(const TopkArgs& a, int j, int n, float s) {
-  return (j < a.keep_sink || j >= n - a.keep_local) ? kForcedKey : order_key(s);
+  return forced_or_key(j, n, a.keep_sink, a.keep_local, s);
 }
 
 __device__ __forceinline__ int page_of(const TopkArgs& a, int row, int j) {
