@@ -188,6 +188,7 @@ def main():
     ap.add_argument("--no-large-k", action="store_true", help="skip the 1M-token k=1024 operating-point line")
     ap.add_argument("--no-index", action="store_true", help="skip the 1M-token index-branch select line")
     ap.add_argument("--no-bf16-summaries", action="store_true", help="skip the 1M-token bf16 summary-pool line")
+    ap.add_argument("--no-forced", action="store_true", help="skip the 1M-token forced sink / local block line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--counters", action="store_true",
@@ -368,6 +369,8 @@ def main():
     if not args.no_bf16_summaries:
         rec["bf16_summaries"] = bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L,
                                                      R, rot)
+    if not args.no_forced:
+        rec["forced_blocks"] = bench_forced(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot)
     tr = recorded_traffic(score_bytes)
     if tr is not None:
         rec["roofline"]["traffic"] = tr["bytes_per_launch"]
@@ -691,6 +694,42 @@ def bench_large_k(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring,
             "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "kv_GBps": kv / t_att / 1e9,
             "kv_hbm_frac": kv / t_att / 1e9 / HBM_PEAK_GBPS, "bytes_per_attend": kv,
             "note": "the pages' ~6 % operating point (16,384 blocks, k = 1024); same caches as the headline"}
+
+
+def bench_forced(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot, sink=1, local=1):
+    """The 1M-token decode with forced blocks on the same rotated caches: the first (sink) and the
+    last (local, holding the new token) block of every row are always kept and count toward k.
+    Whole decode steps; every list is checked to hold the forced blocks."""
+    c0 = cases[0]
+    B, max_len = c0.B, c0.max_seq_len
+    cfg = msa.make_config(c0.Hq, c0.Hkv, c0.top_k, dtype=c0.dtype, softmax_scale=c0.scale)
+    cfg.keep_sink, cfg.keep_local = sink, local
+    dev = q_ring[0].device
+    out = torch.empty((B, c0.Hq, c0.D), dtype=q_ring[0].dtype, device=dev)
+    idx = [torch.empty((B, c0.Hkv, c0.top_k), dtype=torch.int32, device=dev) for _ in range(L)]
+    ws = torch.empty(msa.msa_workspace_size(cfg, msa.MSA_OP_DECODE, B, max_len), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    n_rep = 10
+    per_graph = rot * max(1, 32 // rot)   # whole rotations of the caches and queries
+
+    def step(i):
+        msa.msa_decode_step(cfg, q_ring[i % R], caches[i % L], B, max_len, out, k_new=kn_ring[i % R],
+                            v_new=vn_ring[i % R], idx_out=idx[i % L], workspace=ws)
+    g = timed_graph(step, per_graph, torch)
+    run_graph(g, 2, torch)
+    t_step = run_graph(g, n_rep, torch) / (per_graph * n_rep)
+    del g
+    torch.cuda.synchronize()
+    for l in range(L):
+        nb = (int(cases[l].seq_lens[0]) + 63) // 64
+        rows = idx[l].cpu().numpy().reshape(-1, c0.top_k)
+        forced = {j for j in range(nb) if j < sink or j >= nb - local}
+        if not all(forced <= set(r.tolist()) for r in rows):
+            raise RuntimeError("forced blocks missing from a decode list")
+    log("1M forced blocks (sink %d, local %d): step %.1f us (%.0f tokens/s)" % (sink, local, t_step * 1e6, B / t_step))
+    return {"workload": "decode_bf16_1m_paged", "keep_sink": sink, "keep_local": local, "step_us": t_step * 1e6,
+            "tokens_per_s": B / t_step,
+            "note": "the forced-block option on the headline's caches (same k = 64, the forced blocks among them)"}
 
 
 def bench_bf16_summaries(args, torch, np, msa, caches, cases, q_ring, kn_ring, vn_ring, L, R, rot):
