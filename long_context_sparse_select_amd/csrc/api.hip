@@ -4,8 +4,8 @@
 // Launch sequences ("MiniMax goes sparse: decoding M3's attention from a single diagram",
 // §1 Steps 1-2; §3 decode / prefill):
 //   msa_decode_step   [append: new K/V row, that block's summary and score | score] (one launch) -> top-k
-//                     -> attend -> split-K merge; for bf16, k <= 64 and rows split over several
-//                     workgroups: [append | score + chunk maxima] -> select-and-attend -> split-K merge
+//                     -> attend -> split-K merge; for bf16, k <= 256 on long rows, split over
+//                     several workgroups: [append | score + chunk maxima] -> select-and-attend -> merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend (-> merge of the list splits, for short chunks)
 //   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
@@ -37,10 +37,13 @@ struct Layout {
   bool fused = false;   // decode step: Step 1's TopK inside the attend launch
 };
 
-// A bf16 decode step with k <= kMaxFusedTopK and rows of at most
-// kMaxFusedChunks chunks selects inside its attend launch (launch_decode_select_attend).
+// A bf16 decode step with k <= kMaxFusedTopK and rows of at most kMaxFusedChunks chunks selects
+// inside its attend launch (launch_decode_select_attend); for k > 64 the rows must also hold at
+// least 2k chunks, so that the chunk-maximum bound leaves few candidates (1M tokens, k = 128:
+// 38.9 -> 35.0 us per step; k = 256: 52.2 -> 46.6 us).
 bool fused_decode(const msa_config* c, int row_stride) {
-  return c->q_dtype == MSA_BF16 && c->top_k <= kMaxFusedTopK && row_stride <= kMaxFusedChunks * kScoreChunk;
+  return c->q_dtype == MSA_BF16 && c->top_k <= kMaxFusedTopK && row_stride <= kMaxFusedChunks * kScoreChunk &&
+         (c->top_k <= 64 || row_stride >= 2 * kScoreChunk * c->top_k);
 }
 
 // any_mode: the entry point does not read score_mode (msa_select_index)

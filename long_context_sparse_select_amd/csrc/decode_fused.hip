@@ -48,8 +48,9 @@ constexpr int kCPer = kMaxFusedChunks / kFT;   // chunk maxima per thread (4)
 constexpr int kFBins = 256;
 constexpr int kSurvCap = 512;            // survivor chunks held
 // candidates ranked: a row with fewer chunks than k_eff has no chunk-maximum bound, and all its
-// n < kScoreChunk * k_eff scores are candidates, which this holds
-constexpr int kCandCap = kScoreChunk * kMaxFusedTopK;
+// n < kScoreChunk * k_eff scores are candidates, which this holds for k_eff <= 64; with at least
+// 2 k_eff chunks the bound leaves ~k_eff .. 2 k_eff candidates; more take the exact path
+constexpr int kCandCap = 1024;
 constexpr int kRounds = 8;               // survivor-chunk rounds (16 chunks each) with loads in flight
 
 struct SelectShared {

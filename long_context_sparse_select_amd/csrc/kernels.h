@@ -127,7 +127,7 @@ hipError_t launch_merge_bf16(const AttendArgs& a, hipStream_t st);
 // launch and attends its split of the list. For k <= kMaxFusedTopK and rows of at most
 // kMaxFusedChunks * kScoreChunk blocks; forced sink / local blocks take a key above every score,
 // and so does the maximum of every chunk that holds one.
-constexpr int kMaxFusedTopK = 64;
+constexpr int kMaxFusedTopK = 256;
 constexpr int kMaxFusedChunks = 1024;
 struct FusedArgs {
   AttendArgs att;        // idx / pages unused

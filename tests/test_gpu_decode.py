@@ -266,6 +266,21 @@ def test_full_size_decode_large_k():
     print("1M k=1024: %d rows differ from the oracle inside the band" % off)
 
 
+@pytest.mark.parametrize("B,n,k,sink,local", [(1, 1 << 20, 65, 0, 0), (1, 1 << 20, 256, 0, 0),
+                                              (2, 1 << 19, 128, 1, 1)])
+def test_full_size_decode_fused_large_k(B, n, k, sink, local):
+    """k from 65 to 256 on rows of at least 2k chunks of 16 blocks: Step 1's top-k runs inside the
+    attend launch (chunk-maximum bound, ~k .. 2k candidates ranked), with and without forced
+    blocks; the lists and outputs against the oracle."""
+    kw = dict(workload("decode_bf16_1m_paged", seed=0), B=B, lens=[n] * B, top_k=k)
+    c = make_decode_case_torch(**kw)
+    d = to_device(c)
+    d.cfg.keep_sink, d.cfg.keep_local = sink, local
+    res = run_decode(d)
+    off = full_decode_check(d, res)
+    print("B=%d n=%d k=%d: %d rows differ from the oracle inside the band" % (B, n, k, off))
+
+
 @pytest.mark.parametrize("k", [300, 1500])
 def test_large_k_all_scores_tied(k):
     """Every block scores exactly 0 (all keys zero): the kept blocks are the k smallest indices."""
