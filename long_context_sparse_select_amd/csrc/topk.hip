@@ -320,7 +320,10 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const int n = prefill ? a.base_blocks + row / a.Hkv : (clamp_len(len_raw, a.max_len) + kP - 1) / kP;
   const int keff = min(a.k, n);
   const int ngroups = min(n, NT);     // threads holding at least one candidate
-  const bool fast = n <= kMaxFast && keff < n && keff <= ngroups && keff <= kSmallK;   // uniform
+  // the group-maximum bound prunes well while k_eff is at most a quarter of the groups (a 2048-
+  // candidate row on 512 threads with k = 256 ran 53.5 us per 128k-token step this way, 40.4 us
+  // through the exact select)
+  const bool fast = n <= kMaxFast && keff < n && 4 * keff <= ngroups && keff <= kSmallK;   // uniform
   if (!fast) {   // every candidate kept, or the exact path
     if (keff == n) {
       for (int i = tid; i < n; i += NT) emit(a, row, i, i);
