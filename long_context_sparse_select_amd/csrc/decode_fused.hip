@@ -20,8 +20,10 @@
 //      not in that chunk's recorded maximum);
 //   2. the scores of the survivor chunks (typically ~k chunks, 64 B each) that are >= T0 are the
 //      candidates (>= k_eff of them, every tie of the k_eff-th score among them); each is ranked
-//      exactly by (key desc, index asc) against the others (one thread per candidate); ranks <
-//      k_eff are kept and placed in ascending block order by counting. A candidate's page id is
+//      exactly by (key desc, index asc) against the others (a quad of lanes per candidate); ranks
+//      < k_eff are kept and placed in ascending block order by counting. Forced sink / local
+//      blocks (the FORCED instance) take a key above every score, and so does the maximum of each
+//      chunk that holds one, so the bound keeps them. A candidate's page id is
 //      read in the same round trip as its score, so the attend's K/V loads follow directly;
 //   3. the workgroup attends the kept blocks of ranks [split * bps, (split + 1) * bps) with the
 //      MFMA attend of attend_mfma.h, and writes the output (one split) or its split partial for
@@ -29,8 +31,9 @@
 //      order (the number of kept blocks with a smaller index) is counted, and the blocks whose
 //      positions fall in the same range are written to the index list: the ordering is off the
 //      path to the first load.
-// Rows whose survivors or candidates overflow the LDS lists (mass ties) take an exact path: a
-// bitwise search for the k_eff-th key over the row's scores, then an ordered compaction.
+// Rows whose survivors or candidates overflow the LDS lists (mass ties, or too few chunks for
+// the bound to prune: the host fuses k > 64 only for rows of at least 2k chunks) take an exact
+// path: a bitwise search for the k_eff-th key over the row's scores, then an ordered compaction.
 // Reading the row per workgroup is redundant across a row's splits, but it is ~10 KiB of L2 hits
 // per workgroup instead of a launch and a 64 KiB single-CU round trip.
 #include "common.h"
