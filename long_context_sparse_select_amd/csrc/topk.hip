@@ -320,10 +320,12 @@ __global__ void __launch_bounds__(NT) k_topk(TopkArgs a) {
   const int n = prefill ? a.base_blocks + row / a.Hkv : (clamp_len(len_raw, a.max_len) + kP - 1) / kP;
   const int keff = min(a.k, n);
   const int ngroups = min(n, NT);     // threads holding at least one candidate
-  // the group-maximum bound prunes well while k_eff is at most a quarter of the groups (a 2048-
-  // candidate row on 512 threads with k = 256 ran 53.5 us per 128k-token step this way, 40.4 us
-  // through the exact select)
-  const bool fast = n <= kMaxFast && keff < n && 4 * keff <= ngroups && keff <= kSmallK;   // uniform
+  // With one candidate per thread (n <= NT) the group maxima are the candidates and the bound is
+  // exact. With several, it prunes well while k_eff is at most a quarter of the groups (a 2048-
+  // candidate row on 512 threads with k = 256 ran 53.5 us per 128k-token step through the
+  // bound, 40.4 us through the exact select)
+  const bool fast = n <= kMaxFast && keff < n && keff <= ngroups && (n <= NT || 4 * keff <= ngroups) &&
+                    keff <= kSmallK;   // uniform
   if (!fast) {   // every candidate kept, or the exact path
     if (keff == n) {
       for (int i = tid; i < n; i += NT) emit(a, row, i, i);
