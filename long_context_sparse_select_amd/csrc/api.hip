@@ -43,7 +43,7 @@ struct Layout {
 // 38.9 -> 35.0 us per step; k = 256: 52.2 -> 46.6 us).
 bool fused_decode(const msa_config* c, int row_stride) {
   return c->q_dtype == MSA_BF16 && c->top_k <= kMaxFusedTopK && row_stride <= kMaxFusedChunks * kScoreChunk &&
-         (c->top_k <= 64 || row_stride >= 2 * kScoreChunk * c->top_k);
+         (c->top_k <= 64 || row_stride >= 2 * kMaxRun * c->top_k);
 }
 
 // any_mode: the entry point does not read score_mode (msa_select_index)
@@ -91,7 +91,7 @@ Layout decode_layout(const msa_config* c, int op, int B, int max_len) {
     // mixed lengths up to 1M: a whole step of 181 us fused against 172 us unfused)
     L.fused = fused_decode(c, L.row_stride) && L.nsplit > 1;
     if (L.fused) {
-      L.cstride = (L.row_stride + kScoreChunk - 1) / kScoreChunk;
+      L.cstride = 2 * ((L.row_stride + kScoreChunk - 1) / kScoreChunk);   // two runs per scoring chunk
       L.cmax = off; off += align256(rows * (size_t)(L.cstride > 0 ? L.cstride : 1) * sizeof(float));
     }
   }

@@ -88,11 +88,11 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_mov<0xB1>(x));
-  x = fmaxf(x, dpp_mov<0x4E>(x));
-  x = fmaxf(x, dpp_mov<0x141>(x));
-  x = fmaxf(x, dpp_mov<0x140>(x));
+// Maximum over each half (8 lanes) of a 16-lane row; every lane of the half gets it.
+__device__ __forceinline__ float row8_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
   return x;
 }
 

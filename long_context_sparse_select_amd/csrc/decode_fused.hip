@@ -9,16 +9,16 @@
 // A top-k of a row on one workgroup is a serial chain of loads and barriers that leaves the
 // rest of the chip idle, then hands over to the attend through another launch. Here every
 // attend workgroup of a (sequence, group) row finds the row's exact top-k itself, from what the
-// scoring launch left: the row's scores and its chunk maxima (the largest score of each run of
-// 16 blocks, kScoreChunk). Grid (split, group, sequence), 256 threads:
-//   1. the <= 1024 chunk maxima of the row (4 per thread): a 256-bin histogram of them, linear in
+// scoring launch left: the row's scores and its run maxima (the largest score of each run of
+// 8 blocks, kMaxRun; "chunks" below). Grid (split, group, sequence), 256 threads:
+//   1. the <= 2048 chunk maxima of the row (8 per thread): a 256-bin histogram of them, linear in
 //      score value, gives T0 = the lower edge of the bin where the count from the top reaches
 //      k_eff (less half a bin against float rounding). At least k_eff chunk maxima are >= T0, and
 //      each is the score of a block, so the k_eff-th largest score is >= T0 and every kept block
 //      lies in a chunk whose maximum is >= T0 (a survivor chunk). The sequence's last chunk is
 //      always a survivor (with a new token, its last block's score comes from the append and is
 //      not in that chunk's recorded maximum);
-//   2. the scores of the survivor chunks (typically ~k chunks, 64 B each) that are >= T0 are the
+//   2. the scores of the survivor chunks (typically ~k chunks, 32 B each) that are >= T0 are the
 //      candidates (>= k_eff of them, every tie of the k_eff-th score among them); each is ranked
 //      exactly by (key desc, index asc) against the others (a quad of lanes per candidate); ranks
 //      < k_eff are kept and placed in ascending block order by counting. Forced sink / local
@@ -47,12 +47,13 @@ namespace {
 
 constexpr int kFT = 256;                 // threads per workgroup
 constexpr int kFW = kFT / 64;            // waves
-constexpr int kCPer = kMaxFusedChunks / kFT;   // chunk maxima per thread (4)
+constexpr int kMaxFusedRuns = kMaxFusedChunks * kScoreChunk / kMaxRun;   // 2048
 constexpr int kFBins = 256;
-constexpr int kSurvCap = 512;            // survivor chunks held
+constexpr int kSurvCap = 1024;           // survivor runs held
+static_assert(kFT % kScoreChunk == 0 && kMaxFusedRuns % kFT == 0, "chunks per thread and per round");
 // candidates ranked: a row with fewer chunks than k_eff has no chunk-maximum bound, and all its
-// n < kScoreChunk * k_eff scores are candidates, which this holds for k_eff <= 64; with at least
-// 2 k_eff chunks the bound leaves ~k_eff .. 2 k_eff candidates; more take the exact path
+// n < kMaxRun * k_eff scores are candidates, which this holds for k_eff <= 64; with at least
+// 2 k_eff runs the bound leaves ~k_eff .. 2 k_eff candidates; more take the exact path
 constexpr int kCandCap = 1024;
 constexpr int kRounds = 8;               // survivor-chunk rounds (16 chunks each) with loads in flight
 
@@ -122,8 +123,10 @@ __device__ __forceinline__ void select_exact(const float* srow, const int32_t* t
 // padded with INT_MAX up to kMaxFusedTopK), false when they are in sh.sorted / sh.sortedpg in
 // ascending order (every block kept, or the exact path). All threads call it; it ends with a
 // barrier.
-// FORCED: the first `sink` and last `local` blocks of the row are kept whatever their scores
-template <bool FORCED>
+// FORCED: the first `sink` and last `local` blocks of the row are kept whatever their scores.
+// RUN: blocks per chunk of the bound, kMaxRun (the recorded runs) or 2 kMaxRun (pairs of them:
+// half the maxima to histogram, for k <= 64)
+template <bool FORCED, int RUN>
 __device__ __forceinline__ bool select_row(const float* srow, const float* crow, const int32_t* trow, int n, int keff,
                                            int sink, int local, SelectShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,16 +135,23 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
     __syncthreads();
     return false;
   }
-  const int nch = (n + kScoreChunk - 1) / kScoreChunk;
+  static_assert(RUN == kMaxRun || RUN == 2 * kMaxRun, "a chunk is one or two recorded runs");
+  constexpr int kCPer = kMaxFusedRuns * kMaxRun / RUN / kFT;   // chunk maxima per thread (8 or 4)
+  const int nch = (n + RUN - 1) / RUN;
   uint32_t ck[kCPer];
   bool cv[kCPer];
 #pragma unroll
   for (int i = 0; i < kCPer; ++i) {   // loads first, clamped so none is conditional
     const int c = tid + kFT * i;
     cv[i] = c < nch;
-    ck[i] = order_key(crow[min(c, nch - 1)]);
+    const int cc = min(c, nch - 1);
+    if constexpr (RUN == kMaxRun) {
+      ck[i] = order_key(crow[cc]);
+    } else {   // both runs of the chunk are recorded (-inf for one with no block)
+      ck[i] = max(order_key(crow[2 * cc]), order_key(crow[2 * cc + 1]));
+    }
     // a chunk holding a forced block has that block's key as its maximum
-    if (FORCED && (kScoreChunk * c < sink || (local > 0 && kScoreChunk * (c + 1) > n - local))) ck[i] = kForcedKey;
+    if (FORCED && (RUN * c < sink || (local > 0 && RUN * (c + 1) > n - local))) ck[i] = kForcedKey;
   }
   if (tid == 0) { sh.nsurv = 0; sh.ncand = 0; }
   if (tid < kFBins) sh.hist[tid] = 0u;
@@ -231,16 +241,17 @@ __device__ __forceinline__ bool select_row(const float* srow, const float* crow,
   const int ns = sh.nsurv;
   bool exact = ns > kSurvCap;   // uniform
   if (!exact) {
-    const int sub = tid & 15, slot = tid >> 4;   // 16 lanes per chunk: block 16 c + sub
-    for (int r0 = 0; r0 < ns; r0 += 16 * kRounds) {
+    const int sub = tid & (RUN - 1), slot = tid / RUN;   // RUN lanes per chunk: block RUN c + sub
+    constexpr int kSlots = kFT / RUN;
+    for (int r0 = 0; r0 < ns; r0 += kSlots * kRounds) {
       float v[kRounds];
       int jj[kRounds], pg[kRounds];
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {   // every round's loads in flight before any is used: the
-        const int si = r0 + 16 * r + slot;   // score and, in the same round trip, the block's page id
+        const int si = r0 + kSlots * r + slot;   // score and, in the same round trip, the block's page id
         const int c = sh.surv[min(si, ns - 1)];
-        jj[r] = (si < ns) ? kScoreChunk * c + sub : n;
-        const int jc = min(kScoreChunk * c + sub, n - 1);
+        jj[r] = (si < ns) ? RUN * c + sub : n;
+        const int jc = min(RUN * c + sub, n - 1);
         v[r] = srow[jc];
         pg[r] = trow[jc];
       }
@@ -322,7 +333,7 @@ __device__ __forceinline__ void write_ordered(const SelectShared& sh, int keff, 
 
 // G: heads per group; U: blocks whose K/V loads each wave keeps in flight (the launcher uses 2);
 // FORCED: forced sink / local blocks (keep_sink or keep_local nonzero)
-template <int G, int U, bool FORCED>
+template <int G, int U, bool FORCED, int RUN>
 __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   const AttendArgs& a = f.att;
   __shared__ SelectShared sh;
@@ -368,7 +379,7 @@ __global__ void __launch_bounds__(kFT) k_decode_select_attend(FusedArgs f) {
   const int32_t* trow = a.table + (long long)b * a.max_blocks;
   bool by_rank = false;
   if (keff > 0 && e0 < keff)   // uniform: this split holds kept blocks
-    by_rank = select_row<FORCED>(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff,
+    by_rank = select_row<FORCED, RUN>(f.scores + rowbg * f.row_stride, f.cmax + rowbg * f.cstride, trow, nb, keff,
                                  f.keep_sink, f.keep_local, sh);
   // the blocks this split attends: ranks [e0, e1) (by_rank) or positions [e0, e1) of the ascending list
   const int* lst = by_rank ? sh.sel : sh.sorted;
@@ -436,8 +447,13 @@ hipError_t launch_fused_g(const FusedArgs& f, hipStream_t st) {
   // two blocks in flight per wave, looping over the split's blocks: four measured no faster at
   // G <= 5 and, beyond 256 registers per lane at G >= 6 (one workgroup per CU), ~20 % slower
   if (log_enabled()) log_launch("k_decode_select_attend", grid, kFT, 0, "G=%d, blocks in flight %d", G, 2);
-  if (f.keep_sink > 0 || f.keep_local > 0) k_decode_select_attend<G, 2, true><<<grid, kFT, 0, st>>>(f);
-  else k_decode_select_attend<G, 2, false><<<grid, kFT, 0, st>>>(f);
+  // k <= 64: chunks of 16 blocks (pairs of recorded runs); larger k: the runs of 8 themselves,
+  // twice as many maxima for a bound that still prunes at k up to the row's runs / 2
+  const bool forced = f.keep_sink > 0 || f.keep_local > 0, fine = a.k > 64;
+  if (forced && fine) k_decode_select_attend<G, 2, true, kMaxRun><<<grid, kFT, 0, st>>>(f);
+  else if (forced) k_decode_select_attend<G, 2, true, 2 * kMaxRun><<<grid, kFT, 0, st>>>(f);
+  else if (fine) k_decode_select_attend<G, 2, false, kMaxRun><<<grid, kFT, 0, st>>>(f);
+  else k_decode_select_attend<G, 2, false, 2 * kMaxRun><<<grid, kFT, 0, st>>>(f);
   return hipGetLastError();
 }
 

@@ -55,11 +55,13 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
 // k_new / v_new (nullable, [B][Hkv][128]): the decode step's new token, already counted in seq_lens.
 // The same launch writes its K/V row at position seq_len-1, recomputes that block's summary from
 // its keys and scores the block from the stored summary.
-// cmax (nullable, [B][Hkv][cstride]): the largest score of each run of kScoreChunk blocks j < n_b,
-// the appended block's excepted (-inf for a run with none); cstride >= ceil(row_stride / kScoreChunk)
+// cmax (nullable, [B][Hkv][cstride]): the largest score of each run of kMaxRun blocks j < n_b
+// (two per scoring chunk), the appended block's excepted (-inf for a run with none);
+// cstride >= 2 ceil(row_stride / kScoreChunk) (both runs of every scoring chunk are written)
 // pad: also write -inf for the whole runs past n_b (a caller's score buffer); without it those
 // entries are left as they are (the library's own consumers read a row only up to n_b)
 constexpr int kScoreChunk = 16;
+constexpr int kMaxRun = 8;      // blocks per recorded maximum
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,
                                int max_len, float* scores, int row_stride, const void* k_new, const void* v_new,
                                hipStream_t st, float* cmax = nullptr, int cstride = 0, bool pad = true);
@@ -123,10 +125,11 @@ hipError_t launch_attend_decode(bool bf16, const AttendArgs& a, hipStream_t st);
 hipError_t launch_merge_bf16(const AttendArgs& a, hipStream_t st);
 
 // ---- Steps 1 (TopK) and 2 of a bf16 decode step in one launch (then the merge when split):
-// every attend workgroup selects its row's top-k from the scores and chunk maxima of the scoring
+// every attend workgroup selects its row's top-k from the scores and run maxima of the scoring
 // launch and attends its split of the list. For k <= kMaxFusedTopK and rows of at most
-// kMaxFusedChunks * kScoreChunk blocks; forced sink / local blocks take a key above every score,
-// and so does the maximum of every chunk that holds one.
+// kMaxFusedChunks * kScoreChunk blocks (k > 64: rows of at least 2 k runs of kMaxRun blocks);
+// forced sink / local blocks take a key above every score, and so does the maximum of every run
+// that holds one.
 constexpr int kMaxFusedTopK = 256;
 constexpr int kMaxFusedChunks = 1024;
 struct FusedArgs {

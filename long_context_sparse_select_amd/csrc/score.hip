@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       const int g = e / kChunk, jl = e % kChunk;
       if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
     }
-    if (cmax != nullptr && tid < Hkv) cmax[((long long)b * Hkv + tid) * cstride + chunk] = -INFINITY;
+    if (cmax != nullptr && tid < 2 * Hkv) cmax[((long long)b * Hkv + tid / 2) * cstride + 2 * chunk + tid % 2] = -INFINITY;
     return;
   }
 
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
       const int g = e / kChunk, jl = e % kChunk;
       if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
     }
-    if (cmax != nullptr && tid < Hkv) cmax[((long long)b * Hkv + tid) * cstride + chunk] = -INFINITY;
+    if (cmax != nullptr && tid < 2 * Hkv) cmax[((long long)b * Hkv + tid / 2) * cstride + 2 * chunk + tid % 2] = -INFINITY;
     return;
   }
   summary_loads(0);
@@ -283,10 +283,10 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   __syncthreads();
   // each row's chunk of scores leaves as one contiguous run; with a new token, its block's score
   // is the append workgroup's
-  // The chunk's maximum per group (for the fused select-and-attend) is taken over the scores
-  // written here, in the same pass: the 16 scores of a group are one 16-lane row (kChunk = 16
-  // and every pass covers whole rows), so a row reduction gives it. The appended block's score is
-  // the append workgroup's and is not in it.
+  // The maxima of the chunk's two 8-block runs per group (for the fused select-and-attend) are
+  // taken over the scores written here, in the same pass: the 16 scores of a group are one 16-lane
+  // row (kChunk = 16 and every pass covers whole rows), so a reduction over each half-row gives
+  // them. The appended block's score is the append workgroup's and is not in them.
   static_assert(kChunk == 16 && 256 % kChunk == 0, "one group's chunk of scores per 16-lane row");
   const int jskip = napp > 0 ? nb - 1 : -1;
   for (int e = tid; e < Hkv * kChunk; e += 256) {
@@ -295,8 +295,8 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
     const float v = s_sc[e];
     if (j < jend && j != jskip) scores[((long long)b * Hkv + g) * row_stride + j] = v;
     if (cmax != nullptr) {   // uniform
-      const float mrow = row16_max(j < jend && j < nb && j != jskip ? v : -INFINITY);
-      if (jl == 0) cmax[((long long)b * Hkv + g) * cstride + chunk] = mrow;
+      const float mrun = row8_max(j < jend && j < nb && j != jskip ? v : -INFINITY);
+      if ((jl & (kMaxRun - 1)) == 0) cmax[((long long)b * Hkv + g) * cstride + 2 * chunk + jl / kMaxRun] = mrun;
     }
   }
 }
@@ -431,7 +431,7 @@ template <typename TQ, bool SB>
 void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv, int max_len, float* scores,
                         int row_stride, const TQ* k_new, const TQ* v_new, float* cmax, int cstride, int pad,
                         hipStream_t st) {
-  static_assert(kChunk == kScoreChunk, "chunk maxima cover the scoring kernel's chunks");
+  static_assert(kChunk == kScoreChunk && kChunk == 2 * kMaxRun, "two run maxima per scoring chunk");
   const int napp = k_new != nullptr ? Hkv : 0;
   const dim3 grid(napp + (row_stride + kChunk - 1) / kChunk, B);
   const int lds_floats = Hkv * (kD + kChunk) > 4 * kD + 2 ? Hkv * (kD + kChunk) : 4 * kD + 2;

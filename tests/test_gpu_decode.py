@@ -267,11 +267,13 @@ def test_full_size_decode_large_k():
 
 
 @pytest.mark.parametrize("B,n,k,sink,local", [(1, 1 << 20, 65, 0, 0), (1, 1 << 20, 256, 0, 0),
-                                              (2, 1 << 19, 128, 1, 1)])
+                                              (2, 1 << 19, 128, 1, 1), (1, 1 << 18, 256, 0, 0),
+                                              (1, 1 << 18, 192, 1, 1), (2, 1 << 17, 128, 0, 0)])
 def test_full_size_decode_fused_large_k(B, n, k, sink, local):
-    """k from 65 to 256 on rows of at least 2k chunks of 16 blocks: Step 1's top-k runs inside the
-    attend launch (chunk-maximum bound, ~k .. 2k candidates ranked), with and without forced
-    blocks; the lists and outputs against the oracle."""
+    """k from 65 to 256 on rows of at least 2k runs of 8 blocks (down to exactly 2k at 256k
+    tokens, k = 256): Step 1's top-k runs inside the attend launch (run-maximum bound, ~k .. 2k
+    candidates ranked), with and without forced blocks; the lists and outputs against the
+    oracle."""
     kw = dict(workload("decode_bf16_1m_paged", seed=0), B=B, lens=[n] * B, top_k=k)
     c = make_decode_case_torch(**kw)
     d = to_device(c)
