@@ -40,6 +40,7 @@ constexpr int kMaxK = 4096;
 constexpr int kSmallK = 256;    // k_eff up to this uses the survivor path; larger k the exact select
 constexpr int kRowRank = 512;   // survivors ranked 16 lanes each up to this count
 constexpr int kLBins = 1024;    // bins per pass of the exact select
+constexpr int kBinKeys = 512;   // exact select: a chosen bin of at most this many keys is finished in LDS
 
 struct TopkShared {
   unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
@@ -107,21 +108,24 @@ __device__ void select_fallback(const TopkArgs& a, const float* srow, int row, i
   }
 }
 
-// Exclusive prefix, in ascending block order, of per-(slot, wave) counts of `pred` (slot i of
-// thread t holds block t + NT*i, so the order is slot-major, then wave, then lane). Returns this
-// thread's position for slot i in *pos and the block's total. Two barriers.
+// Exclusive prefixes, in ascending block order, of two predicates at once (slot i of thread t
+// holds block t + NT*i, so the order is slot-major, then wave, then lane): per-(slot, wave) counts
+// packed as (count of a) << 16 | (count of b) and scanned together (each total is at most 16,384,
+// so neither half carries into the other). Two barriers.
 template <int NT>
-__device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&pos)[kPer], TopkShared& sh) {
-  constexpr int kW = NT / 64, kE = kPer * kW;   // entries, at most 256
+__device__ __forceinline__ void ordered_prefix_pair(const bool (&pa)[kPer], const bool (&pb)[kPer], int (&ra)[kPer],
+                                                    int (&rb)[kPer], TopkShared& sh) {
+  constexpr int kW = NT / 64, kE = kPer * kW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned long long bm[kPer];
+  unsigned long long ba[kPer], bb[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    bm[i] = __ballot(pred[i]);
-    if (lane == 0) sh.pre[i * kW + wave] = __popcll(bm[i]);
+    ba[i] = __ballot(pa[i]);
+    bb[i] = __ballot(pb[i]);
+    if (lane == 0) sh.pre[i * kW + wave] = (__popcll(ba[i]) << 16) | __popcll(bb[i]);
   }
   __syncthreads();
-  if (wave == 0) {   // lane l scans entries 4l .. 4l+3, then an exclusive scan across lanes
+  if (wave == 0) {
     int v[4], sum = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) { v[e] = 4 * lane + e < kE ? sh.pre[4 * lane + e] : 0; sum += v[e]; }
@@ -131,19 +135,19 @@ __device__ __forceinline__ int ordered_prefix(const bool (&pred)[kPer], int (&po
       if (lane >= off) incl += y;
     }
     int run = incl - sum;
-    const int total = __shfl(incl, 63);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (4 * lane + e < kE) sh.pre[4 * lane + e] = run;
       run += v[e];
     }
-    if (lane == 0) sh.cnt = total;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    pos[i] = sh.pre[i * kW + wave] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm[i], 0u));
-  return sh.cnt;
+  for (int i = 0; i < kPer; ++i) {
+    const int pre = sh.pre[i * kW + wave];
+    ra[i] = (pre >> 16) + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ba[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba[i], 0u));
+    rb[i] = (pre & 0xffff) + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bb[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bb[i], 0u));
+  }
 }
 
 // Bin of a key on a linear score scale from vlo (bins of 1/vscale): monotone in the key, with
@@ -159,10 +163,12 @@ __device__ __forceinline__ uint32_t value_bin(uint32_t k, float vlo, float vscal
 //     32-bit key range takes at most 4 passes). The first pass bins score values linearly
 //     instead of keys: order keys of typical scores bunch into a sliver of the key range, so a
 //     key-linear first pass piles thousands of LDS atomics onto a few bins and leaves most keys
-//     in the chosen one; the chosen value bin is mapped back to its exact key range by a
-//     min / max over the keys that fall in it;
+//     in the chosen one. A chosen value bin of at most kBinKeys keys (typically a few dozen) is
+//     gathered into LDS and T is the key there with fewer than r = k_eff - (keys above the bin)
+//     larger keys and at least r at or above it, one thread per key; a fuller bin is mapped back
+//     to its exact key range by a min / max over the keys that fall in it and refined;
 //  2. ordered compaction: keys > T, then the ties == T with the smallest block indices, written
-//     at their rank in ascending block order (no sort needed).
+//     at their rank in ascending block order (no sort needed); one prefix pass counts both.
 template <int NT>
 __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const uint32_t (&key)[kPer],
                              const int32_t* trow, TopkShared& sh) {
@@ -184,19 +190,16 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
   kfin = wave_max_u32(kfin);
   if (lane == 0) { sh.red[wave] = kmx; sh.red[kW + wave] = kmn; sh.red[2 * kW + wave] = kfin; }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t mx = 0u, mn = 0xffffffffu, fin = 0u;
-    for (int w = 0; w < kW; ++w) {
-      mx = max(mx, sh.red[w]);
-      mn = min(mn, sh.red[kW + w]);
-      fin = max(fin, sh.red[2 * kW + w]);
-    }
-    sh.range[0] = mn; sh.range[1] = mx; sh.range[2] = fin;
+  uint32_t lo = 0xffffffffu, hi = 0u, fin = 0u, above = 0u;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {   // every thread reads the wave results (no second barrier)
+    hi = max(hi, sh.red[w]);
+    lo = min(lo, sh.red[kW + w]);
+    fin = max(fin, sh.red[2 * kW + w]);
   }
-  __syncthreads();
-  uint32_t lo = sh.range[0], hi = sh.range[1], above = 0u;
-  const float vlo = key_value(lo), vfin = key_value(sh.range[2]);
-  if (lo != hi && sh.range[2] > lo && isfinite(vlo) && isfinite(vfin) && vfin > vlo) {   // uniform
+  bool done = false;   // T (lo == hi) and `above` found through the chosen bin's keys in LDS
+  const float vlo = key_value(lo), vfin = key_value(fin);
+  if (lo != hi && fin > lo && isfinite(vlo) && isfinite(vfin) && vfin > vlo) {   // uniform
     // ---- first pass on a score scale from the smallest key to the largest finite one
     const float vscale = (float)kLBins / (vfin - vlo);
     for (int b = tid; b < kLBins; b += NT) sh.hbig[b] = 0u;
@@ -216,28 +219,65 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
       }
       uint32_t run = incl - local;
       for (int e = 15; e >= 0; --e) {
-        if (run < (uint32_t)keff && run + c[e] >= (uint32_t)keff) { sh.range[0] = 16 * lane + e; sh.range[2] = run; }
+        if (run < (uint32_t)keff && run + c[e] >= (uint32_t)keff) {
+          sh.range[0] = 16 * lane + e; sh.range[1] = c[e]; sh.range[2] = run;
+        }
         run += c[e];
       }
+      if (lane == 0) sh.cnt = 0;
     }
     __syncthreads();
     // ---- exact key range of the chosen bin: every key in it lies in [min, max] of its keys, and
     // (the binning being monotone) every key in that interval is in it; keys above are `above`
     const uint32_t bsel = sh.range[0];
+    const int mbin = (int)sh.range[1];
     above = sh.range[2];
-    uint32_t bmx = 0u, bmn = 0xffffffffu;
+    if (mbin <= kBinKeys) {   // uniform: the bin's keys to LDS, then the (keff - above)-th of them
+      uint32_t* bk = reinterpret_cast<uint32_t*>(sh.comp);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (valid[i] && value_bin(key[i], vlo, vscale) == bsel) { bmx = max(bmx, key[i]); bmn = min(bmn, key[i]); }
-    bmx = wave_max_u32(bmx);
-    bmn = wave_min_u32(bmn);
-    if (lane == 0) { sh.red[wave] = bmx; sh.red[kW + wave] = bmn; }
-    __syncthreads();
-    lo = 0xffffffffu; hi = 0u;
+      for (int i = 0; i < kPer; ++i) {
+        const bool inb = valid[i] && value_bin(key[i], vlo, vscale) == bsel;
+        const unsigned long long bm = __ballot(inb);
+        if (bm != 0ull) {   // wave-uniform
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&sh.cnt, __popcll(bm));
+          base = __builtin_amdgcn_readfirstlane(base);
+          const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (inb && at < kBinKeys) bk[at] = key[i];   // at < mbin: the histogram's own bin test
+        }
+      }
+      __syncthreads();
+      // T is the bin key x with (keys > x) < r <= (keys >= x), r = keff - above (1 <= r <= mbin)
+      const int r = keff - (int)above;
+      for (int t = tid; t < mbin; t += NT) {
+        const uint32_t x = bk[t];
+        int gt = 0, ge = 0;
+        for (int u = 0; u < mbin; ++u) {   // the same address across the wave: broadcast reads
+          const uint32_t y = bk[u];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < r && r <= ge) { sh.range[0] = x; sh.range[2] = above + (uint32_t)gt; }   // equal writes
+      }
+      __syncthreads();
+      lo = hi = sh.range[0];
+      above = sh.range[2];
+      done = true;
+    } else {   // the exact key range of the bin, refined below
+      uint32_t bmx = 0u, bmn = 0xffffffffu;
 #pragma unroll
-    for (int w = 0; w < kW; ++w) { hi = max(hi, sh.red[w]); lo = min(lo, sh.red[kW + w]); }
+      for (int i = 0; i < kPer; ++i)
+        if (valid[i] && value_bin(key[i], vlo, vscale) == bsel) { bmx = max(bmx, key[i]); bmn = min(bmn, key[i]); }
+      bmx = wave_max_u32(bmx);
+      bmn = wave_min_u32(bmn);
+      if (lane == 0) { sh.red[wave] = bmx; sh.red[kW + wave] = bmn; }
+      __syncthreads();
+      lo = 0xffffffffu; hi = 0u;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) { hi = max(hi, sh.red[w]); lo = min(lo, sh.red[kW + w]); }
+    }
   }
-  while (lo != hi) {   // uniform
+  while (!done && lo != hi) {   // uniform
     for (int b = tid; b < kLBins; b += NT) sh.hbig[b] = 0u;
     __syncthreads();
     const unsigned long long span = (unsigned long long)(hi - lo) + 1ull;
@@ -272,25 +312,28 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
   }
   const uint32_t T = lo;
   const int need_eq = keff - (int)above;   // >= 1 ties at T are kept, smallest block indices first
-  bool eq[kPer];
-  int rk[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) eq[i] = valid[i] && key[i] == T;
-  ordered_prefix<NT>(eq, rk, sh);
-  bool sel[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) sel[i] = valid[i] && (key[i] > T || (eq[i] && rk[i] < need_eq));
-  int pg[kPer];   // decode: the kept blocks' page ids, loaded while the prefix is formed
-  if (trow != nullptr) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) pg[i] = sel[i] ? trow[tid + NT * i] : -1;
-  }
-  ordered_prefix<NT>(sel, rk, sh);
+  // one ordered prefix of (keys > T, keys == T): a kept key's position is the keys > T before it
+  // plus the kept ties before it, min(ties before it, need_eq); a tie is kept while its own rank
+  // among the ties is below need_eq
+  bool gt[kPer], eq[kPer];
+  int rg[kPer], re[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    if (sel[i]) {
-      a.idx[(long long)row * a.idx_stride + rk[i]] = tid + NT * i;
-      if (trow != nullptr) a.pages[(long long)row * a.k + rk[i]] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
+    gt[i] = valid[i] && key[i] > T;
+    eq[i] = valid[i] && key[i] == T;
+  }
+  int pg[kPer];   // decode: the candidates' page ids (ties that stay out included), loaded under the prefix
+  if (trow != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) pg[i] = gt[i] || eq[i] ? trow[tid + NT * i] : -1;
+  }
+  ordered_prefix_pair<NT>(gt, eq, rg, re, sh);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (gt[i] || (eq[i] && re[i] < need_eq)) {
+      const int pos = rg[i] + min(re[i], need_eq);
+      a.idx[(long long)row * a.idx_stride + pos] = tid + NT * i;
+      if (trow != nullptr) a.pages[(long long)row * a.k + pos] = page_ok(pg[i], a.num_pages) ? pg[i] : -1;
     }
   }
 }

@@ -53,6 +53,14 @@ def crafted(kind, rng, shape):
             s[r][rng.choice(shape[-1], 40, replace=False)] = -np.inf
     elif kind == "offset":                          # spread 1e-2 on 1000: just under the value-bin guard
         s = 1000.0 + 1e-2 * rng.standard_normal(shape)
+    elif kind == "quantized_fine":                  # steps of 1/64: a dozen ties per value near the k-th
+        s = np.round(rng.standard_normal(shape) * 64) / 64
+    elif kind.startswith("cluster_"):               # m distinct scores within 2e-4 (one value bin)
+        _, where, m = kind.split("_")
+        s = rng.standard_normal(shape)
+        base = 5.0 if where == "top" else 1.72      # above every normal score, or ~700 normals above
+        for r in np.ndindex(shape[:-1]):
+            s[r][rng.choice(shape[-1], int(m), replace=False)] = base + 2e-4 * rng.random(int(m))
     elif kind == "outlier":                         # one huge score stretches the value range
         s = rng.standard_normal(shape)
         for r in np.ndindex(shape[:-1]):
@@ -125,6 +133,12 @@ CASES = [
     ("subnormal", [16384], 1024, 0, 0, 0),
     ("normal", [16384, 4000], 1024, 0, 0, 5),         # -inf scores: key-bin first pass
     ("normal", [16384], 4096, 0, 0, 0),
+    # large k where the chosen value bin is crowded: finished in LDS up to 512 keys, refined by
+    # key bins beyond (2000 distinct keys in one bin), ties inside a small bin
+    ("cluster_top_2000", [16384, 9000], 1024, 0, 0, 0),
+    ("cluster_mid_500", [16384, 12000], 1024, 0, 0, 0),
+    ("cluster_mid_300", [16384], 900, 1, 1, 0),
+    ("quantized_fine", [16384, 6000], 1024, 0, 0, 0),
     ("normal", [20000, 30000], 64, 0, 0, 0),          # memory-based select (rows > 16,384)
     ("quantized", [20000], 1024, 1, 1, 3),
     # small k on every distribution: the group-maximum bound on score-value bins, or key bins
