@@ -5,7 +5,7 @@
 // §1 Steps 1-2; §3 decode / prefill):
 //   msa_decode_step   [append: new K/V row, that block's summary and score | score] (one launch) -> top-k
 //                     -> attend -> split-K merge; for bf16, k <= 256 on long rows, split over
-//                     several workgroups: [append | score + chunk maxima] -> select-and-attend -> merge
+//                     several workgroups: [append | score + run maxima] -> select-and-attend -> merge
 //   msa_prefill_chunk [append + summaries | tile queries] (one launch) -> score -> top-k (+diagonal)
 //                     -> attend (-> merge of the list splits, for short chunks)
 //   msa_prefill_attend  attend (the last launch of msa_prefill_chunk, over given lists)
@@ -32,15 +32,16 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   size_t scores = 0, idx = 0, pages = 0, qtile = 0, part_o = 0, part_ml = 0, cmax = 0, total = 0;
   int row_stride = 0;   // scores per row
-  int cstride = 0;      // chunk maxima per row (fused decode step)
+  int cstride = 0;      // run maxima per row (fused decode step)
   int bps = 1, nsplit = 0;
   bool fused = false;   // decode step: Step 1's TopK inside the attend launch
 };
 
-// A bf16 decode step with k <= kMaxFusedTopK and rows of at most kMaxFusedChunks chunks selects
-// inside its attend launch (launch_decode_select_attend); for k > 64 the rows must also hold at
-// least 2k chunks, so that the chunk-maximum bound leaves few candidates (1M tokens, k = 128:
-// 38.9 -> 35.0 us per step; k = 256: 52.2 -> 46.6 us).
+// A bf16 decode step with k <= kMaxFusedTopK and rows of at most kMaxFusedChunks scoring chunks
+// selects inside its attend launch (launch_decode_select_attend); for k > 64 the rows must also
+// hold at least 2k runs of kMaxRun blocks, so that the run-maximum bound leaves few candidates
+// (1M tokens, k = 128: 38.9 -> 35.0 us per step; k = 256: 52.2 -> 46.6 us; 256k tokens, k = 256:
+// 44.0 -> 42.8 us).
 bool fused_decode(const msa_config* c, int row_stride) {
   return c->q_dtype == MSA_BF16 && c->top_k <= kMaxFusedTopK && row_stride <= kMaxFusedChunks * kScoreChunk &&
          (c->top_k <= 64 || row_stride >= 2 * kMaxRun * c->top_k);
@@ -288,7 +289,7 @@ msa_status run_decode_step(const msa_config* cfg, const void* q, const msa_kv_ca
                            const void* k_new, const void* v_new, int32_t* idx_out, float* scores_out, void* out,
                            float* lse_out, const Layout& L, void* ws, hipStream_t st) {
   float* scores = scores_out ? scores_out : at<float>(ws, L.scores);
-  if (L.fused) {   // score (+ chunk maxima) -> select-and-attend -> merge
+  if (L.fused) {   // score (+ run maxima) -> select-and-attend -> merge
     float* cmax = at<float>(ws, L.cmax);
     MSA_TRY(hip_status(launch_score_decode(true, q, cache_args(cfg, cache), B, cfg->num_q_heads, cfg->num_kv_heads,
                                            max_len, scores, L.row_stride, k_new, v_new, st, cmax, L.cstride,

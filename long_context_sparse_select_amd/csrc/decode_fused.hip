@@ -32,7 +32,7 @@
 //      positions fall in the same range are written to the index list: the ordering is off the
 //      path to the first load.
 // Rows whose survivors or candidates overflow the LDS lists (mass ties, or too few chunks for
-// the bound to prune: the host fuses k > 64 only for rows of at least 2k chunks) take an exact
+// the bound to prune: the host fuses k > 64 only for rows of at least 2k runs) take an exact
 // path: a bitwise search for the k_eff-th key over the row's scores, then an ordered compaction.
 // Reading the row per workgroup is redundant across a row's splits, but it is ~10 KiB of L2 hits
 // per workgroup instead of a launch and a 64 KiB single-CU round trip.

@@ -441,7 +441,7 @@ void launch_score_typed(const TQ* q, const CacheArgs& c, int B, int Hq, int Hkv,
   if (log_enabled())
     log_launch("k_score_decode", grid, 256, lds, "%s q, Hkv=%d, %s summaries%s%s", sizeof(TQ) == 2 ? "bf16" : "f32",
                Hkv, SB ? "bf16" : "f32", napp > 0 ? ", with the new token's append" : "",
-               cmax != nullptr ? ", chunk maxima" : "");
+               cmax != nullptr ? ", run maxima" : "");
 #define MSA_SCORE_CASE(H)                                                                                  \
   case H:                                                                                                  \
     k_score_decode<TQ, H, SB><<<grid, 256, lds, st>>>(q, c.S, c.table, c.lens, c.num_pages, c.max_blocks, Hq, \

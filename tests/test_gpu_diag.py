@@ -54,7 +54,7 @@ def test_log_of_a_decode_step(tmp_path):
                      r"\d+ split\(s\) of \d+ block\(s\), top-k inside the attend launch; workspace \d+ of \d+ B, "
                      r"appending a new token", text), text
     for kernel in (r"k_build_summaries<bf16 keys, f32 summaries>",
-                   r"k_score_decode<bf16 q, Hkv=8, f32 summaries, with the new token's append, chunk maxima> "
+                   r"k_score_decode<bf16 q, Hkv=8, f32 summaries, with the new token's append, run maxima> "
                    r"grid 46 x 1 x 1, 256 threads",
                    r"k_decode_select_attend<G=4, blocks in flight \d> grid \d+ x 8 x 1, 256 threads",
                    r"k_merge<bf16, splits/8 = \d+> grid 32 x 1 x 1, 256 threads"):
