@@ -43,7 +43,10 @@ constexpr int kLBins = 1024;    // bins per pass of the exact select
 constexpr int kBinKeys = 512;   // exact select: a chosen bin of at most this many keys is finished in LDS
 
 struct TopkShared {
-  unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
+  union {                             // one of the two per row, never both live
+    unsigned long long comp[kCap + 2];  // survivors: (key << 32) | ~index, larger = better
+    uint32_t bkeys[kBinKeys];           // exact select: the chosen bin's keys
+  };
   int32_t sel[kMaxK + 4];
   int32_t selpg[kMaxK];
   uint32_t hist[kBins];
@@ -233,7 +236,7 @@ __device__ void select_large(const TopkArgs& a, int row, int n, int keff, const 
     const int mbin = (int)sh.range[1];
     above = sh.range[2];
     if (mbin <= kBinKeys) {   // uniform: the bin's keys to LDS, then the (keff - above)-th of them
-      uint32_t* bk = reinterpret_cast<uint32_t*>(sh.comp);
+      uint32_t* bk = sh.bkeys;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const bool inb = valid[i] && value_bin(key[i], vlo, vscale) == bsel;
