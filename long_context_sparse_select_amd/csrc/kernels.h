@@ -58,8 +58,9 @@ hipError_t launch_prefill_prologue(bool bf16, const CacheArgs& c, const void* k_
 // cmax (nullable, [B][Hkv][cstride]): the largest score of each run of kMaxRun blocks j < n_b
 // (two per scoring chunk), the appended block's excepted (-inf for a run with none);
 // cstride >= 2 ceil(row_stride / kScoreChunk) (both runs of every scoring chunk are written)
-// pad: also write -inf for the whole runs past n_b (a caller's score buffer); without it those
-// entries are left as they are (the library's own consumers read a row only up to n_b)
+// pad: also write -inf over the scores past n_b (a caller's score buffer); without it those
+// entries are left as they are (the library's own consumers read a row only up to n_b). Run
+// maxima past n_b are never written.
 constexpr int kScoreChunk = 16;
 constexpr int kMaxRun = 8;      // blocks per recorded maximum
 hipError_t launch_score_decode(bool bf16, const void* q, const CacheArgs& c, int B, int Hq, int Hkv,

@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kChunk = 16;    // logical blocks per workgroup (decode)
 constexpr int kUnroll = 8;    // pairs in flight per 32-lane slot
+constexpr int kTailBytes = 1 << 18;   // -inf tail bytes (pad) per writing chunk past a sequence's end
 
 // 8 consecutive elements as floats, in 16 B vector loads
 __device__ __forceinline__ void load8(const uint16_t* p, float* f) {
@@ -188,15 +189,33 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
   };
   table_loads(0);
   const int nb = (clamp_len(lens[b], max_len) + kP - 1) / kP;   // in flight with the table loads
-  if (j0 >= nb) {   // a chunk past the sequence's end (batches of mixed lengths): no summary reads;
-    // its -inf scores are written only for a caller's score buffer (pad), since every consumer in
-    // the library reads a row only up to the sequence's length
-    if (!pad) return;
-    for (int e = tid; e < Hkv * kChunk; e += 256) {
-      const int g = e / kChunk, jl = e % kChunk;
-      if (j0 + jl < jend) scores[((long long)b * Hkv + g) * row_stride + j0 + jl] = -INFINITY;
+  if (j0 >= nb) {   // a chunk past the sequence's end (batches of mixed lengths): no summary reads.
+    // A caller's score buffer (pad) gets -inf past the sequence's end (every consumer in the
+    // library reads a row only up to the sequence's length, run maxima included): the first
+    // chunks past the end, one per kTailBytes of the tail (at most all of them), split the tail
+    // of every group's row into equal ranges written with 16 B stores; the other chunks exit
+    // without a write
+    const int vc = (nb + kChunk - 1) / kChunk;     // chunks holding blocks
+    const int wi = chunk - vc;
+    const int from0 = vc * kChunk, tn = row_stride - from0;
+    const long long tail_bytes = (long long)tn * Hkv * 4;
+    const int nw = (int)min((long long)(tn + kChunk - 1) / kChunk,       // past-the-end chunks in the grid
+                            max(1ll, (tail_bytes + kTailBytes - 1) / kTailBytes));
+    if (!pad || wi >= nw) return;
+    const int seg = ((tn + nw - 1) / nw + 3) & ~3;                       // nw * seg >= tn
+    const int lo = from0 + wi * seg, hi = min(row_stride, lo + seg);
+    const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    for (int g = 0; g < Hkv && lo < hi; ++g) {
+      float* row = scores + ((long long)b * Hkv + g) * row_stride + lo;
+      const int n = hi - lo;
+      const int head = min(n, (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / 4u));
+      if (tid < head) row[tid] = -INFINITY;
+      const int nv = (n - head) / 4;
+      float4* r4 = reinterpret_cast<float4*>(row + head);
+      for (int i = tid; i < nv; i += 256) r4[i] = ninf;
+      const int rem = n - head - 4 * nv;
+      if (tid < rem) row[head + 4 * nv + tid] = -INFINITY;
     }
-    if (cmax != nullptr && tid < 2 * Hkv) cmax[((long long)b * Hkv + tid / 2) * cstride + 2 * chunk + tid % 2] = -INFINITY;
     return;
   }
   summary_loads(0);

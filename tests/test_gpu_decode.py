@@ -356,6 +356,36 @@ def test_score_entry_point_matches_select_scores():
     assert torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("Hkv,lens", [
+    (4, [300 * 64, 300 * 64 - 5, 285 * 64, 290 * 64 - 3, 272 * 64, 256 * 64, 100 * 64 + 7, 64, 1]),
+    (8, [2100 * 64, 64, 1000 * 64 + 3, 1800 * 64]),
+    (8, [17000 * 64, 64, 9000 * 64 - 1]),
+])
+def test_score_tails_past_each_end(Hkv, lens):
+    """msa_score writes -inf over every block past each sequence's end and leaves nothing else
+    unwritten, into a buffer that starts as NaN: tails of no block, inside the last scoring
+    chunk, one chunk past the end, several, and a 544 KB tail that several chunks past the end
+    split between them (one writer per 256 KB)."""
+    gen = make_decode_case_torch if max(lens) > 1 << 18 else make_decode_case
+    c = gen(B=len(lens), Hq=2 * Hkv, Hkv=Hkv, lens=lens, top_k=8, dtype="bf16", seed=41, permute=True)
+    d = to_device(c)
+    mb = (c.max_seq_len + 63) // 64
+    s1 = torch.full((c.B, c.Hkv, mb), float("nan"), dtype=torch.float32, device="cuda")
+    msa.msa_score(d.cfg, d.q, d.cache, c.B, c.max_seq_len, s1)
+    torch.cuda.synchronize()
+    s = s1.cpu().numpy()
+    for b, n in enumerate(lens):
+        nb = (n + 63) // 64
+        assert np.all(np.isfinite(s[b, :, :nb])), "b=%d: a block before the end is not scored" % b
+        assert np.all(np.isneginf(s[b, :, nb:])), "b=%d: %d entries past the end not -inf" % (
+            b, int(np.sum(~np.isneginf(s[b, :, nb:]))))
+    s2 = torch.full_like(s1, float("nan"))
+    idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
+    msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+
+
 EDGE = [
     # the largest top-k the library accepts (4096 of 5000 blocks: 256 splits, the widest merge)
     ("bf16_k4096_max", dict(B=1, Hq=8, Hkv=2, lens=[64 * 5000 - 17], top_k=4096, dtype="bf16", permute=True)),
