@@ -131,6 +131,27 @@ __device__ __forceinline__ void decode_append(const T* __restrict__ q, const T* 
 // shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
 // Workgroups x < napp (napp = Hkv with a new token, else 0) append, writing the pool through
 // S_app (the same pool as S, which only the scoring workgroups read); the others score chunks.
+// -inf over entries [lo, hi) of every group's score row of sequence b: 16 B stores across the
+// workgroup. Kept out of line: inlined into the scoring kernel's exit path it raised the kernel's
+// registers past the six-wave step (82 against 78 at 8 groups), and the grid of a batch of mixed
+// lengths then ran with fewer slots.
+__device__ __attribute__((noinline)) void write_neg_inf_rows(float* __restrict__ scores, int b, int Hkv, int row_stride,
+                                                             int lo, int hi) {
+  const int tid = threadIdx.x;
+  const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  for (int g = 0; g < Hkv && lo < hi; ++g) {
+    float* row = scores + ((long long)b * Hkv + g) * row_stride + lo;
+    const int n = hi - lo;
+    const int head = min(n, (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / 4u));
+    if (tid < head) row[tid] = -INFINITY;
+    const int nv = (n - head) / 4;
+    float4* r4 = reinterpret_cast<float4*>(row + head);
+    for (int i = tid; i < nv; i += 256) r4[i] = ninf;
+    const int rem = n - head - 4 * nv;
+    if (tid < rem) row[head + 4 * nv + tid] = -INFINITY;
+  }
+}
+
 template <typename TQ, int HKV, bool SB>
 __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const void* __restrict__ S,
                                                       const int32_t* __restrict__ table,
@@ -195,27 +216,17 @@ __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, 
     // chunks past the end, one per kTailBytes of the tail (at most all of them), split the tail
     // of every group's row into equal ranges written with 16 B stores; the other chunks exit
     // without a write
+    if (!pad) return;
     const int vc = (nb + kChunk - 1) / kChunk;     // chunks holding blocks
     const int wi = chunk - vc;
     const int from0 = vc * kChunk, tn = row_stride - from0;
     const long long tail_bytes = (long long)tn * Hkv * 4;
     const int nw = (int)min((long long)(tn + kChunk - 1) / kChunk,       // past-the-end chunks in the grid
                             max(1ll, (tail_bytes + kTailBytes - 1) / kTailBytes));
-    if (!pad || wi >= nw) return;
+    if (wi >= nw) return;
     const int seg = ((tn + nw - 1) / nw + 3) & ~3;                       // nw * seg >= tn
     const int lo = from0 + wi * seg, hi = min(row_stride, lo + seg);
-    const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    for (int g = 0; g < Hkv && lo < hi; ++g) {
-      float* row = scores + ((long long)b * Hkv + g) * row_stride + lo;
-      const int n = hi - lo;
-      const int head = min(n, (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / 4u));
-      if (tid < head) row[tid] = -INFINITY;
-      const int nv = (n - head) / 4;
-      float4* r4 = reinterpret_cast<float4*>(row + head);
-      for (int i = tid; i < nv; i += 256) r4[i] = ninf;
-      const int rem = n - head - 4 * nv;
-      if (tid < rem) row[head + 4 * nv + tid] = -INFINITY;
-    }
+    write_neg_inf_rows(scores, b, Hkv, row_stride, lo, hi);
     return;
   }
   summary_loads(0);
