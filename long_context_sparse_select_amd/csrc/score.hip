@@ -127,10 +127,6 @@ __device__ __forceinline__ void decode_append(const T* __restrict__ q, const T* 
   if (tid == 0) *dst = s_red[4 * kD] + s_red[4 * kD + 1];
 }
 
-// HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
-// shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
-// Workgroups x < napp (napp = Hkv with a new token, else 0) append, writing the pool through
-// S_app (the same pool as S, which only the scoring workgroups read); the others score chunks.
 // -inf over entries [lo, hi) of every group's score row of sequence b: 16 B stores across the
 // workgroup. Kept out of line: inlined into the scoring kernel's exit path it raised the kernel's
 // registers past the six-wave step (82 against 78 at 8 groups), and the grid of a batch of mixed
@@ -152,6 +148,10 @@ __device__ __attribute__((noinline)) void write_neg_inf_rows(float* __restrict__
   }
 }
 
+// HKV > 0: the number of KV heads as a compile-time constant (so the pair-index divisions are
+// shifts); HKV == 0: a runtime count (generic path). SB: the summary pool holds bf16.
+// Workgroups x < napp (napp = Hkv with a new token, else 0) append, writing the pool through
+// S_app (the same pool as S, which only the scoring workgroups read); the others score chunks.
 template <typename TQ, int HKV, bool SB>
 __global__ void __launch_bounds__(256) k_score_decode(const TQ* __restrict__ q, const void* __restrict__ S,
                                                       const int32_t* __restrict__ table,
