@@ -100,7 +100,7 @@ def run_decode(d: Dev, max_len=None, k_new=None, v_new=None):
     out = torch.empty_like(d.q)
     lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
-    scores = torch.empty((c.B, c.Hkv, max(mb, 1)), dtype=torch.float32, device="cuda")
+    scores = torch.full((c.B, c.Hkv, max(mb, 1)), float("nan"), dtype=torch.float32, device="cuda")   # every entry written
     msa.msa_decode_step(d.cfg, d.q, d.cache, c.B, max_len, out, k_new=k_new, v_new=v_new, idx_out=idx,
                         scores_out=scores, lse_out=lse)
     torch.cuda.synchronize()

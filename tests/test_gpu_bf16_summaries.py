@@ -130,12 +130,13 @@ def test_select_and_score_entry_points_bf16_summaries():
     c = make_decode_case(seed=62, B=2, Hq=32, Hkv=8, lens=[9000, 3000], top_k=16, dtype="bf16", permute=True)
     d = to_device_bf16(c)
     mb = (c.max_seq_len + 63) // 64
-    s1 = torch.empty((c.B, c.Hkv, mb), dtype=torch.float32, device="cuda")
-    s2 = torch.empty_like(s1)
+    s1 = torch.full((c.B, c.Hkv, mb), float("nan"), dtype=torch.float32, device="cuda")   # every entry written
+    s2 = torch.full_like(s1, float("nan"))
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
     msa.msa_score(d.cfg, d.q, d.cache, c.B, c.max_seq_len, s1)
     msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=s2)
     torch.cuda.synchronize()
+    assert not torch.isnan(s1).any() and not torch.isnan(s2).any()
     np.testing.assert_array_equal(s1.cpu().numpy(), s2.cpu().numpy())
     res = run_decode(d)
     np.testing.assert_array_equal(res["idx"].cpu().numpy(), idx.cpu().numpy())

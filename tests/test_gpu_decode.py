@@ -74,7 +74,7 @@ def test_select(name, kw):
     d = to_device(c)
     mb = (c.max_seq_len + 63) // 64
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
-    scores = torch.empty((c.B, c.Hkv, mb), dtype=torch.float32, device="cuda")
+    scores = torch.full((c.B, c.Hkv, mb), float("nan"), dtype=torch.float32, device="cuda")
     msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=scores)
     torch.cuda.synchronize()
     inputs = oracle_inputs(d)
@@ -347,8 +347,8 @@ def test_score_entry_point_matches_select_scores():
     c = make_decode_case(B=3, Hq=32, Hkv=8, lens=[9000, 130, 4096], top_k=8, dtype="bf16", seed=32, permute=True)
     d = to_device(c)
     mb = (c.max_seq_len + 63) // 64
-    s1 = torch.empty((c.B, c.Hkv, mb), dtype=torch.float32, device="cuda")
-    s2 = torch.empty_like(s1)
+    s1 = torch.full((c.B, c.Hkv, mb), float("nan"), dtype=torch.float32, device="cuda")
+    s2 = torch.full_like(s1, float("nan"))
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
     msa.msa_score(d.cfg, d.q, d.cache, c.B, c.max_seq_len, s1)
     msa.msa_select(d.cfg, d.q, d.cache, c.B, c.max_seq_len, idx, scores_out=s2)

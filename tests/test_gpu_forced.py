@@ -97,7 +97,7 @@ def test_index_branch_forced():
     cfg.keep_sink, cfg.keep_local = 2, 1
     mb = (c.max_seq_len + 63) // 64
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((c.B, c.Hkv, mb), dtype=torch.float32, device="cuda")
+    sc = torch.full((c.B, c.Hkv, mb), float("nan"), dtype=torch.float32, device="cuda")
     msa.msa_select_index(cfg, qi, ik, tab, lens, c.B, c.max_seq_len, idx, scores_out=sc)
     torch.cuda.synchronize()
     gi, gs = idx.cpu().numpy(), sc.cpu().numpy()

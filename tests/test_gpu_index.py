@@ -58,7 +58,8 @@ def run_index(c, max_len=None, table=None, scores=True):
     max_len = c.max_seq_len if max_len is None else max_len
     mb = (max_len + 63) // 64
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((c.B, c.Hkv, max(mb, 1)), dtype=torch.float32, device="cuda") if scores else None
+    sc = (torch.full((c.B, c.Hkv, max(mb, 1)), float("nan"), dtype=torch.float32, device="cuda")
+          if scores else None)
     msa.msa_select_index(cfg, qi, ik, tab, lens, c.B, max_len, idx, scores_out=sc)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), (sc.cpu().numpy()[:, :, :mb] if scores else None), host_store(qi), host_store(ik)

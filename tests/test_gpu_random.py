@@ -90,7 +90,7 @@ def test_random_index_select(i):
     tab = torch.from_numpy(np.ascontiguousarray(table)).cuda()
     mb = (c.max_seq_len + 63) // 64
     idx = torch.empty((c.B, c.Hkv, c.top_k), dtype=torch.int32, device="cuda")
-    sc = torch.empty((c.B, c.Hkv, max(mb, 1)), dtype=torch.float32, device="cuda")
+    sc = torch.full((c.B, c.Hkv, max(mb, 1)), float("nan"), dtype=torch.float32, device="cuda")
     msa.msa_select_index(cfg, qi, ik, tab, ln, c.B, c.max_seq_len, idx, scores_out=sc)
     torch.cuda.synchronize()
     ti.full_check(c, idx.cpu().numpy(), sc.cpu().numpy()[:, :, :mb], ti.host_store(qi), ti.host_store(ik),
